@@ -1,0 +1,230 @@
+/*
+ * libsmoe -- routed-expert MoE layer over a window of speculative tokens,
+ * hand-written HIP for AMD MI355X (gfx950).
+ *
+ * Sources the operations follow (cited by page title and paragraph/section):
+ *   [P]  "Specter: Fast MoE Inference via Quantization-Enabled Multi-Step
+ *        Speculative Offloading" (paper body text).
+ *   [D]  Specter repository design notes, page "Design".
+ *   [S]  Korean summary page of Specter ("Specter는 양자화 드래프트로 MoE
+ *        오프로딩의 PCIe 지연을 숨긴다").
+ *
+ * Conventions for every call
+ *   - Pointers are DEVICE pointers unless stated otherwise, owned by the
+ *     caller, 16-byte aligned, and valid for the whole call. The library
+ *     never allocates, frees or keeps a pointer after the call returns.
+ *     Outputs must not alias inputs.
+ *   - `stream` is a hipStream_t (NULL = the null stream). Every call only
+ *     enqueues work on it: no host or device synchronisation, no device to
+ *     host copies, no memsets, so calls can be captured into a HIP graph.
+ *   - Arguments are checked before anything is enqueued; a bad argument
+ *     returns SMOE_EINVAL (null / negative / inconsistent) or
+ *     SMOE_EUNSUPPORTED (outside the kernels' limits) and touches no memory.
+ *     A failed launch returns SMOE_EHIP. smoe_last_error() gives the reason
+ *     (thread-local text).
+ *   - Limits: 1 <= E <= 256; 1 <= k <= min(8, E); H and I multiples of 128;
+ *     group size G in {32, 64, 128}; T*k < 2^24; M <= E.
+ *   - Layouts are row-major. fp16 = IEEE binary16, passed as void*.
+ *   - Packed INT4 weights W[N][K]: codes uint32 [N][K/8], word w of row n
+ *     holds the codes for k = 8w .. 8w+7, the code for k = 8w+j in bits
+ *     4j .. 4j+3; scales fp16 [N][K/G]. A code c stands for (c - 8) * scale.
+ *   - Token t of the window owns routing slots s = t*k + j, j = 0..k-1, in
+ *     rank order (slot s carries expert topk_ids[t][j]).
+ */
+#ifndef SMOE_H
+#define SMOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int smoe_status;
+#define SMOE_OK            0
+#define SMOE_EINVAL       (-1)
+#define SMOE_EUNSUPPORTED (-2)
+#define SMOE_EHIP         (-3)
+
+#define SMOE_ROUTE_RENORM    1  /* smoe_route_topk: renormalise the k weights to sum 1 */
+#define SMOE_ELB_CLEAR_AFTER 1  /* smoe_elb_accumulate_topm: zero the counter after ranking */
+
+/* Version of this interface (bumped on any signature change). */
+int smoe_abi_version(void);
+
+/* Static text for a status code. */
+const char* smoe_status_string(smoe_status status);
+
+/* Text describing the last failure on the calling thread ("" if none). */
+const char* smoe_last_error(void);
+
+/*
+ * Router + top-k.                                     [P] paragraphs on the
+ * Incremental Routing Pattern Analyzer (the draft router's top-k expert IDs)
+ * and on expert-wise verification (the target router's routing decisions);
+ * [D] "Speculative Inference Controller" (routers are shared, FP16/FP32).
+ *
+ * logits[t][e] = x[t] . w_router[e] (+ logit_bias[e]) in float32, summed in
+ * this order: 64 partials p[l] over h = 64c + l for c = 0, 1, ... (each
+ * product and each sum rounded separately, no fused multiply-add), then
+ * p[l] += p[l + off] for off = 32, 16, 8, 4, 2, 1; the bias is added last.
+ * topk_ids[t][0..k-1] = the k experts with the largest logits, by logit
+ * descending then expert ID ascending (-0.0 == +0.0).
+ * topk_w[t][j] = softmax over all E logits, taken at topk_ids[t][j]
+ * (float32); with SMOE_ROUTE_RENORM divided by their sum over j.
+ * shared_gate[t] = 1 / (1 + exp(-x[t] . shared_gate_w)) when both pointers
+ * are non-NULL (sigmoid gate of a shared expert).
+ *
+ *   x            fp16 [T][H]
+ *   w_router     float [E][H]
+ *   logit_bias   float [E] or NULL
+ *   topk_ids     int32 [T][k]   (out)
+ *   topk_w       float [T][k]   (out)
+ *   logits       float [T][E]   (out, optional, NULL to skip)
+ *   shared_gate_w float [H] or NULL; shared_gate float [T] (out) or NULL
+ * T = 0 enqueues nothing. Non-finite logits give an unspecified selection.
+ */
+smoe_status smoe_route_topk(const void* x, const float* w_router, const float* logit_bias,
+                            int T, int H, int E, int k, int flags,
+                            int32_t* topk_ids, float* topk_w, float* logits,
+                            const float* shared_gate_w, float* shared_gate,
+                            void* stream);
+
+/*
+ * Align token groups by expert.                       [P] fused multi-expert
+ * draft kernel paragraph (gather routed tokens by expert assignment) and
+ * expert-wise verification paragraph (pack the tokens of each expert into a
+ * contiguous sub-batch); [D] "Streamlined Execution Engine" (kernels align
+ * token groups).
+ *
+ * A stable counting sort of the S = T*k slots by expert:
+ *   expert_counts[e]   slots routed to e                       int32 [E]
+ *   expert_offsets[e]  exclusive prefix sum; [E] = kept slots  int32 [E+1]
+ *   sorted_slots[p]    slots by (expert, slot) ascending; entries from
+ *                      expert_offsets[E] on are -1             int32 [S]
+ *   active_experts[i]  experts with count > 0 ascending, then -1   int32 [E]
+ *   n_active[0]        number of such experts                 int32 [1]
+ * IDs outside [0, E) are dropped (neither counted nor written). S = 0 is
+ * valid (all outputs describe an empty alignment).
+ */
+smoe_status smoe_align_by_expert(const int32_t* topk_ids, int T, int k, int E,
+                                 int32_t* expert_counts, int32_t* expert_offsets,
+                                 int32_t* sorted_slots, int32_t* active_experts,
+                                 int32_t* n_active, void* stream);
+
+/*
+ * ELB activation counter + top-M prefetch plan.       [P] Incremental Routing
+ * Pattern Analyzer paragraphs (GPU-resident layer-indexed counters
+ * ELB_cnt[j, e] over the draft route sets; per-layer top-M ranking at each
+ * prefetch checkpoint; one compact plan per checkpoint; cleared at the end
+ * of the draft stage); [D] "Predictive I/O Orchestrator" (pattern_analyzer);
+ * [S] "어떻게 쓰나".
+ *
+ * If topk_ids != NULL, for i in [0, n_layers):
+ *     elb_counts[layer_begin + i][e] += #{(t, j) : topk_ids[i][t][j] == e}
+ * (IDs outside [0, E) are not counted). Then if M > 0, for every layer l of
+ * the L layers: plan_ids[l][0..M-1] = the M experts with the largest counts,
+ * by count descending then expert ID ascending (zero counts included);
+ * plan_counts[l][m] = their counts (if plan_counts != NULL). Then, with
+ * SMOE_ELB_CLEAR_AFTER, every counter of the L layers is set to 0.
+ *
+ *   elb_counts   int32 [L][E] (in/out, caller-owned, persists across calls)
+ *   topk_ids     int32 [n_layers][T][k] or NULL
+ *   plan_ids     int32 [L][M] (out; may be NULL when M = 0)
+ *   plan_counts  int32 [L][M] (out) or NULL
+ * The plan stays on the device; the caller copies it to the host.
+ */
+smoe_status smoe_elb_accumulate_topm(int32_t* elb_counts, int L, int E,
+                                     const int32_t* topk_ids, int layer_begin, int n_layers,
+                                     int T, int k, int M,
+                                     int32_t* plan_ids, int32_t* plan_counts,
+                                     int flags, void* stream);
+
+/*
+ * Device workspace (bytes) that the expert FFN calls need for a window of
+ * T tokens, k slots per token and intermediate size I (the fp16
+ * intermediate activations of every slot). Returns 0 for invalid sizes.
+ */
+size_t smoe_ffn_workspace_bytes(int T, int k, int E, int H, int I);
+
+/*
+ * Fused multi-expert W4A16 expert FFN (draft pass).   [P] fused multi-expert
+ * draft kernel paragraph (all active experts' sub-computations in one
+ * launch; tokens gathered by expert into dense tiles), paragraph on Marlin
+ * and narrow expert matrices (2048x1408, 4096x6400 expert MLPs), GPTQ
+ * setup (symmetric INT4, group 128); [D] "Streamlined Execution Engine"
+ * (W4A16: INT4 weight tiles dequantised while computing with FP16
+ * activations; FP32 reduction).
+ *
+ * For every kept slot s routed to expert e (from the alignment), with
+ * t = s / k:
+ *     g = x[t] . Wg_e^T,  u = x[t] . Wu_e^T          (float32 accumulate)
+ *     h = fp16( SiLU(g) * u ),  SiLU(g) = g / (1 + exp(-g))
+ *     slot_out[s] = h . Wd_e^T                        (float32)
+ * with W = (code - 8) * scale. Rows of slot_out for dropped slots are not
+ * written.
+ *
+ *   x              fp16 [T][H]
+ *   wg_q, wu_q     uint32 [E][I][H/8];  wg_s, wu_s fp16 [E][I][H/G]
+ *   wd_q           uint32 [E][H][I/8];  wd_s       fp16 [E][H][I/G]
+ *   sorted_slots   int32 [T*k], expert_offsets int32 [E+1]
+ *                  (as written by smoe_align_by_expert for these T, k, E)
+ *   workspace      device buffer of at least
+ *                  smoe_ffn_workspace_bytes(T, k, E, H, I) bytes
+ *   slot_out       float [T*k][H] (out)
+ */
+smoe_status smoe_w4a16_expert_ffn(const void* x, int T, int k, int E, int H, int I,
+                                  int group_size,
+                                  const uint32_t* wg_q, const void* wg_s,
+                                  const uint32_t* wu_q, const void* wu_s,
+                                  const uint32_t* wd_q, const void* wd_s,
+                                  const int32_t* sorted_slots, const int32_t* expert_offsets,
+                                  void* workspace, size_t workspace_bytes,
+                                  float* slot_out, void* stream);
+
+/*
+ * Expert FFN with FP16 weights (target verification pass and always-on
+ * shared experts).                                    [P] expert-wise
+ * verification paragraphs (target router decisions; tokens of each expert
+ * packed into contiguous sub-batches, GEMVs become GEMMs; routing-weighted
+ * outputs scattered back; strict mathematical equivalence) and the
+ * hybrid-precision layout (shared experts stay FP16); [D] "Streamlined
+ * Execution Engine" (expert_reorder).
+ *
+ * Same computation and alignment as smoe_w4a16_expert_ffn with
+ * W = fp16 weights:
+ *   wg, wu   fp16 [E][I][H];   wd   fp16 [E][H][I]
+ * A shared expert is run as E = 1, k = 1 with sorted_slots = 0..T-1 and
+ * expert_offsets = {0, T}; several shared experts are concatenated along I.
+ */
+smoe_status smoe_fp16_expert_ffn(const void* x, int T, int k, int E, int H, int I,
+                                 const void* wg, const void* wu, const void* wd,
+                                 const int32_t* sorted_slots, const int32_t* expert_offsets,
+                                 void* workspace, size_t workspace_bytes,
+                                 float* slot_out, void* stream);
+
+/*
+ * Weighted combine back to token order.               [P] expert-wise
+ * verification paragraph (scatter the routing-weighted outputs and
+ * accumulate them into their original sequence positions); [D] "Streamlined
+ * Execution Engine" (kernels reduce expert outputs).
+ *
+ *   y[t] = fp16( sum_{j=0..k-1} topk_w[t][j] * slot_out[t*k + j]
+ *                + gate[t] * shared_out[t] )
+ * summed in float32 with j ascending, the shared term last; gate = 1 when
+ * shared_gate is NULL; no shared term when shared_out is NULL.
+ *
+ *   slot_out   float [T*k][H]; topk_w float [T][k]
+ *   shared_out float [T][H] or NULL; shared_gate float [T] or NULL
+ *   y          fp16 [T][H] (out)
+ */
+smoe_status smoe_combine(const float* slot_out, const float* topk_w, int T, int k, int H,
+                         const float* shared_out, const float* shared_gate,
+                         void* y, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SMOE_H */

@@ -1,0 +1,186 @@
+"""ctypes binding of libsmoe (argument marshalling only).
+
+Each function has the name of the C entry point it calls and takes torch
+tensors for device memory (plus an optional torch stream); it checks dtypes,
+devices and contiguity, passes raw pointers and sizes, and raises SmoeError
+on a non-zero status. Every step of the computation runs in the HIP library.
+If the library is missing or cannot be loaded, importing this module fails.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libsmoe.so")
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(
+        f"libsmoe.so not found at {LIB_PATH}; build it first with "
+        "`python -m quantized_speculative_expert_amd.build` (hipcc, gfx950)")
+
+_lib = ctypes.CDLL(LIB_PATH)
+
+_p = ctypes.c_void_p
+_i = ctypes.c_int
+_sz = ctypes.c_size_t
+
+_SIGNATURES = {
+    "smoe_abi_version": (_i, []),
+    "smoe_status_string": (ctypes.c_char_p, [_i]),
+    "smoe_last_error": (ctypes.c_char_p, []),
+    "smoe_route_topk": (_i, [_p, _p, _p, _i, _i, _i, _i, _i, _p, _p, _p, _p, _p, _p]),
+    "smoe_align_by_expert": (_i, [_p, _i, _i, _i, _p, _p, _p, _p, _p, _p]),
+    "smoe_elb_accumulate_topm": (_i, [_p, _i, _i, _p, _i, _i, _i, _i, _i, _p, _p, _i, _p]),
+    "smoe_ffn_workspace_bytes": (_sz, [_i, _i, _i, _i, _i]),
+    "smoe_w4a16_expert_ffn": (_i, [_p, _i, _i, _i, _i, _i, _i, _p, _p, _p, _p, _p, _p,
+                                   _p, _p, _p, _sz, _p, _p]),
+    "smoe_fp16_expert_ffn": (_i, [_p, _i, _i, _i, _i, _i, _p, _p, _p, _p, _p, _p, _sz,
+                                  _p, _p]),
+    "smoe_combine": (_i, [_p, _p, _i, _i, _i, _p, _p, _p, _p]),
+}
+
+for _name, (_res, _args) in _SIGNATURES.items():
+    _fn = getattr(_lib, _name)
+    _fn.restype = _res
+    _fn.argtypes = _args
+
+SMOE_OK = 0
+SMOE_EINVAL = -1
+SMOE_EUNSUPPORTED = -2
+SMOE_EHIP = -3
+SMOE_ROUTE_RENORM = 1
+SMOE_ELB_CLEAR_AFTER = 1
+
+
+class SmoeError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        self.status = status
+        detail = _lib.smoe_last_error().decode()
+        super().__init__(f"{fn}: {_lib.smoe_status_string(status).decode()} ({detail})")
+
+
+def exported_symbols():
+    return sorted(_SIGNATURES)
+
+
+def _check(fn: str, status: int) -> None:
+    if status != SMOE_OK:
+        raise SmoeError(fn, status)
+
+
+def _ptr(t: Optional[torch.Tensor], dtype=None, name: str = "tensor") -> Optional[int]:
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if t.numel() and not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    return t.data_ptr() if t.numel() else None
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    if isinstance(stream, int):
+        return stream or None
+    return stream.cuda_stream or None
+
+
+def smoe_abi_version() -> int:
+    return int(_lib.smoe_abi_version())
+
+
+def smoe_ffn_workspace_bytes(T: int, k: int, E: int, H: int, I: int) -> int:
+    return int(_lib.smoe_ffn_workspace_bytes(T, k, E, H, I))
+
+
+def smoe_route_topk(x, w_router, logit_bias, k: int, flags: int, topk_ids, topk_w,
+                    logits=None, shared_gate_w=None, shared_gate=None, stream=None) -> None:
+    T, H = x.shape
+    E = w_router.shape[0]
+    _check("smoe_route_topk", _lib.smoe_route_topk(
+        _ptr(x, torch.float16, "x"), _ptr(w_router, torch.float32, "w_router"),
+        _ptr(logit_bias, torch.float32, "logit_bias"), T, H, E, k, flags,
+        _ptr(topk_ids, torch.int32, "topk_ids"), _ptr(topk_w, torch.float32, "topk_w"),
+        _ptr(logits, torch.float32, "logits"),
+        _ptr(shared_gate_w, torch.float32, "shared_gate_w"),
+        _ptr(shared_gate, torch.float32, "shared_gate"), _stream(stream)))
+
+
+def smoe_align_by_expert(topk_ids, E: int, expert_counts, expert_offsets, sorted_slots,
+                         active_experts, n_active, stream=None) -> None:
+    T, k = topk_ids.shape
+    _check("smoe_align_by_expert", _lib.smoe_align_by_expert(
+        _ptr(topk_ids, torch.int32, "topk_ids"), T, k, E,
+        _ptr(expert_counts, torch.int32, "expert_counts"),
+        _ptr(expert_offsets, torch.int32, "expert_offsets"),
+        _ptr(sorted_slots, torch.int32, "sorted_slots"),
+        _ptr(active_experts, torch.int32, "active_experts"),
+        _ptr(n_active, torch.int32, "n_active"), _stream(stream)))
+
+
+def smoe_elb_accumulate_topm(elb_counts, topk_ids, layer_begin: int, M: int, plan_ids,
+                             plan_counts=None, flags: int = 0, stream=None) -> None:
+    """topk_ids: int32 [n_layers][T][k] or None (rank only)."""
+    L, E = elb_counts.shape
+    if topk_ids is not None:
+        n_layers, T, k = topk_ids.shape
+    else:
+        n_layers, T, k = 0, 0, 1
+    _check("smoe_elb_accumulate_topm", _lib.smoe_elb_accumulate_topm(
+        _ptr(elb_counts, torch.int32, "elb_counts"), L, E,
+        _ptr(topk_ids, torch.int32, "topk_ids"), layer_begin, n_layers, T, k, M,
+        _ptr(plan_ids, torch.int32, "plan_ids"), _ptr(plan_counts, torch.int32, "plan_counts"),
+        flags, _stream(stream)))
+
+
+def smoe_w4a16_expert_ffn(x, k: int, E: int, I: int, group_size: int, wg_q, wg_s, wu_q, wu_s,
+                          wd_q, wd_s, sorted_slots, expert_offsets, workspace, slot_out,
+                          stream=None) -> None:
+    T, H = x.shape
+    _check("smoe_w4a16_expert_ffn", _lib.smoe_w4a16_expert_ffn(
+        _ptr(x, torch.float16, "x"), T, k, E, H, I, group_size,
+        _ptr(wg_q, torch.int32, "wg_q"), _ptr(wg_s, torch.float16, "wg_s"),
+        _ptr(wu_q, torch.int32, "wu_q"), _ptr(wu_s, torch.float16, "wu_s"),
+        _ptr(wd_q, torch.int32, "wd_q"), _ptr(wd_s, torch.float16, "wd_s"),
+        _ptr(sorted_slots, torch.int32, "sorted_slots"),
+        _ptr(expert_offsets, torch.int32, "expert_offsets"),
+        _ptr(workspace, torch.uint8, "workspace"), workspace.numel(),
+        _ptr(slot_out, torch.float32, "slot_out"), _stream(stream)))
+
+
+def smoe_fp16_expert_ffn(x, k: int, E: int, I: int, wg, wu, wd, sorted_slots, expert_offsets,
+                         workspace, slot_out, stream=None) -> None:
+    T, H = x.shape
+    _check("smoe_fp16_expert_ffn", _lib.smoe_fp16_expert_ffn(
+        _ptr(x, torch.float16, "x"), T, k, E, H, I,
+        _ptr(wg, torch.float16, "wg"), _ptr(wu, torch.float16, "wu"),
+        _ptr(wd, torch.float16, "wd"),
+        _ptr(sorted_slots, torch.int32, "sorted_slots"),
+        _ptr(expert_offsets, torch.int32, "expert_offsets"),
+        _ptr(workspace, torch.uint8, "workspace"), workspace.numel(),
+        _ptr(slot_out, torch.float32, "slot_out"), _stream(stream)))
+
+
+def smoe_combine(slot_out, topk_w, shared_out, shared_gate, y, stream=None) -> None:
+    T, k = topk_w.shape
+    H = y.shape[1]
+    _check("smoe_combine", _lib.smoe_combine(
+        _ptr(slot_out, torch.float32, "slot_out"), _ptr(topk_w, torch.float32, "topk_w"),
+        T, k, H, _ptr(shared_out, torch.float32, "shared_out"),
+        _ptr(shared_gate, torch.float32, "shared_gate"),
+        _ptr(y, torch.float16, "y"), _stream(stream)))
+
+
+def raw_library() -> ctypes.CDLL:
+    """The loaded CDLL (for tests that call the C ABI directly)."""
+    return _lib

@@ -1,0 +1,107 @@
+// smoe_elb_accumulate_topm: ELB activation counter and top-M prefetch plan.
+//
+// Specter paper, Incremental Routing Pattern Analyzer paragraphs: the ELB
+// is a GPU-resident, layer-indexed set of activation counters
+// ELB_cnt[j, e] = number of draft tokens whose top-k route set in layer j
+// contains e; at each prefetch checkpoint the experts of every layer are
+// ranked by count and the top M (the layer's cache slots) form a compact
+// plan; the ELB is cleared at the end of the draft stage. Design notes,
+// "Predictive I/O Orchestrator" (pattern_analyzer accumulates routing
+// counts on the GPU and ranks experts at chunk boundaries).
+//
+// One workgroup per layer. Accumulation: an LDS histogram of the layer's
+// T*k IDs (integer adds, order-free) added to the counter row, which only
+// this workgroup touches. Ranking: expert e's place is the number of
+// experts ahead of it in (count descending, ID ascending) order, found by
+// one pass over the LDS copy of the row; experts placed below M write
+// themselves into the plan. Integer only, so the result is exact and
+// independent of thread timing.
+#include "smoe_internal.hpp"
+
+namespace smoe {
+namespace {
+
+constexpr int kElbThreads = 256;
+
+__global__ __launch_bounds__(kElbThreads) void elb_kernel(
+    int32_t* __restrict__ cnt, int E, const int32_t* __restrict__ ids, int layer_begin,
+    int n_layers, int S, int M, int32_t* __restrict__ plan_ids,
+    int32_t* __restrict__ plan_counts, int clear) {
+  __shared__ int hist[kMaxE];
+  __shared__ int row[kMaxE];
+  const int l = blockIdx.x;
+  int32_t* crow = cnt + static_cast<size_t>(l) * E;
+
+  for (int e = threadIdx.x; e < E; e += kElbThreads) hist[e] = 0;
+  __syncthreads();
+  const int i = l - layer_begin;
+  if (ids != nullptr && i >= 0 && i < n_layers) {
+    const int32_t* lid = ids + static_cast<size_t>(i) * S;
+    for (int s = threadIdx.x; s < S; s += kElbThreads) {
+      const int e = lid[s];
+      if (e >= 0 && e < E) atomicAdd(&hist[e], 1);
+    }
+  }
+  __syncthreads();
+  for (int e = threadIdx.x; e < E; e += kElbThreads) {
+    const int v = crow[e] + hist[e];
+    row[e] = v;
+    if (hist[e] != 0) crow[e] = v;
+  }
+  __syncthreads();
+
+  if (M > 0) {
+    for (int e = threadIdx.x; e < E; e += kElbThreads) {
+      const int c = row[e];
+      int place = 0;
+      for (int f = 0; f < E; ++f) {
+        const int cf = row[f];
+        place += (cf > c || (cf == c && f < e)) ? 1 : 0;
+      }
+      if (place < M) {
+        plan_ids[static_cast<size_t>(l) * M + place] = e;
+        if (plan_counts != nullptr) plan_counts[static_cast<size_t>(l) * M + place] = c;
+      }
+    }
+  }
+  if (clear) {
+    for (int e = threadIdx.x; e < E; e += kElbThreads) crow[e] = 0;
+  }
+}
+
+}  // namespace
+}  // namespace smoe
+
+using namespace smoe;
+
+extern "C" smoe_status smoe_elb_accumulate_topm(int32_t* elb_counts, int L, int E,
+                                                const int32_t* topk_ids, int layer_begin,
+                                                int n_layers, int T, int k, int M,
+                                                int32_t* plan_ids, int32_t* plan_counts,
+                                                int flags, void* stream) {
+  clear_error();
+  SMOE_REQUIRE(L > 0 && E > 0 && M >= 0, SMOE_EINVAL,
+               "elb_accumulate_topm: need L > 0, E > 0, M >= 0 (L=%d E=%d M=%d)", L, E, M);
+  SMOE_REQUIRE(E <= kMaxE, SMOE_EUNSUPPORTED, "elb_accumulate_topm: E must be <= 256 (E=%d)", E);
+  SMOE_REQUIRE(M <= E, SMOE_EINVAL, "elb_accumulate_topm: M must be <= E (M=%d E=%d)", M, E);
+  SMOE_REQUIRE((flags & ~SMOE_ELB_CLEAR_AFTER) == 0, SMOE_EINVAL,
+               "elb_accumulate_topm: unknown flags %d", flags);
+  SMOE_REQUIRE(elb_counts != nullptr, SMOE_EINVAL, "elb_accumulate_topm: null counter");
+  SMOE_REQUIRE(M == 0 || plan_ids != nullptr, SMOE_EINVAL, "elb_accumulate_topm: null plan_ids");
+  int S = 0;
+  if (topk_ids != nullptr) {
+    SMOE_REQUIRE(T >= 0 && k > 0 && n_layers >= 0, SMOE_EINVAL,
+                 "elb_accumulate_topm: need T >= 0, k > 0, n_layers >= 0");
+    SMOE_REQUIRE(k <= kMaxK, SMOE_EUNSUPPORTED, "elb_accumulate_topm: k must be <= 8");
+    SMOE_REQUIRE(layer_begin >= 0 && layer_begin + n_layers <= L, SMOE_EINVAL,
+                 "elb_accumulate_topm: layers [%d, %d) outside [0, %d)", layer_begin,
+                 layer_begin + n_layers, L);
+    SMOE_REQUIRE(static_cast<long long>(T) * k < (1ll << 24), SMOE_EUNSUPPORTED,
+                 "elb_accumulate_topm: T*k must be below 2^24");
+    S = T * k;
+  }
+  hipLaunchKernelGGL(elb_kernel, dim3(L), dim3(kElbThreads), 0, as_stream(stream), elb_counts, E,
+                     topk_ids, layer_begin, topk_ids ? n_layers : 0, S, M, plan_ids, plan_counts,
+                     (flags & SMOE_ELB_CLEAR_AFTER) ? 1 : 0);
+  return check_launch("elb_accumulate_topm");
+}

@@ -1,0 +1,153 @@
+"""One MoE layer on the device: the six libsmoe calls in order.
+
+DeviceLayer holds the device copies of one layer's inputs (any object with
+the attributes of workload.LayerInputs) and the output / scratch buffers,
+and enqueues route -> align -> [ELB] -> routed expert FFN -> shared expert
+FFN -> combine on a stream. It only sequences calls of the HIP library and
+allocates buffers; all arithmetic happens in the library.
+
+Draft pass: INT4 (W4A16) routed experts (Specter paper, fused multi-expert
+draft kernel paragraph). Target pass: FP16 routed experts with the same
+expert-centric gather/scatter (expert-wise verification paragraphs). The
+always-on shared experts are FP16 in both (hybrid-precision layout); they
+depend only on x, so with a side stream they run concurrently with routing
+and the routed experts.
+"""
+
+from __future__ import annotations
+
+from typing import Optional
+
+import numpy as np
+import torch
+
+from . import _lib
+
+
+def _dev(a: Optional[np.ndarray], device) -> Optional[torch.Tensor]:
+    if a is None:
+        return None
+    a = np.ascontiguousarray(a)
+    if a.dtype == np.uint32:
+        a = a.view(np.int32)
+    return torch.from_numpy(a).to(device)
+
+
+class DeviceLayer:
+    def __init__(self, inp, device="cuda", elb_layers: int = 1, with_target: Optional[bool] = None):
+        cfg = inp.cfg
+        self.cfg = cfg
+        self.device = torch.device(device)
+        d = self.device
+        T, k, E, H, I = cfg.T, cfg.k, cfg.E, cfg.H, cfg.I
+        S = T * k
+        self.x = _dev(inp.x, d)
+        self.w_router = _dev(inp.w_router, d)
+        self.router_bias = _dev(inp.router_bias, d)
+        self.shared_gate_w = _dev(inp.shared_gate_w, d)
+        self.wg_q, self.wg_s = _dev(inp.wg_q, d), _dev(inp.wg_s, d)
+        self.wu_q, self.wu_s = _dev(inp.wu_q, d), _dev(inp.wu_s, d)
+        self.wd_q, self.wd_s = _dev(inp.wd_q, d), _dev(inp.wd_s, d)
+        if with_target is None:
+            with_target = inp.wg16 is not None
+        self.wg16 = _dev(inp.wg16, d) if with_target else None
+        self.wu16 = _dev(inp.wu16, d) if with_target else None
+        self.wd16 = _dev(inp.wd16, d) if with_target else None
+        self.sg16, self.su16, self.sd16 = (_dev(inp.sg16, d), _dev(inp.su16, d),
+                                          _dev(inp.sd16, d))
+
+        i32 = dict(dtype=torch.int32, device=d)
+        f32 = dict(dtype=torch.float32, device=d)
+        self.topk_ids = torch.empty((T, k), **i32)
+        self.topk_w = torch.empty((T, k), **f32)
+        self.logits = torch.empty((T, E), **f32)
+        self.counts = torch.empty(E, **i32)
+        self.offsets = torch.empty(E + 1, **i32)
+        self.sorted_slots = torch.empty(S, **i32)
+        self.active = torch.empty(E, **i32)
+        self.n_active = torch.empty(1, **i32)
+        ws = _lib.smoe_ffn_workspace_bytes(T, k, E, H, I)
+        self.workspace = torch.empty(ws, dtype=torch.uint8, device=d)
+        self.slot_out = torch.empty((S, H), **f32)
+        self.y = torch.empty((T, H), dtype=torch.float16, device=d)
+        self.shared_gate = torch.empty(T, **f32) if self.shared_gate_w is not None else None
+        if self.sg16 is not None:
+            Is = self.sg16.shape[0]
+            self.shared_I = Is
+            self.shared_out = torch.empty((T, H), **f32)
+            self.shared_ws = torch.empty(_lib.smoe_ffn_workspace_bytes(T, 1, 1, H, Is),
+                                         dtype=torch.uint8, device=d)
+            self.shared_slots = torch.arange(T, **i32)
+            self.shared_offsets = torch.tensor([0, T], **i32)
+        else:
+            self.shared_out = None
+        self.elb_counts = torch.zeros((elb_layers, E), **i32)
+        M = max(cfg.elb_M, 0)
+        self.plan_ids = torch.empty((elb_layers, max(M, 1)), **i32)
+        self.plan_counts = torch.empty((elb_layers, max(M, 1)), **i32)
+
+    # ---------------------------------------------------------------- steps
+    def route(self, stream=None) -> None:
+        _lib.smoe_route_topk(self.x, self.w_router, self.router_bias, self.cfg.k, 0,
+                             self.topk_ids, self.topk_w, self.logits,
+                             self.shared_gate_w, self.shared_gate, stream=stream)
+
+    def align(self, stream=None) -> None:
+        _lib.smoe_align_by_expert(self.topk_ids, self.cfg.E, self.counts, self.offsets,
+                                  self.sorted_slots, self.active, self.n_active, stream=stream)
+
+    def elb(self, layer: int = 0, M: Optional[int] = None, flags: int = 0, stream=None) -> None:
+        M = self.cfg.elb_M if M is None else M
+        _lib.smoe_elb_accumulate_topm(self.elb_counts, self.topk_ids[None], layer, M,
+                                      self.plan_ids if M > 0 else None,
+                                      self.plan_counts if M > 0 else None, flags, stream=stream)
+
+    def routed_ffn(self, target: bool = False, stream=None) -> None:
+        c = self.cfg
+        if target:
+            _lib.smoe_fp16_expert_ffn(self.x, c.k, c.E, c.I, self.wg16, self.wu16, self.wd16,
+                                      self.sorted_slots, self.offsets, self.workspace,
+                                      self.slot_out, stream=stream)
+        else:
+            _lib.smoe_w4a16_expert_ffn(self.x, c.k, c.E, c.I, c.G, self.wg_q, self.wg_s,
+                                       self.wu_q, self.wu_s, self.wd_q, self.wd_s,
+                                       self.sorted_slots, self.offsets, self.workspace,
+                                       self.slot_out, stream=stream)
+
+    def shared_ffn(self, stream=None) -> None:
+        if self.shared_out is None:
+            return
+        _lib.smoe_fp16_expert_ffn(self.x, 1, 1, self.shared_I, self.sg16, self.su16, self.sd16,
+                                  self.shared_slots, self.shared_offsets, self.shared_ws,
+                                  self.shared_out, stream=stream)
+
+    def combine(self, stream=None) -> None:
+        _lib.smoe_combine(self.slot_out, self.topk_w, self.shared_out, self.shared_gate,
+                          self.y, stream=stream)
+
+    # ---------------------------------------------------------------- whole layer
+    def run(self, target: bool = False, elb: bool = True, side_stream=None) -> None:
+        """Enqueue the whole layer on the current stream.
+
+        With side_stream, the shared expert runs there, ordered after the
+        current stream's prior work and joined before the combine.
+        """
+        main = torch.cuda.current_stream(self.device)
+        if side_stream is not None and self.shared_out is not None:
+            fork = torch.cuda.Event()
+            fork.record(main)
+            side_stream.wait_event(fork)
+            self.shared_ffn(stream=side_stream)
+            join = torch.cuda.Event()
+            join.record(side_stream)
+        else:
+            join = None
+            self.shared_ffn()
+        self.route()
+        self.align()
+        if elb and self.cfg.elb_M > 0 and not target:
+            self.elb()
+        self.routed_ffn(target=target)
+        if join is not None:
+            main.wait_event(join)
+        self.combine()

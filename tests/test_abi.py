@@ -1,0 +1,127 @@
+"""The C-ABI library loads, exports every entry point of include/smoe.h, and
+rejects bad arguments before enqueuing anything (no GPU needed: these calls
+return from argument checking and never reach the HIP runtime)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "smoe.h")
+LIB = os.path.join(ROOT, "quantized_speculative_expert_amd", "libsmoe.so")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(LIB),
+                                reason="libsmoe.so not built (run __graft_entry__.build())")
+
+EINVAL, EUNSUPPORTED = -1, -2
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(smoe_[a-z0-9_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    l = ctypes.CDLL(LIB)
+    l.smoe_status_string.restype = ctypes.c_char_p
+    l.smoe_last_error.restype = ctypes.c_char_p
+    l.smoe_ffn_workspace_bytes.restype = ctypes.c_size_t
+    return l
+
+
+def test_every_declared_symbol_is_exported(lib):
+    names = declared_functions()
+    assert {"smoe_route_topk", "smoe_align_by_expert", "smoe_elb_accumulate_topm",
+            "smoe_w4a16_expert_ffn", "smoe_fp16_expert_ffn", "smoe_combine",
+            "smoe_ffn_workspace_bytes", "smoe_status_string", "smoe_last_error",
+            "smoe_abi_version"} <= set(names)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_binding_signatures_cover_header():
+    # the Python binding declares a signature for every C entry point
+    src = open(os.path.join(ROOT, "quantized_speculative_expert_amd", "_lib.py")).read()
+    for n in declared_functions():
+        assert f'"{n}"' in src, n
+
+
+def test_status_strings(lib):
+    assert lib.smoe_abi_version() == 1
+    assert lib.smoe_status_string(0) == b"SMOE_OK"
+    assert b"EINVAL" in lib.smoe_status_string(EINVAL)
+    assert b"EUNSUPPORTED" in lib.smoe_status_string(EUNSUPPORTED)
+    assert b"EHIP" in lib.smoe_status_string(-3)
+
+
+def test_workspace_bytes(lib):
+    f = lib.smoe_ffn_workspace_bytes
+    f.argtypes = [ctypes.c_int] * 5
+    assert f(17, 6, 64, 2048, 1408) == ((17 * 6 * 1408 * 2 + 255) // 256) * 256
+    assert f(-1, 6, 64, 2048, 1408) == 0
+    assert f(0, 6, 64, 2048, 1408) == 0
+
+
+N = None
+
+
+def test_route_argument_checks(lib):
+    f = lib.smoe_route_topk
+    f.argtypes = [ctypes.c_void_p] * 3 + [ctypes.c_int] * 5 + [ctypes.c_void_p] * 6
+    assert f(N, N, N, 17, 2048, 0, 6, 0, N, N, N, N, N, N) == EINVAL
+    assert f(N, N, N, 17, 2048, 300, 6, 0, N, N, N, N, N, N) == EUNSUPPORTED
+    assert f(N, N, N, 17, 2048, 64, 9, 0, N, N, N, N, N, N) == EUNSUPPORTED
+    assert f(N, N, N, 17, 2000, 64, 6, 0, N, N, N, N, N, N) == EUNSUPPORTED
+    assert f(N, N, N, 17, 2048, 64, 6, 4, N, N, N, N, N, N) == EINVAL       # bad flag
+    assert f(N, N, N, 17, 2048, 64, 6, 0, N, N, N, N, N, N) == EINVAL       # null x
+    assert b"null" in lib.smoe_last_error()
+    assert f(N, N, N, 0, 2048, 64, 6, 0, N, N, N, N, N, N) == 0             # empty window
+
+
+def test_align_argument_checks(lib):
+    f = lib.smoe_align_by_expert
+    f.argtypes = [ctypes.c_void_p] + [ctypes.c_int] * 3 + [ctypes.c_void_p] * 6
+    assert f(N, 17, 6, 0, N, N, N, N, N, N) == EINVAL
+    assert f(N, 17, 6, 257, N, N, N, N, N, N) == EUNSUPPORTED
+    assert f(N, 17, 6, 64, N, N, N, N, N, N) == EINVAL
+
+
+def test_elb_argument_checks(lib):
+    f = lib.smoe_elb_accumulate_topm
+    f.argtypes = ([ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_void_p] +
+                  [ctypes.c_int] * 5 + [ctypes.c_void_p] * 2 + [ctypes.c_int, ctypes.c_void_p])
+    assert f(N, 1, 64, N, 0, 0, 0, 1, 32, N, N, 0, N) == EINVAL            # null counter
+    assert f(1, 1, 64, N, 0, 0, 0, 1, 65, 1, N, 0, N) == EINVAL            # M > E
+    assert f(1, 1, 64, N, 0, 0, 0, 1, 32, N, N, 0, N) == EINVAL            # null plan
+    assert f(1, 1, 64, 1, 0, 2, 17, 6, 32, 1, N, 0, N) == EINVAL           # layers out of range
+    assert f(1, 1, 64, N, 0, 0, 0, 1, 32, 1, N, 2, N) == EINVAL            # bad flag
+
+
+def test_ffn_argument_checks(lib):
+    f = lib.smoe_w4a16_expert_ffn
+    f.argtypes = ([ctypes.c_void_p] + [ctypes.c_int] * 6 + [ctypes.c_void_p] * 9 +
+                  [ctypes.c_size_t, ctypes.c_void_p, ctypes.c_void_p])
+    args = [16, 16, 16, 16, 16, 16, 16, 16, 16]
+    assert f(16, 17, 6, 64, 2048, 1408, 96, *args, 1 << 20, 16, N) == EUNSUPPORTED  # G=96
+    assert f(16, 17, 6, 64, 2048, 1400, 128, *args, 1 << 20, 16, N) == EUNSUPPORTED  # I%128
+    assert f(16, 17, 6, 64, 2048, 1408, 128, *args, 10, 16, N) == EINVAL  # workspace too small
+    assert f(16, 17, 6, 64, 2048, 1408, 128, *args[:-1], 8, 1 << 20, 16, N) == EINVAL  # align
+    g = lib.smoe_fp16_expert_ffn
+    g.argtypes = ([ctypes.c_void_p] + [ctypes.c_int] * 5 + [ctypes.c_void_p] * 6 +
+                  [ctypes.c_size_t, ctypes.c_void_p, ctypes.c_void_p])
+    assert g(N, 17, 6, 64, 2048, 1408, 16, 16, 16, 16, 16, 16, 1 << 20, 16, N) == EINVAL
+    assert g(16, 17, 0, 64, 2048, 1408, 16, 16, 16, 16, 16, 16, 1 << 20, 16, N) == EINVAL
+
+
+def test_combine_argument_checks(lib):
+    f = lib.smoe_combine
+    f.argtypes = [ctypes.c_void_p] * 2 + [ctypes.c_int] * 3 + [ctypes.c_void_p] * 4
+    assert f(N, N, 17, 6, 2048, N, 16, N, N) == EINVAL   # gate without shared output
+    assert f(N, N, 17, 9, 2048, N, N, N, N) == EUNSUPPORTED
+    assert f(N, N, 17, 6, 2048, N, N, N, N) == EINVAL
+    assert f(8, 16, 17, 6, 2048, N, N, 16, N) == EINVAL  # misaligned slot_out
+    assert f(N, N, 0, 6, 2048, N, N, N, N) == 0

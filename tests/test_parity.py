@@ -1,0 +1,441 @@
+"""GPU parity: every libsmoe call against the CPU oracle on the same seeded
+inputs. Integer results (expert IDs, alignment, ELB counts and plans) must
+be bit-exact; router logits too (same float32 order on both sides); floating
+outputs must be within the stated tolerances. Needs an MI355X."""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from workload import get_config, make_layer, quantize_rtn_int4
+from workload.configs import MoEConfig
+
+pytestmark = pytest.mark.gpu
+
+# Layer-output tolerance: per token (or slot) row, max |gpu - ref| / max |ref|.
+# The GPU computes in FP16 x FP16 -> FP32 with the intermediate activation
+# and the output in FP16; expected error is ~1e-3.
+ROW_TOL = 2e-2
+# Routing weights: float32 softmax (expf, float32 sum) vs float64.
+W_RTOL = 2e-5
+
+
+@pytest.fixture(scope="module")
+def smoe():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU visible")
+    from quantized_speculative_expert_amd import _lib  # fails loudly if not built
+    return _lib
+
+
+def dev(a):
+    a = np.ascontiguousarray(a)
+    if a.dtype == np.uint32:
+        a = a.view(np.int32)
+    return torch.from_numpy(a).cuda()
+
+
+def host(t):
+    torch.cuda.synchronize()
+    return t.detach().cpu().numpy()
+
+
+def row_rel_err(got, ref):
+    got = np.asarray(got, np.float64)
+    ref = np.asarray(ref, np.float64)
+    num = np.abs(got - ref).max(axis=1)
+    den = np.maximum(np.abs(ref).max(axis=1), 1e-30)
+    return (num / den).max() if len(num) else 0.0
+
+
+_LAYERS = {}
+
+
+def layer(name, seed=0, layer_idx=0):
+    key = (name, seed, layer_idx)
+    if key not in _LAYERS:
+        _LAYERS[key] = make_layer(get_config(name), seed=seed, layer=layer_idx)
+    return _LAYERS[key]
+
+
+def run_route(smoe, x, w, bias, k, flags=0, gate_w=None):
+    T, E = x.shape[0], w.shape[0]
+    ids = torch.empty((T, k), dtype=torch.int32, device="cuda")
+    wt = torch.empty((T, k), dtype=torch.float32, device="cuda")
+    lg = torch.empty((T, E), dtype=torch.float32, device="cuda")
+    gate = torch.empty(T, dtype=torch.float32, device="cuda") if gate_w is not None else None
+    smoe.smoe_route_topk(dev(x), dev(w), None if bias is None else dev(bias), k, flags, ids, wt,
+                         lg, None if gate_w is None else dev(gate_w), gate)
+    return host(ids), host(wt), host(lg), (host(gate) if gate is not None else None)
+
+
+def run_align(smoe, ids, E):
+    T, k = ids.shape
+    S = T * k
+    out = dict(counts=torch.full((E,), -7, dtype=torch.int32, device="cuda"),
+               offsets=torch.full((E + 1,), -7, dtype=torch.int32, device="cuda"),
+               sorted_slots=torch.full((max(S, 1),), -7, dtype=torch.int32, device="cuda"),
+               active=torch.full((E,), -7, dtype=torch.int32, device="cuda"),
+               n_active=torch.full((1,), -7, dtype=torch.int32, device="cuda"))
+    smoe.smoe_align_by_expert(dev(ids.astype(np.int32)), E, out["counts"], out["offsets"],
+                              out["sorted_slots"][:S], out["active"], out["n_active"])
+    res = {k_: host(v) for k_, v in out.items()}
+    res["sorted_slots"] = res["sorted_slots"][:S]
+    return res
+
+
+def check_align(got, ref):
+    for key in ("counts", "offsets", "sorted_slots", "active"):
+        assert np.array_equal(got[key], ref[key]), key
+    assert int(got["n_active"][0]) == int(ref["n_active"])
+
+
+# ------------------------------------------------------------------ router
+
+@pytest.mark.parametrize("name", ["tiny", "dsv2", "qwen", "phi"])
+def test_route_matches_oracle(smoe, name):
+    L = layer(name)
+    cfg = L.cfg
+    ids, wt, lg, gate = run_route(smoe, L.x, L.w_router, L.router_bias, cfg.k,
+                                  gate_w=L.shared_gate_w)
+    ref_lg = oracle.router_logits_f32(L.x, L.w_router, L.router_bias)
+    assert np.array_equal(lg.view(np.uint32), ref_lg.view(np.uint32))
+    ref_ids = oracle.topk_experts(ref_lg, cfg.k)
+    assert np.array_equal(ids, ref_ids)
+    ref_w = oracle.routing_weights(ref_lg, ref_ids)
+    assert np.allclose(wt, ref_w, rtol=W_RTOL, atol=1e-9)
+    if L.shared_gate_w is not None:
+        assert np.allclose(gate, oracle.shared_gate(L.x, L.shared_gate_w), rtol=1e-5, atol=1e-7)
+
+
+def test_route_batched_zipf_layer(smoe):
+    L = layer("batch", layer_idx=3)
+    ids, wt, lg, _ = run_route(smoe, L.x, L.w_router, L.router_bias, L.cfg.k)
+    ref_lg = oracle.router_logits_f32(L.x, L.w_router, L.router_bias)
+    assert np.array_equal(lg.view(np.uint32), ref_lg.view(np.uint32))
+    assert np.array_equal(ids, oracle.topk_experts(ref_lg, L.cfg.k))
+    assert np.allclose(wt, oracle.routing_weights(ref_lg, ids), rtol=W_RTOL, atol=1e-9)
+
+
+def test_route_golden_order(smoe):
+    import json, os
+    g = json.load(open(os.path.join(os.path.dirname(__file__), "golden",
+                                    "router_order_handworked.json")))
+    x = np.zeros((1, g["H"]), np.float16)
+    for h, v in g["x_nonzero"].items():
+        x[0, int(h)] = v
+    w = np.zeros((g["E"], g["H"]), np.float32)
+    for e, row in enumerate(g["w_nonzero"]):
+        for h, v in row.items():
+            w[e, int(h)] = v
+    ids, wt, lg, _ = run_route(smoe, x, w, None, 1)
+    assert lg[0].tolist() == g["expected_logits"]
+    assert ids[0, 0] == 0
+
+
+def test_route_ties_renorm_and_k_equals_E(smoe):
+    rng = np.random.default_rng(5)
+    x = rng.standard_normal((33, 256)).astype(np.float16)
+    w = (rng.standard_normal((8, 256)) * 0.02).astype(np.float32)
+    w[5] = w[2]          # exact ties between experts 2 and 5
+    w[7] = w[2]
+    for k in (1, 3, 8):
+        for flags in (0, 1):
+            ids, wt, lg, _ = run_route(smoe, x, w, None, k, flags)
+            ref_lg = oracle.router_logits_f32(x, w)
+            ref_ids = oracle.topk_experts(ref_lg, k)
+            assert np.array_equal(ids, ref_ids)
+            ref_w = oracle.routing_weights(ref_lg, ref_ids, renorm=bool(flags))
+            assert np.allclose(wt, ref_w, rtol=W_RTOL, atol=1e-9)
+
+
+def test_route_single_token_and_large_E(smoe):
+    rng = np.random.default_rng(8)
+    x = rng.standard_normal((1, 512)).astype(np.float16)
+    w = (rng.standard_normal((256, 512)) * 0.02).astype(np.float32)
+    ids, wt, lg, _ = run_route(smoe, x, w, None, 8)
+    ref_lg = oracle.router_logits_f32(x, w)
+    assert np.array_equal(lg.view(np.uint32), ref_lg.view(np.uint32))
+    assert np.array_equal(ids, oracle.topk_experts(ref_lg, 8))
+
+
+# ------------------------------------------------------------------ alignment
+
+@pytest.mark.parametrize("E,k,T,seed", [(8, 2, 17, 0), (64, 6, 17, 1), (60, 4, 9, 2),
+                                        (16, 2, 17, 3), (64, 6, 544, 4), (256, 8, 4096, 5),
+                                        (7, 1, 1, 6)])
+def test_align_matches_oracle(smoe, E, k, T, seed):
+    rng = np.random.default_rng(seed)
+    ids = np.stack([rng.permutation(E)[:k] for _ in range(T)]).astype(np.int32)
+    check_align(run_align(smoe, ids, E), oracle.align_by_expert(ids, E))
+
+
+def test_align_edge_cases(smoe):
+    for ids, E in [(np.full((17, 1), 3, np.int32), 8),                   # one expert
+                   (np.zeros((0, 2), np.int32), 8),                      # empty window
+                   (np.array([[0, 9], [-1, 2], [2, 2]], np.int32), 8),   # dropped IDs
+                   (np.tile(np.arange(4, dtype=np.int32), (300, 1)), 4)]:  # k = E
+        check_align(run_align(smoe, ids, E), oracle.align_by_expert(ids, E))
+
+
+def test_align_is_deterministic(smoe):
+    rng = np.random.default_rng(12)
+    ids = rng.integers(0, 64, size=(544, 6)).astype(np.int32)
+    a = run_align(smoe, ids, 64)
+    b = run_align(smoe, ids, 64)
+    for key in a:
+        assert np.array_equal(a[key], b[key])
+
+
+# ------------------------------------------------------------------ ELB
+
+def test_elb_golden_and_clear(smoe):
+    import json, os
+    g = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "elb_handworked.json")))
+    cnt = torch.zeros((g["L"], g["E"]), dtype=torch.int32, device="cuda")
+    ids = dev(np.array(g["ids"], np.int32))
+    plan = torch.empty((g["L"], 3), dtype=torch.int32, device="cuda")
+    pc = torch.empty((g["L"], 3), dtype=torch.int32, device="cuda")
+    smoe.smoe_elb_accumulate_topm(cnt, ids, 0, 3, plan, pc, 0)
+    assert host(cnt).tolist() == g["expected_counts"]
+    assert host(plan).tolist() == g["expected_top3_ids"]
+    assert host(pc).tolist() == g["expected_top3_counts"]
+    plan4 = torch.empty((g["L"], 4), dtype=torch.int32, device="cuda")
+    smoe.smoe_elb_accumulate_topm(cnt, None, 0, 4, plan4, None, smoe.SMOE_ELB_CLEAR_AFTER)
+    assert host(plan4)[0].tolist() == g["expected_top4_ids_layer0"]
+    assert not host(cnt).any()
+    tie = dev(np.array(g["tie_counts"], np.int32))
+    plan1 = torch.empty((1, 3), dtype=torch.int32, device="cuda")
+    smoe.smoe_elb_accumulate_topm(tie, None, 0, 3, plan1, None, 0)
+    assert host(plan1).tolist() == g["tie_expected_top3"]
+
+
+def test_elb_random_layers_and_split_calls(smoe):
+    rng = np.random.default_rng(4)
+    L, E, T, k, M = 26, 64, 17, 6, 32
+    ids = np.stack([np.stack([rng.permutation(E)[:k] for _ in range(T)])
+                    for _ in range(L)]).astype(np.int32)
+    ref = oracle.elb_accumulate(np.zeros((L, E), np.int32), ids, 0)
+    ref_ids, ref_cnt = oracle.elb_topm(ref, M)
+    cnt = torch.zeros((L, E), dtype=torch.int32, device="cuda")
+    plan = torch.empty((L, M), dtype=torch.int32, device="cuda")
+    pc = torch.empty((L, M), dtype=torch.int32, device="cuda")
+    smoe.smoe_elb_accumulate_topm(cnt, dev(ids), 0, M, plan, pc, 0)
+    assert np.array_equal(host(cnt), ref)
+    assert np.array_equal(host(plan), ref_ids) and np.array_equal(host(pc), ref_cnt)
+    # token by token, one layer per call, accumulate only: same counter
+    cnt2 = torch.zeros((L, E), dtype=torch.int32, device="cuda")
+    for t in range(T):
+        for l in range(0, L, 5):
+            smoe.smoe_elb_accumulate_topm(cnt2, dev(np.ascontiguousarray(ids[l:l + 5, t:t + 1])),
+                                          l, 0, None, None, 0)
+    assert np.array_equal(host(cnt2), ref)
+
+
+# ------------------------------------------------------------------ expert FFN
+
+def oracle_slots_int4(L, ids, slots=None):
+    cfg = L.cfg
+
+    def load(e):
+        return (oracle.dequant_int4(L.wg_q[e], L.wg_s[e], cfg.G),
+                oracle.dequant_int4(L.wu_q[e], L.wu_s[e], cfg.G),
+                oracle.dequant_int4(L.wd_q[e], L.wd_s[e], cfg.G))
+    return oracle.routed_ffn_expertwise(L.x, ids, load)
+
+
+def run_w4a16(smoe, x, ids, E, I, G, wg_q, wg_s, wu_q, wu_s, wd_q, wd_s):
+    T, k = ids.shape
+    H = x.shape[1]
+    al = oracle.align_by_expert(ids, E)
+    ws = torch.empty(smoe.smoe_ffn_workspace_bytes(T, k, E, H, I), dtype=torch.uint8,
+                     device="cuda")
+    out = torch.full((T * k, H), float("nan"), dtype=torch.float32, device="cuda")
+    smoe.smoe_w4a16_expert_ffn(dev(x), k, E, I, G, dev(wg_q), dev(wg_s), dev(wu_q), dev(wu_s),
+                               dev(wd_q), dev(wd_s), dev(al["sorted_slots"]),
+                               dev(al["offsets"]), ws, out)
+    return host(out)
+
+
+@pytest.mark.parametrize("name", ["tiny", "dsv2", "qwen"])
+def test_w4a16_ffn_matches_oracle(smoe, name):
+    L = layer(name)
+    cfg = L.cfg
+    ids = oracle.topk_experts(oracle.router_logits_f32(L.x, L.w_router, L.router_bias), cfg.k)
+    got = run_w4a16(smoe, L.x, ids, cfg.E, cfg.I, cfg.G, L.wg_q, L.wg_s, L.wu_q, L.wu_s,
+                    L.wd_q, L.wd_s)
+    ref = oracle_slots_int4(L, ids)
+    assert np.isfinite(got).all()
+    err = row_rel_err(got, ref)
+    assert err <= ROW_TOL, err
+
+
+def _synthetic_int4(E, H, I, G, seed):
+    rng = np.random.default_rng(seed)
+    q = {}
+    for nm, (n, kk) in (("wg", (I, H)), ("wu", (I, H)), ("wd", (H, I))):
+        codes, scales = zip(*[quantize_rtn_int4(
+            (rng.standard_normal((n, kk)) * 0.02).astype(np.float32), G) for _ in range(E)])
+        q[nm + "_q"], q[nm + "_s"] = np.stack(codes), np.stack(scales)
+    return q
+
+
+@pytest.mark.parametrize("E,k,T,H,I,G", [
+    (8, 2, 17, 256, 512, 32),        # G = 32 path
+    (8, 2, 128, 256, 384, 64),       # 32 slots per expert: two 16-slot MFMA groups
+    (4, 2, 150, 256, 256, 128),      # 75 slots per expert: 64-slot chunks, several per expert
+    (16, 1, 1, 384, 256, 128),       # a single token
+    (6, 3, 40, 128, 128, 64),        # minimal sizes, ragged chunks
+])
+def test_w4a16_ffn_shapes(smoe, E, k, T, H, I, G):
+    rng = np.random.default_rng(T * 7 + E)
+    x = rng.standard_normal((T, H)).astype(np.float16)
+    q = _synthetic_int4(E, H, I, G, seed=E + H)
+    ids = np.stack([rng.permutation(E)[:k] for _ in range(T)]).astype(np.int32)
+    got = run_w4a16(smoe, x, ids, E, I, G, q["wg_q"], q["wg_s"], q["wu_q"], q["wu_s"],
+                    q["wd_q"], q["wd_s"])
+
+    def load(e):
+        return tuple(oracle.dequant_int4(q[n + "_q"][e], q[n + "_s"][e], G) for n in ("wg", "wu", "wd"))
+    ref = oracle.routed_ffn_expertwise(x, ids, load)
+    err = row_rel_err(got, ref)
+    assert err <= ROW_TOL, err
+
+
+def test_w4a16_ffn_one_hot_expert(smoe):
+    # every slot on one expert: many chunks of the same expert
+    E, k, T, H, I, G = 8, 1, 300, 256, 256, 64
+    rng = np.random.default_rng(3)
+    x = rng.standard_normal((T, H)).astype(np.float16)
+    q = _synthetic_int4(E, H, I, G, seed=1)
+    ids = np.full((T, k), 6, np.int32)
+    got = run_w4a16(smoe, x, ids, E, I, G, q["wg_q"], q["wg_s"], q["wu_q"], q["wu_s"],
+                    q["wd_q"], q["wd_s"])
+
+    def load(e):
+        return tuple(oracle.dequant_int4(q[n + "_q"][e], q[n + "_s"][e], G) for n in ("wg", "wu", "wd"))
+    assert row_rel_err(got, oracle.routed_ffn_expertwise(x, ids, load)) <= ROW_TOL
+
+
+def run_fp16(smoe, x, ids, E, I, wg, wu, wd):
+    T, k = ids.shape
+    H = x.shape[1]
+    al = oracle.align_by_expert(ids, E)
+    ws = torch.empty(smoe.smoe_ffn_workspace_bytes(T, k, E, H, I), dtype=torch.uint8,
+                     device="cuda")
+    out = torch.full((T * k, H), float("nan"), dtype=torch.float32, device="cuda")
+    smoe.smoe_fp16_expert_ffn(dev(x), k, E, I, dev(wg), dev(wu), dev(wd),
+                              dev(al["sorted_slots"]), dev(al["offsets"]), ws, out)
+    return host(out)
+
+
+def test_fp16_ffn_shared_expert_dsv2(smoe):
+    L = layer("dsv2")
+    T = L.cfg.T
+    ids = np.zeros((T, 1), np.int32)
+    got = run_fp16(smoe, L.x, ids, 1, L.sg16.shape[0], L.sg16[None], L.su16[None], L.sd16[None])
+    ref = oracle.shared_ffn(L.x, L.sg16, L.su16, L.sd16)
+    assert row_rel_err(got, ref) <= ROW_TOL
+
+
+@pytest.mark.parametrize("E,k,T,H,I", [(8, 2, 17, 256, 512), (4, 2, 150, 256, 256),
+                                       (16, 1, 1, 384, 256)])
+def test_fp16_ffn_shapes(smoe, E, k, T, H, I):
+    rng = np.random.default_rng(E * T)
+    x = rng.standard_normal((T, H)).astype(np.float16)
+    wg = (rng.standard_normal((E, I, H)) * 0.02).astype(np.float16)
+    wu = (rng.standard_normal((E, I, H)) * 0.02).astype(np.float16)
+    wd = (rng.standard_normal((E, H, I)) * 0.02).astype(np.float16)
+    ids = np.stack([rng.permutation(E)[:k] for _ in range(T)]).astype(np.int32)
+    got = run_fp16(smoe, x, ids, E, I, wg, wu, wd)
+    ref = oracle.routed_ffn_expertwise(x, ids, lambda e: (wg[e], wu[e], wd[e]))
+    assert row_rel_err(got, ref) <= ROW_TOL
+
+
+def test_phi_draft_and_target(smoe):
+    L = layer("phi")
+    cfg = L.cfg
+    ids = oracle.topk_experts(oracle.router_logits_f32(L.x, L.w_router), cfg.k)
+    flat = ids.ravel()
+    # sample: the slots of three experts (the oracle computes them one by one)
+    experts = sorted(set(flat.tolist()))[:3]
+    sel = np.flatnonzero(np.isin(flat, experts))
+    draft = run_w4a16(smoe, L.x, ids, cfg.E, cfg.I, cfg.G, L.wg_q, L.wg_s, L.wu_q, L.wu_s,
+                      L.wd_q, L.wd_s)
+    target = run_fp16(smoe, L.x, ids, cfg.E, cfg.I, L.wg16, L.wu16, L.wd16)
+    assert np.isfinite(draft).all() and np.isfinite(target).all()
+    for e in experts:
+        s = np.flatnonzero(flat == e)
+        xt = L.x[s // cfg.k].astype(np.float64)
+        ref_d = oracle.swiglu(xt, oracle.dequant_int4(L.wg_q[e], L.wg_s[e], cfg.G),
+                              oracle.dequant_int4(L.wu_q[e], L.wu_s[e], cfg.G),
+                              oracle.dequant_int4(L.wd_q[e], L.wd_s[e], cfg.G))
+        ref_t = oracle.swiglu(xt, L.wg16[e], L.wu16[e], L.wd16[e])
+        assert row_rel_err(draft[s], ref_d) <= ROW_TOL
+        assert row_rel_err(target[s], ref_t) <= ROW_TOL
+    assert len(sel) > 0
+
+
+# ------------------------------------------------------------------ combine
+
+def test_combine_matches_oracle(smoe):
+    rng = np.random.default_rng(31)
+    for T, k, H, shared, gated in [(17, 6, 2048, True, False), (9, 4, 2048, True, True),
+                                   (17, 2, 4096, False, False), (1, 1, 128, False, False)]:
+        so = rng.standard_normal((T * k, H)).astype(np.float32)
+        w = rng.random((T, k)).astype(np.float32)
+        sh = rng.standard_normal((T, H)).astype(np.float32) if shared else None
+        g = rng.random(T).astype(np.float32) if gated else None
+        y = torch.empty((T, H), dtype=torch.float16, device="cuda")
+        smoe.smoe_combine(dev(so), dev(w), None if sh is None else dev(sh),
+                          None if g is None else dev(g), y)
+        _, ref16 = oracle.combine(so, w, sh, g)
+        y64 = oracle.combine(so, w, sh, g)[0]
+        got = host(y).astype(np.float64)
+        # fp16 output: within one fp16 rounding step of the float64 sum
+        assert np.all(np.abs(got - y64) <= np.abs(y64) * 2.0 ** -10 + 1e-6)
+
+
+# ------------------------------------------------------------------ whole layer
+
+@pytest.mark.parametrize("name", ["tiny", "dsv2", "qwen"])
+@pytest.mark.parametrize("side", [False, True])
+def test_layer_draft_matches_oracle(smoe, name, side):
+    from quantized_speculative_expert_amd.layer import DeviceLayer
+    L = layer(name)
+    ref = oracle.moe_layer(L, "draft")
+    d = DeviceLayer(L)
+    d.run(side_stream=torch.cuda.Stream() if side else None)
+    assert np.array_equal(host(d.topk_ids), ref["ids"])
+    assert np.array_equal(host(d.sorted_slots), ref["sorted_slots"])
+    assert int(host(d.n_active)[0]) == int(ref["n_active"])
+    err = row_rel_err(host(d.y), ref["y64"])
+    assert err <= ROW_TOL, err
+    if L.cfg.elb_M:
+        ref_cnt = oracle.elb_accumulate(np.zeros((1, L.cfg.E), np.int32), ref["ids"][None], 0)
+        pid, pc = oracle.elb_topm(ref_cnt, L.cfg.elb_M)
+        assert np.array_equal(host(d.elb_counts), ref_cnt)
+        assert np.array_equal(host(d.plan_ids), pid) and np.array_equal(host(d.plan_counts), pc)
+
+
+def test_layer_graph_replay_matches_eager(smoe):
+    from quantized_speculative_expert_amd.layer import DeviceLayer
+    L = layer("dsv2")
+    d = DeviceLayer(L)
+    d.run(elb=False)
+    eager = host(d.y).copy()
+    side = torch.cuda.Stream()
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            d.run(elb=False, side_stream=side)
+    torch.cuda.current_stream().wait_stream(s)
+    for _ in range(3):
+        d.y.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(host(d.y), eager)
