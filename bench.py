@@ -1,0 +1,306 @@
+#!/usr/bin/env python3
+"""Throughput of the routed-expert MoE layer over a speculative window, one MI355X.
+
+Default workload: the DeepSeek-V2-Lite-shaped draft layer over a K=16 window
+(17 tokens): 64 routed experts, softmax top-6, hidden 2048, intermediate 1408,
+INT4 group-128 routed weights with fp16 scales, two always-on FP16 shared
+experts, and the activation counter (ELB) with a top-32 plan.
+
+One step = one pass of the whole hot path over one window, every stage in the
+HIP library: FP16 shared experts, router top-k, alignment by expert, ELB
+accumulate + top-M, fused W4A16 routed-expert FFN, weighted combine. A step is
+captured as one HIP graph per weight copy; the copies are rotated (more than
+1 GiB in total, above the 256 MB last-level cache) so every step streams its
+weights from HBM. Inputs are resident in HBM before the timed region starts.
+
+Printed: one JSON line with tokens/s (whole job), ms per step, the layer's
+achieved HBM bandwidth, a roofline entry for the dominant call (the fused
+W4A16 expert FFN, timed with HIP events on the stream it runs on) and the CPU
+reference timed on this host's cores on a bounded sample.
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "W4A16 MoE-layer tokens/sec + achieved HBM GB/s fraction, K=16 window"
+PEAK_HBM_GBPS = 8000.0          # MI355X HBM3E, vendor figure
+MIN_ROTATION_BYTES = 1 << 30    # rotate weight copies over at least this many bytes
+PROFILES = os.path.join(ROOT, "profiles")
+FFN_SOURCES = [os.path.join(ROOT, "quantized_speculative_expert_amd", "csrc", f)
+               for f in ("ffn.hip", "smoe_internal.hpp")]
+
+
+def log(msg: str) -> None:
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def parse_args():
+    p = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=2000, help="timed steps")
+    p.add_argument("--warmup", type=int, default=100, help="untimed warmup steps")
+    p.add_argument("--config", default="dsv2", help="workload shape (default dsv2)")
+    p.add_argument("--copies", type=int, default=0,
+                   help="weight copies to rotate (0 = enough for >= 1 GiB)")
+    p.add_argument("--no-side-stream", action="store_true",
+                   help="run the shared experts on the main stream instead of a side branch")
+    p.add_argument("--cpu-reps", type=int, default=2,
+                   help="full layers the CPU reference runs for cpu_baseline (0 = skip)")
+    return p.parse_args()
+
+
+# ----------------------------------------------------------------------------- bytes
+
+def _nbytes(t) -> int:
+    return 0 if t is None else t.numel() * t.element_size()
+
+
+def expert_bytes(d) -> int:
+    """Bytes of one routed expert's weights as streamed by the kernels."""
+    return sum(_nbytes(t) for t in (d.wg_q, d.wg_s, d.wu_q, d.wu_s, d.wd_q, d.wd_s)) // d.cfg.E
+
+
+def layer_bytes(d, n_active: int) -> dict:
+    """Algorithmic HBM bytes of one layer step (each tensor read or written once).
+
+    Routed: the codes and scales of the distinct experts the window touches.
+    Shared: the FP16 shared experts. Router: its weight matrix (and bias / gate
+    vector). Activations: x read, y written. Routing metadata, the ELB counter
+    and intermediates (h, per-slot outputs) are below 0.5 % and not counted.
+    """
+    c = d.cfg
+    routed = n_active * expert_bytes(d)
+    shared = sum(_nbytes(t) for t in (d.sg16, d.su16, d.sd16))
+    router = sum(_nbytes(t) for t in (d.w_router, d.router_bias, d.shared_gate_w))
+    act = 2 * c.T * c.H * 2
+    return {"routed": routed, "shared": shared, "router": router, "activations": act,
+            "total": routed + shared + router + act}
+
+
+def ffn_bytes(d, n_active: int) -> int:
+    """Algorithmic bytes of one fused W4A16 expert-FFN call: touched experts'
+    codes + scales, x read once, per-slot fp32 outputs written once."""
+    c = d.cfg
+    return n_active * expert_bytes(d) + c.T * c.H * 2 + c.S * c.H * 4
+
+
+# ----------------------------------------------------------------------------- traffic
+
+def source_digest() -> str:
+    h = hashlib.sha256()
+    for f in FFN_SOURCES:
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def recorded_traffic(config: str):
+    """HBM bytes per FFN call from the committed rocprofv3 counter summary.
+
+    Returns None when no summary exists for this workload or when the kernel
+    sources changed since the counters were taken.
+    """
+    path = os.path.join(PROFILES, f"w4a16_expert_ffn_{config}_traffic.md")
+    if not os.path.exists(path):
+        return None
+    m = re.search(r"^TRAFFIC_JSON: (\{.*\})\s*$", open(path).read(), re.M)
+    if not m:
+        return None
+    rec = json.loads(m.group(1))
+    if rec.get("source_digest") != source_digest():
+        return None
+    return rec.get("bytes_per_call")
+
+
+# ----------------------------------------------------------------------------- CPU leg
+
+def cpu_baseline(cfg_name: str, reps: int):
+    """The CPU reference (oracle) timed on this host on `reps` full layers."""
+    import numpy as np
+    from threadpoolctl import threadpool_info
+
+    import oracle
+    from workload import get_config, make_layer
+
+    cfg = get_config(cfg_name)
+    L = make_layer(cfg, seed=0)
+    t0 = time.perf_counter()
+    for _ in range(reps):
+        r = oracle.moe_layer(L, "draft")
+        if cfg.elb_M:
+            cnt = oracle.elb_accumulate(np.zeros((1, cfg.E), np.int32), r["ids"][None], 0)
+            oracle.elb_topm(cnt, cfg.elb_M)
+    dt = time.perf_counter() - t0
+    blas = [i.get("num_threads", 1) for i in threadpool_info()]
+    cores = max(blas) if blas else 1
+    return {"value": cfg.T * reps / dt, "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "sample": (f"{reps} full {cfg.name} layers of {cfg.T} tokens (route, align, ELB "
+                       f"top-{cfg.elb_M}, INT4 dequantise + float64 SwiGLU of the touched "
+                       f"experts, shared experts, combine) in {dt:.1f} s; BLAS matmuls on "
+                       f"{cores} threads, the rest single-threaded NumPy"),
+            "ms_per_layer": 1e3 * dt / reps}
+
+
+# ----------------------------------------------------------------------------- GPU leg
+
+def percentiles(xs):
+    import numpy as np
+    a = np.asarray(xs, dtype=float)
+    return {"median": float(np.median(a)), "p10": float(np.percentile(a, 10)),
+            "p90": float(np.percentile(a, 90)), "mean": float(a.mean())}
+
+
+def main() -> int:
+    args = parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only: the layer runs on a single MI355X and this "
+              f"build has no multi-GPU path (asked for --gpus {args.gpus}, WORLD_SIZE {world})",
+              file=sys.stderr)
+        return 2
+
+    import torch
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU (torch.cuda.is_available() is False)", file=sys.stderr)
+        return 1
+    from quantized_speculative_expert_amd.layer import DeviceLayer
+    from workload import get_config, make_layer
+
+    cfg = get_config(args.config)
+    if cfg.layers != 1:
+        print(f"config {cfg.name} is a {cfg.layers}-layer stack; bench.py times single layers",
+              file=sys.stderr)
+        return 2
+    log(f"generating {cfg.name} inputs (seed 0)")
+    inp = make_layer(cfg, seed=0, want_fp16=False)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    base = DeviceLayer(inp, device=dev, with_target=False)
+    del inp
+    wbytes = base.weight_bytes()
+    copies = args.copies or max(2, -(-MIN_ROTATION_BYTES // wbytes))
+    layers = [base] + [base.with_weight_copy() for _ in range(copies - 1)]
+    log(f"{copies} weight copies x {wbytes / 2**20:.1f} MiB resident")
+
+    side = None if args.no_side_stream else torch.cuda.Stream(device=dev)
+    use_elb = cfg.elb_M > 0
+
+    # eager run once (checks every call), then capture one graph per copy
+    for d in layers:
+        d.run(elb=use_elb, side_stream=side)
+    torch.cuda.synchronize()
+    cap = torch.cuda.Stream(device=dev)
+    cap.wait_stream(torch.cuda.current_stream())
+    step_graphs, ffn_graphs = [], []
+    with torch.cuda.stream(cap):
+        for d in layers:
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=cap):
+                d.run(elb=use_elb, side_stream=side)
+            step_graphs.append(g)
+            g2 = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g2, stream=cap):
+                d.routed_ffn()
+            ffn_graphs.append(g2)
+    torch.cuda.current_stream().wait_stream(cap)
+    torch.cuda.synchronize()
+
+    stream = torch.cuda.current_stream()
+    log(f"warmup {args.warmup} steps")
+    for i in range(args.warmup):
+        step_graphs[i % copies].replay()
+    torch.cuda.synchronize()
+
+    # ---- timed region: exactly `steps` layer steps
+    K = args.steps
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(K + 1)]
+    log(f"timing {K} steps")
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    evs[0].record(stream)
+    for i in range(K):
+        step_graphs[i % copies].replay()
+        evs[i + 1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    step_us = [1e3 * evs[i].elapsed_time(evs[i + 1]) for i in range(K)]
+    gpu_total_ms = evs[0].elapsed_time(evs[K])
+
+    n_active = int(base.n_active.item())
+    lb = layer_bytes(base, n_active)
+    ms_per_step = 1e3 * wall / K
+    tokens_per_s = cfg.T * K / wall
+    layer_gbps = lb["total"] * K / wall / 1e9
+
+    # ---- dominant call: fused W4A16 expert FFN (two launches), HIP events on its stream
+    log(f"timing {K} W4A16 expert-FFN calls")
+    fe = [torch.cuda.Event(enable_timing=True) for _ in range(K + 1)]
+    torch.cuda.synchronize()
+    fe[0].record(stream)
+    for i in range(K):
+        ffn_graphs[i % copies].replay()
+        fe[i + 1].record(stream)
+    torch.cuda.synchronize()
+    ffn_us = [1e3 * fe[i].elapsed_time(fe[i + 1]) for i in range(K)]
+    ffn_stats = percentiles(ffn_us)
+    fb = ffn_bytes(base, n_active)
+    achieved = fb / (ffn_stats["mean"] * 1e3)  # bytes/ns = GB/s
+    traffic = recorded_traffic(cfg.name)
+    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBPS,
+                "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBPS, 4),
+                "traffic": traffic, "kernel": "smoe_w4a16_expert_ffn (ffn_kernel stage 1 + 2)",
+                "bytes_per_launch": fb, "us_per_launch": round(ffn_stats["mean"], 2)}
+
+    cpu = None
+    if args.cpu_reps > 0:
+        log(f"CPU reference on {args.cpu_reps} layers")
+        cpu = cpu_baseline(cfg.name, args.cpu_reps)
+
+    out = {
+        "metric": METRIC,
+        "value": round(tokens_per_s, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16",
+        "data": "synthetic",
+        "config": {
+            "workload": (f"{cfg.name}: {cfg.description}; seed 0; one graph per step, "
+                         f"{copies} rotated weight copies"),
+            "T": cfg.T, "E": cfg.E, "k": cfg.k, "H": cfg.H, "I": cfg.I, "G": cfg.G,
+            "shared_I": cfg.shared_I, "elb_M": cfg.elb_M, "weights": "int4 g%d + fp16 scales" % cfg.G,
+            "side_stream": side is not None,
+        },
+        "hbm_gbps": round(layer_gbps, 1),
+        "hbm_frac": round(layer_gbps / PEAK_HBM_GBPS, 4),
+        "layer_us": {k_: round(v, 2) for k_, v in percentiles(step_us).items()},
+        "layer_us_gpu_mean": round(1e3 * gpu_total_ms / K, 2),
+        "ffn_us": {k_: round(v, 2) for k_, v in ffn_stats.items()},
+        "n_active": n_active,
+        "layer_bytes": lb,
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -16,6 +16,7 @@ and the routed experts.
 
 from __future__ import annotations
 
+import copy
 from typing import Optional
 
 import numpy as np
@@ -85,6 +86,29 @@ class DeviceLayer:
         M = max(cfg.elb_M, 0)
         self.plan_ids = torch.empty((elb_layers, max(M, 1)), **i32)
         self.plan_counts = torch.empty((elb_layers, max(M, 1)), **i32)
+
+    _WEIGHTS = ("w_router", "router_bias", "shared_gate_w", "wg_q", "wg_s", "wu_q", "wu_s",
+                "wd_q", "wd_s", "wg16", "wu16", "wd16", "sg16", "su16", "sd16")
+
+    def weight_bytes(self) -> int:
+        """Device bytes held by this layer's weights (router, routed, shared)."""
+        return sum(t.numel() * t.element_size() for t in
+                   (getattr(self, n) for n in self._WEIGHTS) if t is not None)
+
+    def with_weight_copy(self) -> "DeviceLayer":
+        """A runner over fresh device copies of every weight tensor.
+
+        Inputs, outputs and scratch buffers are shared with this runner (so
+        the two must not run concurrently); only the weights get new
+        addresses. Used to rotate several copies so that each call reads its
+        weights from HBM rather than from a cache holding the previous call's.
+        """
+        other = copy.copy(self)
+        for n in self._WEIGHTS:
+            t = getattr(self, n)
+            if t is not None:
+                setattr(other, n, t.clone())
+        return other
 
     # ---------------------------------------------------------------- steps
     def route(self, stream=None) -> None:
