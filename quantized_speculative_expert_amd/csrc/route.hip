@@ -6,13 +6,15 @@
 // full precision (hybrid-precision layout; design notes, "Speculative
 // Inference Controller").
 //
-// One workgroup (16 waves) per tile of `tt` tokens. The x tile is staged in
-// LDS as float32; each wave owns experts e = wave, wave+16, ... and forms
-// the float32 dot product in the stated order: lane l keeps the partial sum
-// of the terms h = 64c + l for c = 0, 1, ... (multiply and add rounded
-// separately, contraction disabled), then the halving tree
-// p[l] += p[l + off], off = 32 .. 1, is done with shuffles. One wave per
-// token then takes the top-k by repeated wave-wide maxima of a 64-bit key
+// One workgroup of 8 waves per token. The token's x row is staged in LDS as
+// float32; wave w owns experts e = w, w + 8, ... and forms the float32 dot
+// product in the stated order: lane l keeps the partial sum of the terms
+// h = 64c + l for c = 0, 1, ... (multiply and add rounded separately,
+// contraction disabled), then the halving tree p[l] += p[l + off],
+// off = 32 .. 1, is done with shuffles. A wave issues the router-row loads
+// of two experts (up to 32 chunks each) before using any of them, so the
+// row reads overlap instead of waiting one latency per chunk. One wave then
+// takes the top-k by repeated wave-wide maxima of a 64-bit key
 // (order-preserving float bits, then inverted expert ID, so ties go to the
 // lower ID) and the softmax weights over all E logits.
 #include "smoe_internal.hpp"
@@ -20,9 +22,9 @@
 namespace smoe {
 namespace {
 
-constexpr int kRouteThreads = 1024;
+constexpr int kRouteThreads = 512;
 constexpr int kRouteWaves = kRouteThreads / kWave;
-constexpr int kMaxTT = 4;
+constexpr int kSlice = 32;  // chunks of 64 per load batch (2048 h)
 
 struct RouteArgs {
   const _Float16* x;
@@ -33,7 +35,7 @@ struct RouteArgs {
   float* wout;
   float* logits;
   float* gate;
-  int T, H, E, k, flags, tt;
+  int T, H, E, k, flags;
 };
 
 // Increasing map float -> uint32 with -0.0 and +0.0 sent to the same key.
@@ -46,59 +48,69 @@ __device__ __forceinline__ uint32_t order_key(float f) {
 __global__ __launch_bounds__(kRouteThreads) void route_kernel(RouteArgs a) {
 #pragma clang fp contract(off)
   extern __shared__ float smem[];
-  const int t0 = blockIdx.x * a.tt;
-  const int nt = min(a.tt, a.T - t0);
+  const int t = blockIdx.x;
   const int H = a.H, E = a.E;
-  float* xs = smem;                   // [tt][H]
-  float* lg = smem + a.tt * H;        // [tt][E + 1]; column E = shared-gate dot
+  float* xs = smem;        // [H]
+  float* lg = smem + H;    // [E + 1]; entry E = shared-gate dot
   const int wave = threadIdx.x / kWave;
   const int lane = threadIdx.x % kWave;
 
-  for (int i = threadIdx.x; i < nt * H; i += kRouteThreads)
-    xs[i] = static_cast<float>(a.x[static_cast<size_t>(t0) * H + i]);
+  for (int i = threadIdx.x; i < H; i += kRouteThreads)
+    xs[i] = static_cast<float>(a.x[static_cast<size_t>(t) * H + i]);
   __syncthreads();
 
   const bool want_gate = a.gate_w != nullptr && a.gate != nullptr;
   const int nrows = E + (want_gate ? 1 : 0);
   const int nc = H / kWave;
-  for (int e = wave; e < nrows; e += kRouteWaves) {
-    const float* wr = e < E ? a.w + static_cast<size_t>(e) * H : a.gate_w;
-    float p[kMaxTT] = {0.0f, 0.0f, 0.0f, 0.0f};
-    for (int c = 0; c < nc; ++c) {
-      const float wv = wr[c * kWave + lane];
+  auto row_ptr = [&](int e) { return e < E ? a.w + static_cast<size_t>(e) * H : a.gate_w; };
+  // experts e0 = wave + 2*kRouteWaves*j and e1 = e0 + kRouteWaves, two at a time
+  for (int e0 = wave; e0 < nrows; e0 += 2 * kRouteWaves) {
+    const int e1 = e0 + kRouteWaves;
+    const bool has1 = e1 < nrows;
+    const float* w0 = row_ptr(e0);
+    const float* w1 = has1 ? row_ptr(e1) : w0;
+    float p0 = 0.0f, p1 = 0.0f;
+    for (int c0 = 0; c0 < nc; c0 += kSlice) {
+      float v0[kSlice], v1[kSlice];
 #pragma unroll
-      for (int q = 0; q < kMaxTT; ++q) {
-        if (q < nt) {
-          const float prod = xs[q * H + c * kWave + lane] * wv;
-          p[q] = p[q] + prod;
+      for (int j = 0; j < kSlice; ++j) {
+        const int c = min(c0 + j, nc - 1);
+        v0[j] = w0[c * kWave + lane];
+        v1[j] = w1[c * kWave + lane];
+      }
+#pragma unroll
+      for (int j = 0; j < kSlice; ++j) {
+        if (c0 + j < nc) {
+          const float xv = xs[(c0 + j) * kWave + lane];
+          const float q0 = xv * v0[j];
+          const float q1 = xv * v1[j];
+          p0 = p0 + q0;
+          p1 = p1 + q1;
         }
       }
     }
 #pragma unroll
-    for (int q = 0; q < kMaxTT; ++q) {
-#pragma unroll
-      for (int off = kWave / 2; off >= 1; off >>= 1) {
-        const float other = __shfl_down(p[q], off, kWave);
-        p[q] = p[q] + other;
-      }
+    for (int off = kWave / 2; off >= 1; off >>= 1) {
+      const float o0 = __shfl_down(p0, off, kWave);
+      const float o1 = __shfl_down(p1, off, kWave);
+      p0 = p0 + o0;
+      p1 = p1 + o1;
     }
     if (lane == 0) {
-#pragma unroll
-      for (int q = 0; q < kMaxTT; ++q) {
-        if (q < nt) {
-          float v = p[q];
-          if (e < E && a.bias != nullptr) v = v + a.bias[e];
-          lg[q * (E + 1) + e] = v;
-        }
+      float v = p0;
+      if (e0 < E && a.bias != nullptr) v = v + a.bias[e0];
+      lg[e0] = v;
+      if (has1) {
+        float u = p1;
+        if (e1 < E && a.bias != nullptr) u = u + a.bias[e1];
+        lg[e1] = u;
       }
     }
   }
   __syncthreads();
 
-  if (wave >= nt) return;
-  const int q = wave;
-  const int t = t0 + q;
-  const float* l = lg + q * (E + 1);
+  if (wave != 0) return;
+  const float* l = lg;
 
   uint64_t key[kMaxE / kWave];
 #pragma unroll
@@ -172,12 +184,7 @@ extern "C" smoe_status smoe_route_topk(const void* x, const float* w_router,
   SMOE_REQUIRE(static_cast<long long>(T) * k < (1ll << 24), SMOE_EUNSUPPORTED,
                "route_topk: T*k must be below 2^24");
 
-  // Token tile: several tokens per workgroup only for long windows, so short
-  // windows spread over more compute units; LDS holds tt*H + tt*(E+1) floats.
-  int tt = T >= 256 ? kMaxTT : 1;
-  while (tt > 1 && (tt * H + tt * (E + 1)) * 4 > 64 * 1024) --tt;
-  const size_t lds = static_cast<size_t>(tt) * (H + E + 1) * sizeof(float);
-  SMOE_REQUIRE(lds <= 64 * 1024, SMOE_EUNSUPPORTED, "route_topk: H too large for one token tile");
+  const size_t lds = static_cast<size_t>(H + E + 1) * sizeof(float);
 
   RouteArgs a;
   a.x = static_cast<const _Float16*>(x);
@@ -193,8 +200,6 @@ extern "C" smoe_status smoe_route_topk(const void* x, const float* w_router,
   a.E = E;
   a.k = k;
   a.flags = flags;
-  a.tt = tt;
-  const int grid = (T + tt - 1) / tt;
-  hipLaunchKernelGGL(route_kernel, dim3(grid), dim3(kRouteThreads), lds, as_stream(stream), a);
+  hipLaunchKernelGGL(route_kernel, dim3(T), dim3(kRouteThreads), lds, as_stream(stream), a);
   return check_launch("route_topk");
 }

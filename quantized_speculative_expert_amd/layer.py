@@ -68,7 +68,7 @@ class DeviceLayer:
         self.active = torch.empty(E, **i32)
         self.n_active = torch.empty(1, **i32)
         ws = _lib.smoe_ffn_workspace_bytes(T, k, E, H, I)
-        self.workspace = torch.empty(ws, dtype=torch.uint8, device=d)
+        self.workspace = torch.zeros(ws, dtype=torch.uint8, device=d)
         self.slot_out = torch.empty((S, H), **f32)
         self.y = torch.empty((T, H), dtype=torch.float16, device=d)
         self.shared_gate = torch.empty(T, **f32) if self.shared_gate_w is not None else None
@@ -76,7 +76,7 @@ class DeviceLayer:
             Is = self.sg16.shape[0]
             self.shared_I = Is
             self.shared_out = torch.empty((T, H), **f32)
-            self.shared_ws = torch.empty(_lib.smoe_ffn_workspace_bytes(T, 1, 1, H, Is),
+            self.shared_ws = torch.zeros(_lib.smoe_ffn_workspace_bytes(T, 1, 1, H, Is),
                                          dtype=torch.uint8, device=d)
             self.shared_slots = torch.arange(T, **i32)
             self.shared_offsets = torch.tensor([0, T], **i32)

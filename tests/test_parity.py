@@ -249,7 +249,7 @@ def run_w4a16(smoe, x, ids, E, I, G, wg_q, wg_s, wu_q, wu_s, wd_q, wd_s):
     T, k = ids.shape
     H = x.shape[1]
     al = oracle.align_by_expert(ids, E)
-    ws = torch.empty(smoe.smoe_ffn_workspace_bytes(T, k, E, H, I), dtype=torch.uint8,
+    ws = torch.zeros(smoe.smoe_ffn_workspace_bytes(T, k, E, H, I), dtype=torch.uint8,
                      device="cuda")
     out = torch.full((T * k, H), float("nan"), dtype=torch.float32, device="cuda")
     smoe.smoe_w4a16_expert_ffn(dev(x), k, E, I, G, dev(wg_q), dev(wg_s), dev(wu_q), dev(wu_s),
@@ -322,7 +322,7 @@ def run_fp16(smoe, x, ids, E, I, wg, wu, wd):
     T, k = ids.shape
     H = x.shape[1]
     al = oracle.align_by_expert(ids, E)
-    ws = torch.empty(smoe.smoe_ffn_workspace_bytes(T, k, E, H, I), dtype=torch.uint8,
+    ws = torch.zeros(smoe.smoe_ffn_workspace_bytes(T, k, E, H, I), dtype=torch.uint8,
                      device="cuda")
     out = torch.full((T * k, H), float("nan"), dtype=torch.float32, device="cuda")
     smoe.smoe_fp16_expert_ffn(dev(x), k, E, I, dev(wg), dev(wu), dev(wd),
@@ -433,9 +433,14 @@ def test_layer_graph_replay_matches_eager(smoe):
         with torch.cuda.graph(g, stream=s):
             d.run(elb=False, side_stream=side)
     torch.cuda.current_stream().wait_stream(s)
+    ids_eager = host(d.topk_ids).copy()
     for _ in range(3):
         d.y.zero_()
+        d.topk_ids.fill_(-1)
         torch.cuda.synchronize()
         g.replay()
         torch.cuda.synchronize()
-        assert np.array_equal(host(d.y), eager)
+        assert np.array_equal(host(d.topk_ids), ids_eager)
+        # split-K tiles add fp32 partial sums with device atomics, so the
+        # float output may differ from the eager run in the last bits
+        assert row_rel_err(host(d.y), eager) <= 1e-3
