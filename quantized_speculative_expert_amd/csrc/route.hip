@@ -12,7 +12,7 @@
 // h = 64c + l for c = 0, 1, ... (multiply and add rounded separately,
 // contraction disabled), then the halving tree p[l] += p[l + off],
 // off = 32 .. 1, is done with shuffles. A wave issues the router-row loads
-// of two experts (up to 32 chunks each) before using any of them, so the
+// of four experts (up to 32 chunks each) before using any of them, so the
 // row reads overlap instead of waiting one latency per chunk. One wave then
 // takes the top-k by repeated wave-wide maxima of a 64-bit key
 // (order-preserving float bits, then inverted expert ID, so ties go to the
@@ -63,47 +63,58 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(RouteArgs a) {
   const int nrows = E + (want_gate ? 1 : 0);
   const int nc = H / kWave;
   auto row_ptr = [&](int e) { return e < E ? a.w + static_cast<size_t>(e) * H : a.gate_w; };
-  // experts e0 = wave + 2*kRouteWaves*j and e1 = e0 + kRouteWaves, two at a time
-  for (int e0 = wave; e0 < nrows; e0 += 2 * kRouteWaves) {
-    const int e1 = e0 + kRouteWaves;
-    const bool has1 = e1 < nrows;
-    const float* w0 = row_ptr(e0);
-    const float* w1 = has1 ? row_ptr(e1) : w0;
-    float p0 = 0.0f, p1 = 0.0f;
+  // experts e = wave + kRouteWaves * (kPerRound * j + i), kPerRound at a time:
+  // all their row loads of a slice go out before any is used
+  constexpr int kPerRound = 4;
+  for (int e0 = wave; e0 < nrows; e0 += kPerRound * kRouteWaves) {
+    const float* wr[kPerRound];
+    bool has[kPerRound];
+#pragma unroll
+    for (int i = 0; i < kPerRound; ++i) {
+      const int e = e0 + i * kRouteWaves;
+      has[i] = e < nrows;
+      wr[i] = row_ptr(has[i] ? e : e0);
+    }
+    float p[kPerRound];
+#pragma unroll
+    for (int i = 0; i < kPerRound; ++i) p[i] = 0.0f;
     for (int c0 = 0; c0 < nc; c0 += kSlice) {
-      float v0[kSlice], v1[kSlice];
+      float v[kPerRound][kSlice];
 #pragma unroll
       for (int j = 0; j < kSlice; ++j) {
         const int c = min(c0 + j, nc - 1);
-        v0[j] = w0[c * kWave + lane];
-        v1[j] = w1[c * kWave + lane];
+#pragma unroll
+        for (int i = 0; i < kPerRound; ++i) v[i][j] = wr[i][c * kWave + lane];
       }
 #pragma unroll
       for (int j = 0; j < kSlice; ++j) {
         if (c0 + j < nc) {
           const float xv = xs[(c0 + j) * kWave + lane];
-          const float q0 = xv * v0[j];
-          const float q1 = xv * v1[j];
-          p0 = p0 + q0;
-          p1 = p1 + q1;
+#pragma unroll
+          for (int i = 0; i < kPerRound; ++i) {
+            const float prod = xv * v[i][j];
+            p[i] = p[i] + prod;
+          }
         }
       }
     }
 #pragma unroll
     for (int off = kWave / 2; off >= 1; off >>= 1) {
-      const float o0 = __shfl_down(p0, off, kWave);
-      const float o1 = __shfl_down(p1, off, kWave);
-      p0 = p0 + o0;
-      p1 = p1 + o1;
+#pragma unroll
+      for (int i = 0; i < kPerRound; ++i) {
+        const float o = __shfl_down(p[i], off, kWave);
+        p[i] = p[i] + o;
+      }
     }
     if (lane == 0) {
-      float v = p0;
-      if (e0 < E && a.bias != nullptr) v = v + a.bias[e0];
-      lg[e0] = v;
-      if (has1) {
-        float u = p1;
-        if (e1 < E && a.bias != nullptr) u = u + a.bias[e1];
-        lg[e1] = u;
+#pragma unroll
+      for (int i = 0; i < kPerRound; ++i) {
+        const int e = e0 + i * kRouteWaves;
+        if (has[i]) {
+          float v = p[i];
+          if (e < E && a.bias != nullptr) v = v + a.bias[e];
+          lg[e] = v;
+        }
       }
     }
   }
