@@ -53,8 +53,9 @@ def parse_args():
     p.add_argument("--config", default="dsv2", help="workload shape (default dsv2)")
     p.add_argument("--copies", type=int, default=0,
                    help="weight copies to rotate (0 = enough for >= 1 GiB)")
-    p.add_argument("--no-side-stream", action="store_true",
-                   help="run the shared experts on the main stream instead of a side branch")
+    p.add_argument("--shared", choices=("fused", "separate", "side"), default="fused",
+                   help="shared experts inside the routed FFN launches (fused), as a call of "
+                        "their own on the main stream (separate) or on a side stream (side)")
     p.add_argument("--cpu-reps", type=int, default=2,
                    help="full layers the CPU reference runs for cpu_baseline (0 = skip)")
     return p.parse_args()
@@ -88,11 +89,15 @@ def layer_bytes(d, n_active: int) -> dict:
             "total": routed + shared + router + act}
 
 
-def ffn_bytes(d, n_active: int) -> int:
-    """Algorithmic bytes of one fused W4A16 expert-FFN call: touched experts'
-    codes + scales, x read once, per-slot fp32 outputs written once."""
+def ffn_bytes(d, n_active: int, with_shared: bool) -> int:
+    """Algorithmic bytes of one W4A16 expert-FFN call: touched experts' codes
+    + scales, x read once, per-slot fp32 outputs written once; with the
+    shared experts also their FP16 weights and fp32 outputs."""
     c = d.cfg
-    return n_active * expert_bytes(d) + c.T * c.H * 2 + c.S * c.H * 4
+    b = n_active * expert_bytes(d) + c.T * c.H * 2 + c.S * c.H * 4
+    if with_shared and d.shared_out is not None:
+        b += sum(_nbytes(t) for t in (d.sg16, d.su16, d.sd16)) + c.T * c.H * 4
+    return b
 
 
 # ----------------------------------------------------------------------------- traffic
@@ -105,11 +110,11 @@ def source_digest() -> str:
     return h.hexdigest()[:16]
 
 
-def recorded_traffic(config: str):
+def recorded_traffic(config: str, shared_mode: str):
     """HBM bytes per FFN call from the committed rocprofv3 counter summary.
 
-    Returns None when no summary exists for this workload or when the kernel
-    sources changed since the counters were taken.
+    Returns None when no summary exists for this workload and shared-expert
+    mode, or when the kernel sources changed since the counters were taken.
     """
     path = os.path.join(PROFILES, f"w4a16_expert_ffn_{config}_traffic.md")
     if not os.path.exists(path):
@@ -118,7 +123,7 @@ def recorded_traffic(config: str):
     if not m:
         return None
     rec = json.loads(m.group(1))
-    if rec.get("source_digest") != source_digest():
+    if rec.get("source_digest") != source_digest() or rec.get("shared") != shared_mode:
         return None
     return rec.get("bytes_per_call")
 
@@ -194,12 +199,16 @@ def main() -> int:
     layers = [base] + [base.with_weight_copy() for _ in range(copies - 1)]
     log(f"{copies} weight copies x {wbytes / 2**20:.1f} MiB resident")
 
-    side = None if args.no_side_stream else torch.cuda.Stream(device=dev)
+    fused = args.shared == "fused"
+    side = torch.cuda.Stream(device=dev) if args.shared == "side" else None
     use_elb = cfg.elb_M > 0
+
+    def step(d):
+        d.run(elb=use_elb, fuse_shared=fused, side_stream=side)
 
     # eager run once (checks every call), then capture one graph per copy
     for d in layers:
-        d.run(elb=use_elb, side_stream=side)
+        step(d)
     torch.cuda.synchronize()
     cap = torch.cuda.Stream(device=dev)
     cap.wait_stream(torch.cuda.current_stream())
@@ -208,11 +217,11 @@ def main() -> int:
         for d in layers:
             g = torch.cuda.CUDAGraph()
             with torch.cuda.graph(g, stream=cap):
-                d.run(elb=use_elb, side_stream=side)
+                step(d)
             step_graphs.append(g)
             g2 = torch.cuda.CUDAGraph()
             with torch.cuda.graph(g2, stream=cap):
-                d.routed_ffn()
+                d.routed_ffn(with_shared=fused)
             ffn_graphs.append(g2)
     torch.cuda.current_stream().wait_stream(cap)
     torch.cuda.synchronize()
@@ -244,7 +253,8 @@ def main() -> int:
     tokens_per_s = cfg.T * K / wall
     layer_gbps = lb["total"] * K / wall / 1e9
 
-    # ---- dominant call: fused W4A16 expert FFN (two launches), HIP events on its stream
+    # ---- dominant call: W4A16 expert FFN (two launches; with the shared
+    # experts when fused), HIP events on the stream it runs on
     log(f"timing {K} W4A16 expert-FFN calls")
     fe = [torch.cuda.Event(enable_timing=True) for _ in range(K + 1)]
     torch.cuda.synchronize()
@@ -255,12 +265,14 @@ def main() -> int:
     torch.cuda.synchronize()
     ffn_us = [1e3 * fe[i].elapsed_time(fe[i + 1]) for i in range(K)]
     ffn_stats = percentiles(ffn_us)
-    fb = ffn_bytes(base, n_active)
+    fb = ffn_bytes(base, n_active, fused)
     achieved = fb / (ffn_stats["mean"] * 1e3)  # bytes/ns = GB/s
-    traffic = recorded_traffic(cfg.name)
+    traffic = recorded_traffic(cfg.name, args.shared)
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBPS,
                 "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBPS, 4),
-                "traffic": traffic, "kernel": "smoe_w4a16_expert_ffn (ffn_kernel stage 1 + 2)",
+                "traffic": traffic,
+                "kernel": ("smoe_w4a16_expert_ffn (ffn_kernel stage 1 + 2, routed"
+                           + (" + shared experts)" if fused else " experts)")),
                 "bytes_per_launch": fb, "us_per_launch": round(ffn_stats["mean"], 2)}
 
     cpu = None
@@ -286,7 +298,7 @@ def main() -> int:
                          f"{copies} rotated weight copies"),
             "T": cfg.T, "E": cfg.E, "k": cfg.k, "H": cfg.H, "I": cfg.I, "G": cfg.G,
             "shared_I": cfg.shared_I, "elb_M": cfg.elb_M, "weights": "int4 g%d + fp16 scales" % cfg.G,
-            "side_stream": side is not None,
+            "shared_experts": args.shared,
         },
         "hbm_gbps": round(layer_gbps, 1),
         "hbm_frac": round(layer_gbps / PEAK_HBM_GBPS, 4),

@@ -143,10 +143,19 @@ smoe_status smoe_elb_accumulate_topm(int32_t* elb_counts, int L, int E,
 
 /*
  * Device workspace (bytes) that the expert FFN calls need for a window of
- * T tokens, k slots per token and intermediate size I (the fp16
- * intermediate activations of every slot). Returns 0 for invalid sizes.
+ * T tokens, k slots per token, routed intermediate size I and shared
+ * intermediate size shared_I (0 = no shared expert): two fp32 buffers of
+ * the gate and up projections of every slot, and a small call counter.
+ * Returns 0 for invalid sizes.
+ *
+ * Workspace contract: the caller fills the buffer with zeros before its
+ * first use, and again before using it with a different (T, k, I,
+ * shared_I). The FFN calls keep it consistent from one call to the next
+ * (each call clears what the following call accumulates into), so it must
+ * not be written between calls, and two calls that share a workspace must
+ * not run concurrently.
  */
-size_t smoe_ffn_workspace_bytes(int T, int k, int E, int H, int I);
+size_t smoe_ffn_workspace_bytes(int T, int k, int E, int H, int I, int shared_I);
 
 /*
  * Fused multi-expert W4A16 expert FFN (draft pass).   [P] fused multi-expert
@@ -162,17 +171,32 @@ size_t smoe_ffn_workspace_bytes(int T, int k, int E, int H, int I);
  *     g = x[t] . Wg_e^T,  u = x[t] . Wu_e^T          (float32 accumulate)
  *     h = fp16( SiLU(g) * u ),  SiLU(g) = g / (1 + exp(-g))
  *     slot_out[s] = h . Wd_e^T                        (float32)
- * with W = (code - 8) * scale. Rows of slot_out for dropped slots are not
- * written.
+ * with W = (code - 8) * scale. Rows of slot_out for slots that the
+ * alignment dropped are zero.
+ *
+ * With shared_I > 0 the same launches also run the always-on FP16 shared
+ * expert (hybrid-precision layout: shared experts stay FP16) over every
+ * token: shared_out[t] = fp16(SiLU(x[t] . Sg^T) * (x[t] . Su^T)) . Sd^T.
+ * Several shared experts are passed concatenated along shared_I (their
+ * outputs add up).
  *
  *   x              fp16 [T][H]
  *   wg_q, wu_q     uint32 [E][I][H/8];  wg_s, wu_s fp16 [E][I][H/G]
  *   wd_q           uint32 [E][H][I/8];  wd_s       fp16 [E][H][I/G]
  *   sorted_slots   int32 [T*k], expert_offsets int32 [E+1]
  *                  (as written by smoe_align_by_expert for these T, k, E)
+ *   shared_I       0, or the shared intermediate size (multiple of 128)
+ *   shared_wg, shared_wu  fp16 [shared_I][H];  shared_wd fp16 [H][shared_I]
+ *                  (NULL when shared_I = 0)
  *   workspace      device buffer of at least
- *                  smoe_ffn_workspace_bytes(T, k, E, H, I) bytes
+ *                  smoe_ffn_workspace_bytes(T, k, E, H, I, shared_I) bytes,
+ *                  256-byte aligned, under the workspace contract above
  *   slot_out       float [T*k][H] (out)
+ *   shared_out     float [T][H] (out; NULL when shared_I = 0)
+ *
+ * Output tiles whose reduction is split between workgroups are summed with
+ * float atomics, so where more than two workgroups share a tile the last
+ * bits of the result may differ from call to call.
  */
 smoe_status smoe_w4a16_expert_ffn(const void* x, int T, int k, int E, int H, int I,
                                   int group_size,
@@ -180,8 +204,10 @@ smoe_status smoe_w4a16_expert_ffn(const void* x, int T, int k, int E, int H, int
                                   const uint32_t* wu_q, const void* wu_s,
                                   const uint32_t* wd_q, const void* wd_s,
                                   const int32_t* sorted_slots, const int32_t* expert_offsets,
+                                  int shared_I, const void* shared_wg, const void* shared_wu,
+                                  const void* shared_wd,
                                   void* workspace, size_t workspace_bytes,
-                                  float* slot_out, void* stream);
+                                  float* slot_out, float* shared_out, void* stream);
 
 /*
  * Expert FFN with FP16 weights (target verification pass and always-on
@@ -192,17 +218,19 @@ smoe_status smoe_w4a16_expert_ffn(const void* x, int T, int k, int E, int H, int
  * hybrid-precision layout (shared experts stay FP16); [D] "Streamlined
  * Execution Engine" (expert_reorder).
  *
- * Same computation and alignment as smoe_w4a16_expert_ffn with
- * W = fp16 weights:
+ * Same computation, alignment, shared-expert option and workspace contract
+ * as smoe_w4a16_expert_ffn with routed weights W = fp16 values:
  *   wg, wu   fp16 [E][I][H];   wd   fp16 [E][H][I]
- * A shared expert is run as E = 1, k = 1 with sorted_slots = 0..T-1 and
- * expert_offsets = {0, T}; several shared experts are concatenated along I.
+ * A shared expert can also be run on its own as E = 1, k = 1 with
+ * sorted_slots = 0..T-1 and expert_offsets = {0, T}.
  */
 smoe_status smoe_fp16_expert_ffn(const void* x, int T, int k, int E, int H, int I,
                                  const void* wg, const void* wu, const void* wd,
                                  const int32_t* sorted_slots, const int32_t* expert_offsets,
+                                 int shared_I, const void* shared_wg, const void* shared_wu,
+                                 const void* shared_wd,
                                  void* workspace, size_t workspace_bytes,
-                                 float* slot_out, void* stream);
+                                 float* slot_out, float* shared_out, void* stream);
 
 /*
  * Weighted combine back to token order.               [P] expert-wise

@@ -36,11 +36,11 @@ _SIGNATURES = {
     "smoe_route_topk": (_i, [_p, _p, _p, _i, _i, _i, _i, _i, _p, _p, _p, _p, _p, _p]),
     "smoe_align_by_expert": (_i, [_p, _i, _i, _i, _p, _p, _p, _p, _p, _p]),
     "smoe_elb_accumulate_topm": (_i, [_p, _i, _i, _p, _i, _i, _i, _i, _i, _p, _p, _i, _p]),
-    "smoe_ffn_workspace_bytes": (_sz, [_i, _i, _i, _i, _i]),
+    "smoe_ffn_workspace_bytes": (_sz, [_i, _i, _i, _i, _i, _i]),
     "smoe_w4a16_expert_ffn": (_i, [_p, _i, _i, _i, _i, _i, _i, _p, _p, _p, _p, _p, _p,
-                                   _p, _p, _p, _sz, _p, _p]),
-    "smoe_fp16_expert_ffn": (_i, [_p, _i, _i, _i, _i, _i, _p, _p, _p, _p, _p, _p, _sz,
-                                  _p, _p]),
+                                   _p, _p, _i, _p, _p, _p, _p, _sz, _p, _p, _p]),
+    "smoe_fp16_expert_ffn": (_i, [_p, _i, _i, _i, _i, _i, _p, _p, _p, _p, _p, _i, _p, _p, _p,
+                                  _p, _sz, _p, _p, _p]),
     "smoe_combine": (_i, [_p, _p, _i, _i, _i, _p, _p, _p, _p]),
 }
 
@@ -99,8 +99,19 @@ def smoe_abi_version() -> int:
     return int(_lib.smoe_abi_version())
 
 
-def smoe_ffn_workspace_bytes(T: int, k: int, E: int, H: int, I: int) -> int:
-    return int(_lib.smoe_ffn_workspace_bytes(T, k, E, H, I))
+def smoe_ffn_workspace_bytes(T: int, k: int, E: int, H: int, I: int, shared_I: int = 0) -> int:
+    return int(_lib.smoe_ffn_workspace_bytes(T, k, E, H, I, shared_I))
+
+
+def _shared_args(shared, shared_out):
+    """(shared_I, wg, wu, wd, out) pointers of the optional shared expert."""
+    if shared is None:
+        if shared_out is not None:
+            raise ValueError("shared_out given without shared-expert weights")
+        return 0, None, None, None, None
+    sg, su, sd = shared
+    return (sg.shape[0], _ptr(sg, torch.float16, "shared_wg"), _ptr(su, torch.float16, "shared_wu"),
+            _ptr(sd, torch.float16, "shared_wd"), _ptr(shared_out, torch.float32, "shared_out"))
 
 
 def smoe_route_topk(x, w_router, logit_bias, k: int, flags: int, topk_ids, topk_w,
@@ -145,30 +156,34 @@ def smoe_elb_accumulate_topm(elb_counts, topk_ids, layer_begin: int, M: int, pla
 
 def smoe_w4a16_expert_ffn(x, k: int, E: int, I: int, group_size: int, wg_q, wg_s, wu_q, wu_s,
                           wd_q, wd_s, sorted_slots, expert_offsets, workspace, slot_out,
-                          stream=None) -> None:
+                          shared=None, shared_out=None, stream=None) -> None:
+    """shared: optional (wg, wu, wd) fp16 weights of the always-on shared expert."""
     T, H = x.shape
+    sI, sg, su, sd, so = _shared_args(shared, shared_out)
     _check("smoe_w4a16_expert_ffn", _lib.smoe_w4a16_expert_ffn(
         _ptr(x, torch.float16, "x"), T, k, E, H, I, group_size,
         _ptr(wg_q, torch.int32, "wg_q"), _ptr(wg_s, torch.float16, "wg_s"),
         _ptr(wu_q, torch.int32, "wu_q"), _ptr(wu_s, torch.float16, "wu_s"),
         _ptr(wd_q, torch.int32, "wd_q"), _ptr(wd_s, torch.float16, "wd_s"),
         _ptr(sorted_slots, torch.int32, "sorted_slots"),
-        _ptr(expert_offsets, torch.int32, "expert_offsets"),
+        _ptr(expert_offsets, torch.int32, "expert_offsets"), sI, sg, su, sd,
         _ptr(workspace, torch.uint8, "workspace"), workspace.numel(),
-        _ptr(slot_out, torch.float32, "slot_out"), _stream(stream)))
+        _ptr(slot_out, torch.float32, "slot_out"), so, _stream(stream)))
 
 
 def smoe_fp16_expert_ffn(x, k: int, E: int, I: int, wg, wu, wd, sorted_slots, expert_offsets,
-                         workspace, slot_out, stream=None) -> None:
+                         workspace, slot_out, shared=None, shared_out=None, stream=None) -> None:
+    """shared: optional (wg, wu, wd) fp16 weights of the always-on shared expert."""
     T, H = x.shape
+    sI, sg, su, sd, so = _shared_args(shared, shared_out)
     _check("smoe_fp16_expert_ffn", _lib.smoe_fp16_expert_ffn(
         _ptr(x, torch.float16, "x"), T, k, E, H, I,
         _ptr(wg, torch.float16, "wg"), _ptr(wu, torch.float16, "wu"),
         _ptr(wd, torch.float16, "wd"),
         _ptr(sorted_slots, torch.int32, "sorted_slots"),
-        _ptr(expert_offsets, torch.int32, "expert_offsets"),
+        _ptr(expert_offsets, torch.int32, "expert_offsets"), sI, sg, su, sd,
         _ptr(workspace, torch.uint8, "workspace"), workspace.numel(),
-        _ptr(slot_out, torch.float32, "slot_out"), _stream(stream)))
+        _ptr(slot_out, torch.float32, "slot_out"), so, _stream(stream)))
 
 
 def smoe_combine(slot_out, topk_w, shared_out, shared_gate, y, stream=None) -> None:

@@ -2,34 +2,40 @@
 //
 // Specter paper: fused multi-expert draft kernel paragraph (the routed
 // tokens are gathered by expert and all active experts' sub-computations run
-// in one launch) and expert-wise verification paragraphs (tokens of each
-// expert packed into one sub-batch, outputs scattered back). Design notes,
-// "Streamlined Execution Engine": W4A16 dequantises INT4 weight tiles while
-// computing with FP16 activations; FP32 reductions.
+// in one launch), expert-wise verification paragraphs (tokens of each expert
+// packed into one sub-batch, outputs scattered back) and the hybrid-precision
+// layout (always-on shared experts stay FP16). Design notes, "Streamlined
+// Execution Engine": W4A16 dequantises INT4 weight tiles while computing
+// with FP16 activations; FP32 reductions.
 //
-// Two launches per call, each over all active experts at once:
+// Two launches per call, each over all active routed experts and the
+// optional FP16 shared expert at once:
 //   stage 1  g[p] = x_t . Wg^T,  u[p] = x_t . Wu^T          (fp32, p = sorted slot position)
-//   stage 2  slot_out[s] = fp16(SiLU(g[p]) * u[p]) . Wd^T    (s = sorted_slots[p])
+//   stage 2  out[s] = fp16(SiLU(g[p]) * u[p]) . Wd^T          (s = sorted_slots[p])
 // SiLU(g) * u is formed (and rounded to fp16) while stage 2 stages its rows.
+// The shared expert takes every token in order (its slot t is token t).
 //
 // The layer is bound by streaming the weights from HBM (a few slots per
 // expert), so every weight byte is read once per slot chunk and the work is
 // cut into many equal pieces spread evenly over the whole GPU:
 //
+// * Blocks. A block is 64 bytes of one weight row: 128 k of INT4 codes or
+//   32 k of FP16 values, so both formats fill the same register ring and an
+//   item (D blocks) streams the same bytes whatever the format.
 // * Work list. The slots of each expert are cut into chunks of `csz` slots
 //   (one chunk per expert when every token picks an expert at most once). A
 //   row tile is 128 rows of gate and up (stage 1) or 256 rows of down
 //   (stage 2): 16 / 32 rows per wave of an 8-wave workgroup. The reduction
-//   dim K is cut into P parts of D blocks of 128 k. An item is (chunk, row
-//   tile, part): every item streams the same number of weight bytes. Items
-//   are numbered part-fastest; the persistent grid gives every busy
-//   workgroup the same count q = ceil(n / nwg) of consecutive items. The
-//   list is built on the device from expert_offsets (nothing is read back).
+//   dim K is cut into parts of D blocks. An item is (chunk, row tile, part);
+//   the routed experts' items come first, the shared expert's after them.
+//   The persistent grid gives every busy workgroup the same count
+//   q = ceil(n / nwg) of consecutive items. The list is built on the device
+//   from expert_offsets (nothing is read back).
 // * Split K. A workgroup adds the consecutive parts of a tile in registers.
-//   A tile it holds whole is stored; a tile shared with a neighbouring
-//   workgroup is added into the output with device-scope float atomics
-//   (no return value, so nobody waits). Outputs that take atomics start at
-//   zero: stage 1 clears slot_out for stage 2, and the g/u buffer of the
+//   A tile it holds whole is stored; a tile shared with other workgroups is
+//   added into the output with device-scope float atomics (no return value,
+//   so nobody waits). Outputs that take atomics start at zero: stage 1
+//   clears slot_out and shared_out for stage 2, and the g/u buffer of the
 //   next call. The workspace keeps two g/u buffers and a two-word call
 //   counter that picks the current one: stage 1 reads word 0 and writes
 //   word 1, stage 2 reads word 1 and writes word 0, so no word is written
@@ -40,7 +46,7 @@
 //   when the chunk changes, k-permuted for INT4 (below) and padded by 16
 //   bytes per row so the MFMA operand reads are bank-conflict free. The
 //   first staging issues its loads before the weight prologue, so it never
-//   waits behind it. Rows of K above the LDS budget are staged in phases.
+//   waits behind it. Rows longer than the LDS budget are staged in phases.
 // * Weight ring. Each wave streams its rows through a register ring of D
 //   blocks that runs on across items; weights are the only global loads in
 //   it, so the in-order vector memory counter never waits on anything but
@@ -63,13 +69,12 @@
 // eight values come out in k order 0,4,1,5,2,6,3,7, and the activations are
 // staged with the same permutation within each group of 8.
 //
-// Word layout per 128-k block so that each MFMA's 32 k lie in one
+// INT4 word layout per block so that each MFMA's 32 k lie in one
 // quantisation group (lane group g, MFMA step q):
 //   G = 128: word 4g + q  (one 16-byte load of words 4g .. 4g+3);
 //   G =  64: word 8(q/2) + 2g + q%2 (two 8-byte loads);
 //   G =  32: word 4q + g  (four 4-byte loads).
-// FP16 weights: step q, lane group g takes k = 32q + 8g .. +7 (four 16-byte
-// loads per block; each wave instruction reads 16 rows x 64 bytes).
+// FP16 block: one MFMA step, lane group g takes k = 8g .. 8g+7 of the block.
 #include <algorithm>
 #include <atomic>
 #include <type_traits>
@@ -84,57 +89,65 @@ typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
 
 enum { kInt4 = 0, kFp16 = 1 };
-constexpr int kKB = 128;                   // k per block
+constexpr int kBlockBytes = 64;            // bytes of one weight row per block
 constexpr int kWavesPerWg = 8;             // 4 waves per SIMD at two workgroups per CU
 constexpr int kThreads = kWavesPerWg * kWave;
 constexpr int kMaxChunk = 32;              // slots per chunk (two MFMA column groups)
-constexpr int kTabInts = 2 * (kMaxE + 1);
+constexpr int kCpOff = (kMaxE + 1 + 3) / 4 * 4;  // chunk prefix table, 16-byte aligned
+constexpr int kTabInts = kCpOff + kMaxE + 1;
 constexpr int kTabBytes = (kTabInts * 4 + 15) / 16 * 16;  // offsets, chunk prefix
 static_assert(kTabBytes % 16 == 0, "staged rows must start 16-byte aligned");
 constexpr int kMaxSlotsLds = 1024;         // sorted slots kept whole in LDS up to this many
 constexpr int kLdsPerCu = 160 * 1024;      // gfx950
 constexpr int kLdsBudget = kLdsPerCu / 2;  // per workgroup: two workgroups per CU
 constexpr int kRowPad = 16;                // bytes of padding per staged row
+constexpr int kD = 4;                      // blocks per item (8 KB per wave)
+constexpr int kPhaseK = kD * 128;          // staged phases are whole INT4 items
 #ifndef SMOE_FFN_MAX_WG
 #define SMOE_FFN_MAX_WG 512
 #endif
-#ifndef SMOE_FFN_D_INT4
-#define SMOE_FFN_D_INT4 4
-#endif
-#ifndef SMOE_FFN_D_FP16
-#define SMOE_FFN_D_FP16 1
-#endif
 constexpr int kMaxWg = SMOE_FFN_MAX_WG;    // persistent grid cap
-constexpr int kDInt4 = SMOE_FFN_D_INT4;    // blocks per item, INT4 weights (2 KB per block and wave)
-constexpr int kDFp16 = SMOE_FFN_D_FP16;    // blocks per item, FP16 weights (8 KB per block and wave)
 
-struct FfnArgs {
-  const uint16_t* x;            // stage 1 activations [T][K] (fp16 bits)
-  const int32_t* sorted_slots;  // [S]
-  const int32_t* offsets;       // [E+1]
+// A set of experts that share a weight format and shapes: the routed
+// experts (group 0) or the shared expert (group 1, FP16).
+struct Group {
   const uint8_t* w0;            // stage 1: gate; stage 2: down
   const uint8_t* w1;            // stage 1: up
-  const uint16_t* s0;           // INT4 scales of w0 / w1 (fp16 bits)
+  const uint16_t* s0;           // INT4 group scales of w0 / w1 (fp16 bits)
   const uint16_t* s1;
-  float* gu;                    // two g/u buffers, each [2][S][I] fp32
-  float* out;                   // slot_out [S][H]: stage 1 clears it, stage 2 fills it
-  int* epoch;                   // [2] call counter words
-  long long gu_buf;             // floats per g/u buffer (2 * S * I)
+  float* out;                   // stage 2 output [rows][H] (slot_out or shared_out)
   long long w_estride;          // bytes per expert
   long long s_estride;          // scale elements per expert
+  long long gu_off;             // float offset of the group's g/u planes in a buffer
   int w_rstride;                // bytes per weight row
   int s_rstride;                // scale elements per row
-  int E, k, S, K, N, I, H;
-  int tiles;                    // row tiles per chunk
-  int parts;                    // K parts per tile
-  int csz;                      // slots per chunk = activation rows staged
-  int chunks_upper;             // chunks the work list can hold
-  int kp;                       // k-blocks per staged phase (a multiple of D)
+  int fmt;                      // kInt4 or kFp16
+  int N, K;                     // output rows and reduction length of this stage
+  int nblk;                     // blocks per weight row
+  int tiles, parts;             // row tiles and K parts per chunk
+  int csz;                      // slots per chunk
+  int rows;                     // slots of the group (S routed, T shared)
+};
+
+struct FfnArgs {
+  const uint16_t* x;            // activations [T][H] (fp16 bits)
+  const int32_t* sorted_slots;  // [S]
+  const int32_t* offsets;       // [E+1]
+  float* gu;                    // two g/u buffers
+  int* epoch;                   // [2] call counter words
+  long long gu_buf;             // floats per g/u buffer
+  int E, k, S, T, H;
+  int chunks_upper;             // routed chunks the work list can hold
+  int n_groups;                 // 1, or 2 with a shared expert
+  int kph;                      // k per staged phase (a multiple of kPhaseK)
   int stride;                   // LDS bytes per staged row
   int slots_lds;                // all S sorted slots copied to LDS at start
   int xs_off;                   // LDS byte offset of the staged rows
+  int rows_lds;                 // staged rows the LDS holds (largest chunk)
+  Group grp[2];
 };
 
 template <typename T, typename U>
@@ -172,63 +185,28 @@ __device__ __forceinline__ u32x4 permute_k8(u32x4 d) {
   return e;
 }
 
-// Word index (within a 128-k block) that MFMA step q of lane group g uses.
+// Word index (within an INT4 block) that MFMA step q of lane group g uses.
 template <int G>
 __device__ __forceinline__ int int4_word(int g, int q) {
   constexpr int per = G / 32;  // MFMA steps per quantisation group
   return (q / per) * (G / 8) + g * per + (q % per);
 }
 
-// k offset (within a 128-k block) of the 8 activations that lane group g
-// feeds to MFMA step q.
-template <int WK, int G>
-__device__ __forceinline__ int a_koff(int g, int q) {
-  return WK == kInt4 ? 8 * int4_word<G>(g, q) : 32 * q + 8 * g;
-}
-
-template <int WK, int G>
-struct Block {
-  static constexpr int NW = WK == kInt4 ? 1 : 4;   // u32x4 per matrix
-  static constexpr int NQ = WK == kInt4 ? kKB / G : 1;
-  u32x4 w[2][NW];
-};
-
-// One item: part `part` of row tile `tile` of chunk `chunk` (expert e,
-// sorted positions [seg0, seg0 + m)).
+// One item: part `part` of row tile `tile` of chunk `chunk` of group `grp`
+// (expert e, positions [seg0, seg0 + m) of the group's slots).
 struct Item {
-  int chunk, tile, part, e, seg0, m;
+  int grp, chunk, tile, part, e, seg0, m;
 };
 
-__device__ __forceinline__ Item decode_item(const int* s_off, const int* s_cp, int E, int tiles,
-                                            int parts, int csz, int item) {
-  Item it;
-  const int ct = item / parts;
-  it.part = item - ct * parts;
-  it.chunk = ct / tiles;
-  it.tile = ct - it.chunk * tiles;
-  const int lane = lane_id();
-  int found = -1;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int e = 4 * lane + i;
-    if (e < E && s_cp[e] <= it.chunk && it.chunk < s_cp[e + 1]) found = e;
-  }
-  const uint64_t mask = __ballot(found >= 0);
-  const int src = mask ? __ffsll(static_cast<long long>(mask)) - 1 : 0;
-  it.e = uniform(__shfl(found, src, kWave));
-  it.seg0 = s_off[it.e] + (it.chunk - s_cp[it.e]) * csz;
-  it.m = min(csz, s_off[it.e + 1] - it.seg0);
-  return it;
-}
 
-template <int WK, int G, int STAGE, int NC, int D>
+template <int WK, int G, int STAGE, int NC>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) void ffn_kernel(
     FfnArgs a) {
-  using Blk = Block<WK, G>;
-  constexpr int NQ = Blk::NQ;
+  constexpr int D = kD;
+  constexpr int NQ = WK == kInt4 ? 128 / G : 1;  // INT4 group scales per block
   extern __shared__ __align__(16) uint8_t smem[];
   int* s_off = reinterpret_cast<int*>(smem);
-  int* s_cp = s_off + (kMaxE + 1);
+  int* s_cp = s_off + kCpOff;
   int* s_slots = reinterpret_cast<int*>(smem + kTabBytes);  // all slots, or the chunk's
   uint8_t* xs = smem + a.xs_off;
 
@@ -238,8 +216,6 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
   const int g = lane >> 4;
   const int r16 = lane & 15;
   const int E = a.E;
-  const int P = a.parts;
-  const int nblk = a.K / kKB;
   const int b = blockIdx.x;
 
   // ---- one round trip for the work list: expert offsets, sorted slots
@@ -256,24 +232,24 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
     }
   }
   const int ep = a.epoch[STAGE == 1 ? 0 : 1];
-  // the g/u buffer of this call
-  float* gu = a.gu + ((STAGE == 1 ? ep : ep - 1) & 1) * a.gu_buf;
+  float* gu = a.gu + ((STAGE == 1 ? ep : ep - 1) & 1) * a.gu_buf;  // this call's g/u
   if (tid <= E) s_off[tid] = min(max(offv, 0), a.S);  // clamped to [0, S]
   if (a.slots_lds) {
 #pragma unroll
     for (int j = 0; j < kSlotsPer; ++j)
       if (tid + j * kThreads < a.S) s_slots[tid + j * kThreads] = slv[j];
   }
-  if (b == 0 && tid == 0) a.epoch[STAGE == 1 ? 1 : 0] = ep + 1 - (STAGE == 1 ? 0 : 1);
+  if (b == 0 && tid == 0) a.epoch[STAGE == 1 ? 1 : 0] = STAGE == 1 ? ep + 1 : ep;
   __syncthreads();
 
-  // ---- work list: chunk prefix over experts
+  // ---- work list: chunk prefix over the routed experts
+  const int csz0 = a.grp[0].csz;
   if (wave == 0) {
     int n[4], tot = 0;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int e = 4 * lane + i;
-      n[i] = e < E ? (max(s_off[e + 1] - s_off[e], 0) + a.csz - 1) / a.csz : 0;
+      n[i] = e < E ? (max(s_off[e + 1] - s_off[e], 0) + csz0 - 1) / csz0 : 0;
       tot += n[i];
     }
     const int incl = wave_inclusive_scan(tot);
@@ -289,26 +265,32 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
   __syncthreads();
   // (inconsistent offsets could describe more chunks than the list holds;
   // the excess is ignored)
-  const int n_items = min(s_cp[E], a.chunks_upper) * a.tiles * P;
+  const int n_r = min(s_cp[E], a.chunks_upper) * a.grp[0].tiles * a.grp[0].parts;
+  const int n_s = a.n_groups > 1
+                      ? (a.T + a.grp[1].csz - 1) / a.grp[1].csz * a.grp[1].tiles * a.grp[1].parts
+                      : 0;
+  const int n_items = n_r + n_s;
   // q items per workgroup and only ceil(n_items / q) workgroups busy, so
   // every busy workgroup streams the same number of bytes
   const int q = (n_items + gridDim.x - 1) / gridDim.x;
   const int i0 = b * q;
   const int i1 = min(n_items, i0 + q);
 
-  // Stage 1 clears what split tiles will add into: slot_out (for stage 2)
-  // and the other g/u buffer (for the next call). Each workgroup clears its
+  // Stage 1 clears what split tiles will add into: the stage-2 outputs and
+  // the other g/u buffer (for the next call). Each workgroup clears its
   // share once its own items are done (or at once if it has none).
   auto clear_share = [&]() {
     if (STAGE != 1) return;
     float* other = a.gu + ((ep + 1) & 1) * a.gu_buf;
-    const long long n_gu = a.gu_buf / 4, n_out = static_cast<long long>(a.S) * a.H / 4;
-    const long long tot = n_gu + n_out;
+    const long long n0 = a.gu_buf / 4;
+    const long long n1 = n0 + static_cast<long long>(a.S) * a.H / 4;
+    const long long tot = n1 + (a.n_groups > 1 ? static_cast<long long>(a.T) * a.H / 4 : 0);
     const long long per = (tot + gridDim.x - 1) / gridDim.x;
     const long long lo = per * b, hi = min(tot, lo + per);
     for (long long i = lo + tid; i < hi; i += kThreads) {
-      f32x4* dst = i < n_gu ? reinterpret_cast<f32x4*>(other) + i
-                            : reinterpret_cast<f32x4*>(a.out) + (i - n_gu);
+      f32x4* dst = i < n0   ? reinterpret_cast<f32x4*>(other) + i
+                   : i < n1 ? reinterpret_cast<f32x4*>(a.grp[0].out) + (i - n0)
+                            : reinterpret_cast<f32x4*>(a.grp[1].out) + (i - n1);
       *dst = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
     }
   };
@@ -317,85 +299,114 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
     return;
   }
 
+  auto decode = [&](int item) {
+    Item it;
+    if (item < n_r) {
+      const int P = a.grp[0].parts, tiles = a.grp[0].tiles;
+      const int ct = item / P;
+      it.grp = 0;
+      it.part = item - ct * P;
+      it.chunk = ct / tiles;
+      it.tile = ct - it.chunk * tiles;
+      // s_cp is non-decreasing, so the chunk's expert is the number of
+      // experts whose chunks start at or before it, minus one
+      const i32x4 cp = *reinterpret_cast<const i32x4*>(s_cp + 4 * lane);
+      int n = 0;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) n += __popcll(__ballot(4 * lane + i < E && cp[i] <= it.chunk));
+      it.e = uniform(max(n - 1, 0));
+      it.seg0 = s_off[it.e] + (it.chunk - s_cp[it.e]) * csz0;
+      it.m = min(csz0, s_off[it.e + 1] - it.seg0);
+    } else {
+      const int P = a.grp[1].parts, tiles = a.grp[1].tiles, csz = a.grp[1].csz;
+      const int i = item - n_r;
+      const int ct = i / P;
+      it.grp = 1;
+      it.part = i - ct * P;
+      it.chunk = ct / tiles;
+      it.tile = ct - it.chunk * tiles;
+      it.e = 0;
+      it.seg0 = it.chunk * csz;
+      it.m = min(csz, a.T - it.seg0);
+    }
+    return it;
+  };
+
   // weight row of matrix m for this lane in row tile `tile`
   auto row_of = [&](int tile, int m) {
     return STAGE == 1 ? tile * (kWavesPerWg * 16) + wave * 16 + r16
                       : tile * (kWavesPerWg * 32) + wave * 32 + m * 16 + r16;
   };
-  const int lane_kb = WK == kInt4 ? (G == 128 ? 16 * g : (G == 64 ? 8 * g : 4 * g)) : 16 * g;
 
   // ---- load cursor
   const uint8_t* wp[2];
   const uint16_t* sp[2];
-  int l_blk0 = 0;  // first block of the item being loaded
-  auto set_load_item = [&](int item) {
-    const Item it = decode_item(s_off, s_cp, E, a.tiles, P, a.csz, item);
+  int l_blk0 = 0, l_nblk = 1, l_fmt = kFp16;
+  auto set_load_item = [&](const Item& it) {
+    const Group& gr = a.grp[it.grp];
+    l_fmt = WK == kInt4 ? gr.fmt : kFp16;
     l_blk0 = it.part * D;
+    l_nblk = gr.nblk;
+    const int lane_kb = (l_fmt == kInt4 && G == 64) ? 8 * g : (l_fmt == kInt4 && G == 32) ? 4 * g
+                                                                                          : 16 * g;
 #pragma unroll
     for (int m = 0; m < 2; ++m) {
-      const int row = min(row_of(it.tile, m), a.N - 1);  // rows past N: loaded, never stored
-      const uint8_t* wm = (STAGE == 1 && m == 1) ? a.w1 : a.w0;
-      wp[m] = wm + it.e * a.w_estride + static_cast<long long>(row) * a.w_rstride + lane_kb;
-      if (WK == kInt4) {
-        const uint16_t* sm = (STAGE == 1 && m == 1) ? a.s1 : a.s0;
-        sp[m] = sm + it.e * a.s_estride + static_cast<long long>(row) * a.s_rstride;
+      const int row = min(row_of(it.tile, m), gr.N - 1);  // rows past N: loaded, never stored
+      const uint8_t* wm = (STAGE == 1 && m == 1) ? gr.w1 : gr.w0;
+      wp[m] = wm + it.e * gr.w_estride + static_cast<long long>(row) * gr.w_rstride + lane_kb;
+      if (WK == kInt4) {  // (FP16 groups: null + 0)
+        const uint16_t* sm = (STAGE == 1 && m == 1) ? gr.s1 : gr.s0;
+        sp[m] = sm + it.e * gr.s_estride + static_cast<long long>(row) * gr.s_rstride;
       }
     }
   };
-  auto load = [&](Blk& r, int blk) {
+  auto load = [&](u32x4 (&r)[2], int blk) {
 #pragma unroll
     for (int m = 0; m < 2; ++m) {
-      if (WK == kInt4) {
-        const uint8_t* base = wp[m] + blk * (kKB / 2);
-        if (G == 128) {
-          r.w[m][0] = *reinterpret_cast<const u32x4*>(base);
-        } else if (G == 64) {
+      const uint8_t* base = wp[m] + blk * kBlockBytes;
+      if (WK == kInt4 && G != 128 && l_fmt == kInt4) {
+        if (G == 64) {
           const u32x2 lo = *reinterpret_cast<const u32x2*>(base);
           const u32x2 hi = *reinterpret_cast<const u32x2*>(base + 32);
-          r.w[m][0] = u32x4{lo[0], lo[1], hi[0], hi[1]};
+          r[m] = u32x4{lo[0], lo[1], hi[0], hi[1]};
         } else {
 #pragma unroll
           for (int qq = 0; qq < 4; ++qq)
-            r.w[m][0][qq] = *reinterpret_cast<const uint32_t*>(base + 16 * qq);
+            r[m][qq] = *reinterpret_cast<const uint32_t*>(base + 16 * qq);
         }
       } else {
-        const uint8_t* base = wp[m] + blk * (kKB * 2);
-#pragma unroll
-        for (int c = 0; c < 4; ++c) r.w[m][c] = *reinterpret_cast<const u32x4*>(base + 64 * c);
+        r[m] = *reinterpret_cast<const u32x4*>(base);
       }
     }
   };
 
   // INT4 group scales of an item, one load per matrix: lane group g holds
-  // the scales of blocks blk0 + g + 4j of its row (NS words each); block d
-  // reads them from lane (d % 4, row) with a cross-lane shuffle.
-  static_assert(WK != kInt4 || D % 4 == 0, "INT4 items are whole groups of 4 blocks");
-  constexpr int DJ = (D + 3) / 4;
+  // the scales of block blk0 + g of its row (NS words); block d reads them
+  // from lane (d, row) with a cross-lane shuffle.
+  static_assert(D == 4, "one INT4 scale block per lane group");
   constexpr int NS = NQ == 4 ? 2 : 1;
-  uint32_t sring[2][DJ][NS], scur[2][DJ][NS];
+  uint32_t sring[2][NS], scur[2][NS];
   auto load_scales = [&](int blk0) {
 #pragma unroll
-    for (int m = 0; m < 2; ++m)
-#pragma unroll
-      for (int j = 0; j < DJ; ++j) {
-        const uint16_t* sptr = sp[m] + min(blk0 + g + 4 * j, nblk - 1) * NQ;
-        if (NQ == 1) {
-          sring[m][j][0] = *sptr;
-        } else if (NQ == 2) {
-          sring[m][j][0] = *reinterpret_cast<const uint32_t*>(sptr);
-        } else {
-          const u32x2 v = *reinterpret_cast<const u32x2*>(sptr);
-          sring[m][j][0] = v[0];
-          sring[m][j][1] = v[1];
-        }
+    for (int m = 0; m < 2; ++m) {
+      const uint16_t* sptr = sp[m] + min(blk0 + g, l_nblk - 1) * NQ;
+      if (NQ == 1) {
+        sring[m][0] = *sptr;
+      } else if (NQ == 2) {
+        sring[m][0] = *reinterpret_cast<const uint32_t*>(sptr);
+      } else {
+        const u32x2 v = *reinterpret_cast<const u32x2*>(sptr);
+        sring[m][0] = v[0];
+        sring[m][1] = v[1];
       }
+    }
   };
 
   f32x4 acc[2][NC];
   uint32_t dq_lo = 0x000F000Fu, dq_magic = 0x64006400u;
   asm volatile("" : "+v"(dq_lo), "+v"(dq_magic));  // keep the masks in VGPRs
 
-  // Slot r of chunk `it` (from the full copy in LDS, or the chunk's copy).
+  // Slot r of routed chunk `it` (from the full copy in LDS, or the chunk's copy).
   auto chunk_slot = [&](const Item& it, int r) {
     return a.slots_lds ? s_slots[it.seg0 + r] : s_slots[r];
   };
@@ -403,57 +414,63 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
   // slots read a staged row and their results are dropped.
   int arow[NC];
 #pragma unroll
-  for (int cg = 0; cg < NC; ++cg) arow[cg] = min(16 * cg + r16, a.csz - 1) * a.stride;
+  for (int cg = 0; cg < NC; ++cg) arow[cg] = min(16 * cg + r16, a.rows_lds - 1) * a.stride;
 
-  auto compute = [&](const Blk& r, int bp, int d, auto nce_tag) {
+  // One INT4 block (128 k) at k offset kk of the staged rows.
+  auto compute_int4 = [&](const u32x4 (&r)[2], int kk, int d, auto nce_tag) {
     constexpr int NCE = decltype(nce_tag)::value;
-    f16x8 A[NCE][4];
-#pragma unroll
-    for (int cg = 0; cg < NCE; ++cg) {
-      const uint8_t* ar = xs + arow[cg] + bp * (kKB * 2);
+    constexpr int per = G / 32;
+    f16x8 A[NCE == 1 ? 4 : 1];
+    if (NCE == 1) {
 #pragma unroll
       for (int qq = 0; qq < 4; ++qq)
-        A[cg][qq] = *reinterpret_cast<const f16x8*>(ar + 2 * a_koff<WK, G>(g, qq));
+        A[qq] = *reinterpret_cast<const f16x8*>(xs + arow[0] + 2 * (kk + 8 * int4_word<G>(g, qq)));
     }
 #pragma unroll
     for (int m = 0; m < 2; ++m) {
-      if (WK == kInt4) {
-        f16x8 B[4];
+      f16x8 B[4];
 #pragma unroll
-        for (int qq = 0; qq < 4; ++qq) B[qq] = dequant_word(r.w[m][0][qq], dq_lo, dq_magic);
-        constexpr int per = G / 32;
+      for (int qq = 0; qq < 4; ++qq) B[qq] = dequant_word(r[m][qq], dq_lo, dq_magic);
 #pragma unroll
-        for (int grp = 0; grp < NQ; ++grp) {
-          const int src = (d & 3) * 16 + r16;
-          const uint32_t word = __shfl(scur[m][d >> 2][NQ == 4 ? (grp >> 1) : 0], src, kWave);
-          const uint32_t sbits = (NQ == 4) ? (word >> (16 * (grp & 1))) : (word >> (16 * grp));
-          const float sc =
-              static_cast<float>(bitcast<_Float16>(static_cast<uint16_t>(sbits & 0xFFFFu)));
+      for (int grp = 0; grp < NQ; ++grp) {
+        const int src = d * 16 + r16;
+        const uint32_t word = __shfl(scur[m][NQ == 4 ? (grp >> 1) : 0], src, kWave);
+        const uint32_t sbits = (NQ == 4) ? (word >> (16 * (grp & 1))) : (word >> (16 * grp));
+        const float sc =
+            static_cast<float>(bitcast<_Float16>(static_cast<uint16_t>(sbits & 0xFFFFu)));
 #pragma unroll
-          for (int cg = 0; cg < NCE; ++cg) {
-            f32x4 t = {0.0f, 0.0f, 0.0f, 0.0f};
+        for (int cg = 0; cg < NCE; ++cg) {
+          f32x4 t = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-            for (int qq = 0; qq < per; ++qq)
-              t = __builtin_amdgcn_mfma_f32_16x16x32_f16(A[cg][grp * per + qq],
-                                                         B[grp * per + qq], t, 0, 0, 0);
-            acc[m][cg] += sc * t;
+          for (int qq = 0; qq < per; ++qq) {
+            const int q = grp * per + qq;
+            const f16x8 Aq = NCE == 1 ? A[q]
+                                      : *reinterpret_cast<const f16x8*>(
+                                            xs + arow[cg] + 2 * (kk + 8 * int4_word<G>(g, q)));
+            t = __builtin_amdgcn_mfma_f32_16x16x32_f16(Aq, B[q], t, 0, 0, 0);
           }
-        }
-      } else {
-#pragma unroll
-        for (int qq = 0; qq < 4; ++qq) {
-          const f16x8 Bq = bitcast<f16x8>(r.w[m][qq]);
-#pragma unroll
-          for (int cg = 0; cg < NCE; ++cg)
-            acc[m][cg] =
-                __builtin_amdgcn_mfma_f32_16x16x32_f16(A[cg][qq], Bq, acc[m][cg], 0, 0, 0);
+          acc[m][cg] += sc * t;
+          // one column group's operands in registers at a time
+          if (NCE > 1) __builtin_amdgcn_sched_barrier(0);
         }
       }
     }
   };
+  // One FP16 block (32 k) at k offset kk of the staged rows.
+  auto compute_fp16 = [&](const u32x4 (&r)[2], int kk, auto nce_tag) {
+    constexpr int NCE = decltype(nce_tag)::value;
+#pragma unroll
+    for (int cg = 0; cg < NCE; ++cg) {
+      const f16x8 A = *reinterpret_cast<const f16x8*>(xs + arow[cg] + 2 * (kk + 8 * g));
+#pragma unroll
+      for (int m = 0; m < 2; ++m)
+        acc[m][cg] =
+            __builtin_amdgcn_mfma_f32_16x16x32_f16(A, bitcast<f16x8>(r[m]), acc[m][cg], 0, 0, 0);
+    }
+  };
 
-  // Staged activations, eight columns at a time: stage 1 copies x of the
-  // slot's token; stage 2 forms fp16(SiLU(g) * u) of the position. The loads
+  // Staged activations, eight k at a time: stage 1 copies x of the slot's
+  // token; stage 2 forms fp16(SiLU(g) * u) of the position. The loads
   // (load_raw) and the conversion (finish) are split so that a batch of
   // loads is in flight before anything waits on it.
   struct Raw1 {
@@ -467,24 +484,30 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
   // stay in bounds.
   auto load_raw = [&](const Item& it, int r, int col, Raw& raw) -> bool {
     if constexpr (STAGE == 1) {
-      const int slot = chunk_slot(it, r);
-      const bool ok = slot >= 0 && slot < a.S;
-      raw.v = *reinterpret_cast<const u32x4*>(
-          a.x + static_cast<long long>(ok ? slot / a.k : 0) * a.K + col);
+      int tok = it.seg0 + r;  // shared expert: slot t is token t
+      bool ok = true;
+      if (it.grp == 0) {
+        const int slot = chunk_slot(it, r);
+        ok = slot >= 0 && slot < a.S;
+        tok = ok ? slot / a.k : 0;
+      }
+      raw.v = *reinterpret_cast<const u32x4*>(a.x + static_cast<long long>(tok) * a.H + col);
       return ok;
     } else {
-      const float* gr = gu + static_cast<long long>(it.seg0 + r) * a.I + col;
-      const float* ur = gr + static_cast<long long>(a.S) * a.I;
-      raw.g0 = *reinterpret_cast<const f32x4*>(gr);
-      raw.g1 = *reinterpret_cast<const f32x4*>(gr + 4);
+      const Group& gr = a.grp[it.grp];
+      const float* gr_ = gu + gr.gu_off + static_cast<long long>(it.seg0 + r) * gr.K + col;
+      const float* ur = gr_ + static_cast<long long>(gr.rows) * gr.K;
+      raw.g0 = *reinterpret_cast<const f32x4*>(gr_);
+      raw.g1 = *reinterpret_cast<const f32x4*>(gr_ + 4);
       raw.u0 = *reinterpret_cast<const f32x4*>(ur);
       raw.u1 = *reinterpret_cast<const f32x4*>(ur + 4);
       return true;
     }
   };
-  auto finish = [&](const Raw& raw) -> u32x4 {
+  auto finish = [&](const Raw& raw, bool perm) -> u32x4 {
+    u32x4 v;
     if constexpr (STAGE == 1) {
-      return WK == kInt4 ? permute_k8(raw.v) : raw.v;
+      v = raw.v;
     } else {
       f16x8 h;
 #pragma unroll
@@ -492,23 +515,24 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
         h[i] = static_cast<_Float16>(raw.g0[i] / (1.0f + __expf(-raw.g0[i])) * raw.u0[i]);
         h[4 + i] = static_cast<_Float16>(raw.g1[i] / (1.0f + __expf(-raw.g1[i])) * raw.u1[i]);
       }
-      const u32x4 v = bitcast<u32x4>(h);
-      return WK == kInt4 ? permute_k8(v) : v;
+      v = bitcast<u32x4>(h);
     }
+    return perm ? permute_k8(v) : v;
   };
 
-  // Stage the activation rows of chunk `it`, k-blocks [phase*kp, ...), into
+  // Stage the activation rows of chunk `it`, k range [k0, k1), into
   // LDS. `mid` runs right after the first batch of loads is issued, so the
   // weight prologue can go out behind it without the staging waiting on it.
-  auto stage_rows = [&](const Item& it, int phase, auto batch_tag, auto&& mid) {
+  auto stage_rows = [&](const Item& it, int k0, int k1, auto batch_tag, auto&& mid) {
     constexpr int NB = decltype(batch_tag)::value;  // pieces in flight per thread
+    const Group& gr = a.grp[it.grp];
     __syncthreads();  // every wave is done with the previous rows
-    if (!a.slots_lds) {
+    if (!a.slots_lds && it.grp == 0) {
       if (tid < it.m) s_slots[tid] = a.sorted_slots[it.seg0 + tid];
       __syncthreads();
     }
-    const int kb0 = phase * a.kp;
-    const int npr = min(a.kp, nblk - kb0) * (kKB / 8);  // 16-byte pieces per row
+    const bool perm = WK == kInt4 && gr.fmt == kInt4;
+    const int npr = (k1 - k0) / 8;  // 16-byte pieces per row
     const int tot = it.m * npr;
     for (int base = 0; base < tot; base += NB * kThreads) {
       Raw raw[NB];
@@ -517,13 +541,13 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
       for (int j = 0; j < NB; ++j) {
         const int i = min(base + j * kThreads + tid, tot - 1);
         const int r = i / npr, c = i - r * npr;
-        const bool ok = load_raw(it, r, kb0 * kKB + 8 * c, raw[j]);
+        const bool ok = load_raw(it, r, k0 + 8 * c, raw[j]);
         dst[j] = (ok && base + j * kThreads + tid < tot) ? r * a.stride + 16 * c : -1;
       }
       if (base == 0) mid();
 #pragma unroll
       for (int j = 0; j < NB; ++j)
-        if (dst[j] >= 0) *reinterpret_cast<u32x4*>(xs + dst[j]) = finish(raw[j]);
+        if (dst[j] >= 0) *reinterpret_cast<u32x4*>(xs + dst[j]) = finish(raw[j], perm);
     }
     __syncthreads();
   };
@@ -531,6 +555,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
   // Write the sums of a tile; a tile split with other workgroups is added
   // into the (zeroed) output with device-scope atomics.
   auto write_tile = [&](const Item& it, bool whole) {
+    const Group& gr = a.grp[it.grp];
 #pragma unroll
     for (int cg = 0; cg < NC; ++cg) {
 #pragma unroll
@@ -540,15 +565,18 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
 #pragma unroll
         for (int m = 0; m < 2; ++m) {
           const int row = row_of(it.tile, STAGE == 1 ? 0 : m);
-          if (row >= a.N) continue;
+          if (row >= gr.N) continue;
           float* dst;
           if (STAGE == 1) {
-            dst = gu + static_cast<long long>(m) * a.S * a.I +
-                  static_cast<long long>(it.seg0 + rr) * a.I + row;
+            dst = gu + gr.gu_off + static_cast<long long>(m) * gr.rows * gr.N +
+                  static_cast<long long>(it.seg0 + rr) * gr.N + row;
           } else {
-            const int slot = chunk_slot(it, rr);
-            if (slot < 0 || slot >= a.S) continue;
-            dst = a.out + static_cast<long long>(slot) * a.H + row;
+            int slot = it.seg0 + rr;  // shared expert: slot t is token t
+            if (it.grp == 0) {
+              slot = chunk_slot(it, rr);
+              if (slot < 0 || slot >= a.S) continue;
+            }
+            dst = gr.out + static_cast<long long>(slot) * a.H + row;
           }
           if (whole)
             *dst = acc[m][cg][i];
@@ -560,20 +588,44 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
     }
   };
 
+  auto kblk_of = [&](int fmt) { return (WK == kInt4 && fmt == kInt4) ? 128 : 32; };
+  // k window to stage for item `it` (number `item`): if this workgroup's
+  // remaining items all lie in the item's tile, just the k they cover;
+  // else the LDS phase holding the item (the rows then serve the next
+  // tiles of the chunk too). At most kph wide.
+  int st_lo = 0, st_hi = 0;
+  auto window = [&](const Item& it, int item) {
+    const Group& gr = a.grp[it.grp];
+    const int kpart = D * kblk_of(WK == kInt4 ? gr.fmt : kFp16);
+    const int k0 = it.part * kpart;
+    const int left_in_tile = gr.parts - 1 - it.part;  // items after this one in its tile
+    if (i1 - 1 - item <= left_in_tile) {
+      st_lo = k0;
+      st_hi = min(gr.K, min(k0 + a.kph, (it.part + i1 - item) * kpart));
+    } else {
+      st_lo = k0 / a.kph * a.kph;
+      st_hi = min(gr.K, st_lo + a.kph);
+    }
+  };
+
   // ---- prologue: stage the first chunk, the first item's blocks in flight
-  Item ci = decode_item(s_off, s_cp, E, a.tiles, P, a.csz, i0);
-  set_load_item(i0);
-  Blk ring[D];
-  int staged_chunk = ci.chunk, staged_phase = (ci.part * D) / a.kp;
-  stage_rows(ci, staged_phase, std::integral_constant<int, STAGE == 1 ? 4 : 2>(), [&]() {
-    if (WK == kInt4) load_scales(l_blk0);
+  Item ci = decode(i0);
+  set_load_item(ci);
+  u32x4 ring[D][2];
+  int c_fmt = l_fmt, c_nblk = l_nblk;
+  int staged_id = ci.grp * (1 << 24) + ci.chunk;
+  window(ci, i0);
+  stage_rows(ci, st_lo, st_hi, std::integral_constant<int, STAGE == 1 ? 4 : 2>(), [&]() {
+    if (WK == kInt4 && l_fmt == kInt4) load_scales(l_blk0);
 #pragma unroll
-    for (int d = 0; d < D; ++d) load(ring[d], min(l_blk0 + d, nblk - 1));
+    for (int d = 0; d < D; ++d) load(ring[d], min(l_blk0 + d, l_nblk - 1));
   });
   int seg_pa = ci.part;  // first part of the tile accumulated so far
 
   for (int item = i0; item < i1; ++item) {
+    const int P = a.grp[ci.grp].parts;
     const int blk0 = ci.part * D;
+    const int kblk = kblk_of(c_fmt);
     if (item == i0 || ci.part == 0) {
       seg_pa = ci.part;
 #pragma unroll
@@ -581,41 +633,56 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
 #pragma unroll
         for (int cg = 0; cg < NC; ++cg) acc[m][cg] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
     }
-    const int phase = blk0 / a.kp;
-    if (ci.chunk != staged_chunk || phase != staged_phase) {
-      stage_rows(ci, phase, std::integral_constant<int, STAGE == 1 ? 2 : 1>(), []() {});
-      staged_chunk = ci.chunk;
-      staged_phase = phase;
+    const int id = ci.grp * (1 << 24) + ci.chunk;
+    const int k0 = blk0 * kblk;
+    const int k1 = min(a.grp[ci.grp].K, k0 + D * kblk);
+    if (id != staged_id || k0 < st_lo || k1 > st_hi) {
+      window(ci, item);
+      stage_rows(ci, st_lo, st_hi, std::integral_constant<int, STAGE == 1 ? 2 : 1>(), []() {});
+      staged_id = id;
     }
 
     // the load cursor moves to the next item
     const bool l_live = item + 1 < i1;
-    if (l_live) set_load_item(item + 1);
-
-    const bool wide = NC == 2 && ci.m > 16;
-    const int bp0 = blk0 - phase * a.kp;
     if (WK == kInt4) {
 #pragma unroll
       for (int m = 0; m < 2; ++m)
 #pragma unroll
-        for (int j = 0; j < DJ; ++j)
-#pragma unroll
-          for (int t = 0; t < NS; ++t) scur[m][j][t] = sring[m][j][t];
-      if (l_live) load_scales(l_blk0);
+        for (int t = 0; t < NS; ++t) scur[m][t] = sring[m][t];
     }
+    Item nxt = ci;
+    if (l_live) {
+      nxt = decode(item + 1);
+      set_load_item(nxt);
+      if (WK == kInt4 && l_fmt == kInt4) load_scales(l_blk0);
+    }
+
+    const bool wide = NC == 2 && ci.m > 16;
+    const int kk0 = k0 - st_lo;
 #pragma unroll
     for (int d = 0; d < D; ++d) {
-      if (blk0 + d < nblk) {
-        if (wide)
-          compute(ring[d], bp0 + d, d, std::integral_constant<int, NC>());
-        else
-          compute(ring[d], bp0 + d, d, std::integral_constant<int, 1>());
+      if (blk0 + d < c_nblk) {
+        if (WK == kInt4 && c_fmt == kInt4) {
+          if (wide)
+            compute_int4(ring[d], kk0 + d * 128, d, std::integral_constant<int, NC>());
+          else
+            compute_int4(ring[d], kk0 + d * 128, d, std::integral_constant<int, 1>());
+        } else {
+          if (wide)
+            compute_fp16(ring[d], kk0 + d * 32, std::integral_constant<int, NC>());
+          else
+            compute_fp16(ring[d], kk0 + d * 32, std::integral_constant<int, 1>());
+        }
       }
-      if (l_live) load(ring[d], min(l_blk0 + d, nblk - 1));
+      if (l_live) load(ring[d], min(l_blk0 + d, l_nblk - 1));
     }
 
     if (item + 1 == i1 || ci.part == P - 1) write_tile(ci, seg_pa == 0 && ci.part == P - 1);
-    if (item + 1 < i1) ci = decode_item(s_off, s_cp, E, a.tiles, P, a.csz, item + 1);
+    if (l_live) {
+      ci = nxt;
+      c_fmt = l_fmt;
+      c_nblk = l_nblk;
+    }
   }
   clear_share();
 }
@@ -636,62 +703,10 @@ int cu_count() {
   return v;
 }
 
-// Launch plan of one stage: K parts, LDS phase length kp (a multiple of D,
-// so phases start on item boundaries), staged row stride, LDS layout.
-struct StagePlan {
-  int parts, kp, stride, lds, items, slots_lds, xs_off;
-};
-
-StagePlan plan_stage(int D, int csz, int S, int K, int chunks_upper, int tiles) {
-  StagePlan p{};
-  const int nblk = K / kKB;
-  p.parts = (nblk + D - 1) / D;
-  p.items = chunks_upper * tiles * p.parts;
-  p.slots_lds = S <= kMaxSlotsLds ? 1 : 0;
-  p.xs_off = kTabBytes + ((p.slots_lds ? S : kMaxChunk) * 4 + 15) / 16 * 16;
-  const int per_row = (kLdsBudget - p.xs_off) / csz;
-  const int kp_cap = std::max(1, (per_row - kRowPad) / (kKB * 2));
-  const int kpmax = std::max(D, kp_cap / D * D);
-  const int phases = (nblk + kpmax - 1) / kpmax;
-  const int per_phase = (nblk + phases - 1) / phases;
-  p.kp = (per_phase + D - 1) / D * D;
-  p.stride = std::min(p.kp, nblk) * kKB * 2 + kRowPad;
-  p.lds = p.xs_off + csz * p.stride;
-  return p;
-}
-
-template <int WK, int G, int STAGE, int NC>
-smoe_status launch_stage(const FfnArgs& a, const StagePlan& p, hipStream_t st) {
-  constexpr int D = WK == kInt4 ? kDInt4 : kDFp16;
-  auto kern = ffn_kernel<WK, G, STAGE, NC, D>;
-  static std::atomic<int> attr_done{0};
-  if (!attr_done.load(std::memory_order_acquire)) {
-    if (hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                            hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBudget) != hipSuccess) {
-      set_error("expert_ffn: cannot raise the dynamic LDS limit to %d bytes", kLdsBudget);
-      return SMOE_EHIP;
-    }
-    attr_done.store(1, std::memory_order_release);
-  }
-  const int per_cu = 2 * p.lds <= kLdsPerCu ? 2 : 1;
-  const int nwg = std::max(1, std::min({p.items, per_cu * cu_count(), kMaxWg}));
-  hipLaunchKernelGGL(kern, dim3(nwg), dim3(kThreads), p.lds, st, a);
-  return check_launch(STAGE == 1 ? "expert_ffn stage 1" : "expert_ffn stage 2");
-}
-
-template <int WK, int G, int NC>
-smoe_status launch_ffn(const FfnArgs& a1, const FfnArgs& a2, const StagePlan& p1,
-                       const StagePlan& p2, hipStream_t st) {
-  smoe_status s = launch_stage<WK, G, 1, NC>(a1, p1, st);
-  if (s != SMOE_OK) return s;
-  return launch_stage<WK, G, 2, NC>(a2, p2, st);
-}
-
-// Slots per chunk: two 16-slot MFMA column groups when one expert is
+// Slots per routed chunk: two 16-slot MFMA column groups when one expert is
 // expected to hold more than 16 of the window's slots (long windows, or few
-// experts such as a shared expert that every token uses), else one (an
-// expert with more slots then gets a second chunk and reads its weights
-// twice, which at these windows is rare).
+// experts), else one (an expert with more slots then gets a second chunk and
+// reads its weights twice, which at these windows is rare).
 int chunk_slots(long long T, long long k, long long E) {
   const long long S = T * k;
   const bool wide = T > 16 && (T > 24 || S > 8 * std::min(E, S));
@@ -705,78 +720,206 @@ int tiles_of(long long N, int rows_per_wave) {
 }
 
 // Workspace layout: call counter (2 words, padded to 256 bytes) | two g/u
-// buffers of [2][S][I] fp32.
+// buffers, each [2][S][I] fp32 (routed) followed by [2][T][Is] fp32 (shared).
 constexpr size_t kEpochBytes = 256;
-size_t workspace_bytes(long long T, long long k, long long I) {
-  return kEpochBytes + static_cast<size_t>(4 * T * k * I) * sizeof(float);
+long long gu_floats(long long T, long long k, long long I, long long Is) {
+  return 2 * T * k * I + 2 * T * Is;
+}
+size_t workspace_bytes(long long T, long long k, long long I, long long Is) {
+  return kEpochBytes + static_cast<size_t>(2 * gu_floats(T, k, I, Is)) * sizeof(float);
 }
 
-smoe_status check_common(const char* who, const void* x, int T, int k, int E, int H, int I,
-                         const int32_t* sorted_slots, const int32_t* offsets,
-                         const void* workspace, size_t ws_bytes, const float* slot_out) {
-  SMOE_REQUIRE(T >= 0 && k > 0 && E > 0 && H > 0 && I > 0, SMOE_EINVAL,
-               "%s: need T >= 0 and k, E, H, I > 0 (T=%d k=%d E=%d H=%d I=%d)", who, T, k, E, H, I);
-  SMOE_REQUIRE(E <= kMaxE && k <= kMaxK && k <= E, SMOE_EUNSUPPORTED,
-               "%s: need E <= 256 and k <= min(8, E) (E=%d k=%d)", who, E, k);
-  SMOE_REQUIRE(H % 128 == 0 && I % 128 == 0, SMOE_EUNSUPPORTED,
-               "%s: H and I must be multiples of 128 (H=%d I=%d)", who, H, I);
-  SMOE_REQUIRE(H <= 16384 && I <= 32768, SMOE_EUNSUPPORTED,
-               "%s: need H <= 16384 and I <= 32768 (H=%d I=%d)", who, H, I);
-  SMOE_REQUIRE(static_cast<long long>(T) * k < (1ll << 24) &&
-                   static_cast<long long>(T) * k * std::max(H, I) < (1ll << 31),
-               SMOE_EUNSUPPORTED, "%s: T*k must be below 2^24 and T*k*max(H, I) below 2^31",
-               who);
-  if (T == 0) return SMOE_OK;
-  SMOE_REQUIRE(x && sorted_slots && offsets && workspace && slot_out, SMOE_EINVAL,
-               "%s: null pointer", who);
-  const size_t need = workspace_bytes(T, k, I);
-  SMOE_REQUIRE(ws_bytes >= need, SMOE_EINVAL, "%s: workspace of %zu bytes is below the %zu needed",
-               who, ws_bytes, need);
-  SMOE_REQUIRE(aligned16(x) && (reinterpret_cast<uintptr_t>(workspace) & 255u) == 0 &&
-                   aligned16(slot_out),
-               SMOE_EINVAL,
-               "%s: x and slot_out must be 16-byte aligned, the workspace 256-byte aligned", who);
-  return SMOE_OK;
+// Weights of one group as the entry points hand them over.
+struct GroupWeights {
+  int fmt;                       // kInt4 or kFp16
+  const void *wg, *wu, *wd;      // codes (INT4) or values (FP16)
+  const void *sg, *su, *sd;      // INT4 scales, else null
+  int E, I, G;                   // experts, intermediate size, INT4 group size
+  int csz, rows;                 // slots per chunk, slots of the group
+  float* out;                    // stage 2 output rows
+  long long gu_off;              // float offset of its g/u planes
+};
+
+// Row geometry of a [E][N][K] weight tensor in the group's format.
+void set_matrix(Group& g, const GroupWeights& w, int N, int K, const void* wq, const void* ws) {
+  g.fmt = w.fmt;
+  g.N = N;
+  g.K = K;
+  g.w_rstride = w.fmt == kInt4 ? K / 2 : K * 2;
+  g.w_estride = static_cast<long long>(g.w_rstride) * N;
+  g.nblk = g.w_rstride / kBlockBytes;
+  g.s_rstride = w.fmt == kInt4 ? K / w.G : 0;
+  g.s_estride = static_cast<long long>(g.s_rstride) * N;
+  g.w0 = static_cast<const uint8_t*>(wq);
+  g.s0 = static_cast<const uint16_t*>(ws);
+  g.parts = (g.nblk + kD - 1) / kD;
+  g.csz = w.csz;
+  g.rows = w.rows;
+  g.out = w.out;
+  g.gu_off = w.gu_off;
 }
 
-// Fill the stage arguments and launch plans shared by both weight formats.
-void fill_args(int D, FfnArgs& a1, FfnArgs& a2, StagePlan& p1, StagePlan& p2, int& nc,
-               const void* x, int T, int k, int E, int H, int I, const int32_t* sorted_slots,
-               const int32_t* offsets, void* workspace, float* slot_out) {
+struct StagePlans {
+  FfnArgs a1, a2;
+  int lds1, lds2;
+  long long items1, items2;  // upper bounds of the work lists
+  int nc;
+};
+
+// LDS layout of a stage: the table, the sorted slots, then rows_lds staged
+// rows of the phase length (a multiple of whole INT4 items, balanced over
+// the phases that the longest K needs).
+int plan_lds(FfnArgs& a, int kmax) {
+  a.slots_lds = a.S <= kMaxSlotsLds ? 1 : 0;
+  a.xs_off = kTabBytes + ((a.slots_lds ? a.S : kMaxChunk) * 4 + 15) / 16 * 16;
+  const int per_row = (kLdsBudget - a.xs_off) / a.rows_lds;
+  const int kph_cap = std::max(kPhaseK, (per_row - kRowPad) / 2 / kPhaseK * kPhaseK);
+  const int phases = (kmax + kph_cap - 1) / kph_cap;
+  const int per_phase = (kmax + phases - 1) / phases;
+  a.kph = (per_phase + kPhaseK - 1) / kPhaseK * kPhaseK;
+  a.stride = std::min(a.kph, kmax) * 2 + kRowPad;
+  return a.xs_off + a.rows_lds * a.stride;
+}
+
+void make_plans(StagePlans& p, const void* x, int T, int k, int H, const int32_t* sorted_slots,
+                const int32_t* offsets, void* workspace, const GroupWeights* gw, int n_groups) {
   const int S = T * k;
-  const int csz = chunk_slots(T, k, E);
-  nc = csz > 16 ? 2 : 1;
-  const int chunks_upper = std::min(E, S) + S / csz;
   uint8_t* wsb = static_cast<uint8_t*>(workspace);
+  FfnArgs& a1 = p.a1;
   a1 = FfnArgs{};
   a1.x = static_cast<const uint16_t*>(x);
   a1.sorted_slots = sorted_slots;
   a1.offsets = offsets;
   a1.epoch = reinterpret_cast<int*>(wsb);
   a1.gu = reinterpret_cast<float*>(wsb + kEpochBytes);
-  a1.gu_buf = 2ll * S * I;
-  a1.out = slot_out;
-  a1.E = E; a1.k = k; a1.S = S; a1.I = I; a1.H = H;
-  a1.K = H; a1.N = I;
-  a1.tiles = tiles_of(I, 16);
-  a1.csz = csz;
-  a1.chunks_upper = chunks_upper;
-  p1 = plan_stage(D, csz, S, H, chunks_upper, a1.tiles);
-  a1.parts = p1.parts;
-  a1.kp = p1.kp;
-  a1.stride = p1.stride;
-  a1.slots_lds = p1.slots_lds;
-  a1.xs_off = p1.xs_off;
-
+  a1.gu_buf = gu_floats(T, k, gw[0].I, n_groups > 1 ? gw[1].I : 0);
+  a1.E = gw[0].E; a1.k = k; a1.S = S; a1.T = T; a1.H = H;
+  a1.chunks_upper = std::min(gw[0].E, S) + S / gw[0].csz;
+  a1.n_groups = n_groups;
+  a1.rows_lds = 1;
+  for (int i = 0; i < n_groups; ++i) a1.rows_lds = std::max(a1.rows_lds, gw[i].csz);
+  p.nc = a1.rows_lds > 16 ? 2 : 1;
+  FfnArgs& a2 = p.a2;
   a2 = a1;
-  a2.K = I; a2.N = H;
-  a2.tiles = tiles_of(H, 32);
-  p2 = plan_stage(D, csz, S, I, chunks_upper, a2.tiles);
-  a2.parts = p2.parts;
-  a2.kp = p2.kp;
-  a2.stride = p2.stride;
-  a2.slots_lds = p2.slots_lds;
-  a2.xs_off = p2.xs_off;
+  p.items1 = p.items2 = 0;
+  int kmax2 = 0;
+  for (int i = 0; i < n_groups; ++i) {
+    const GroupWeights& w = gw[i];
+    const long long chunks = i == 0 ? a1.chunks_upper : (T + w.csz - 1) / w.csz;
+    set_matrix(a1.grp[i], w, w.I, H, w.wg, w.sg);
+    a1.grp[i].w1 = static_cast<const uint8_t*>(w.wu);
+    a1.grp[i].s1 = static_cast<const uint16_t*>(w.su);
+    a1.grp[i].tiles = tiles_of(w.I, 16);
+    p.items1 += chunks * a1.grp[i].tiles * a1.grp[i].parts;
+    set_matrix(a2.grp[i], w, H, w.I, w.wd, w.sd);
+    a2.grp[i].w1 = nullptr;
+    a2.grp[i].s1 = nullptr;
+    a2.grp[i].tiles = tiles_of(H, 32);
+    p.items2 += chunks * a2.grp[i].tiles * a2.grp[i].parts;
+    kmax2 = std::max(kmax2, w.I);
+  }
+  p.lds1 = plan_lds(a1, H);
+  p.lds2 = plan_lds(a2, kmax2);
+}
+
+template <int WK, int G, int STAGE, int NC>
+smoe_status launch_stage(const FfnArgs& a, int lds, long long items, hipStream_t st) {
+  auto kern = ffn_kernel<WK, G, STAGE, NC>;
+  static std::atomic<int> attr_done{0};
+  if (!attr_done.load(std::memory_order_acquire)) {
+    if (hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBudget) != hipSuccess) {
+      set_error("expert_ffn: cannot raise the dynamic LDS limit to %d bytes", kLdsBudget);
+      return SMOE_EHIP;
+    }
+    attr_done.store(1, std::memory_order_release);
+  }
+  const int per_cu = 2 * lds <= kLdsPerCu ? 2 : 1;
+  const long long cap = std::min<long long>(per_cu * cu_count(), kMaxWg);
+  const int nwg = static_cast<int>(std::max(1ll, std::min(items, cap)));
+  hipLaunchKernelGGL(kern, dim3(nwg), dim3(kThreads), lds, st, a);
+  return check_launch(STAGE == 1 ? "expert_ffn stage 1" : "expert_ffn stage 2");
+}
+
+template <int WK, int G, int NC>
+smoe_status launch_ffn(const StagePlans& p, hipStream_t st) {
+  smoe_status s = launch_stage<WK, G, 1, NC>(p.a1, p.lds1, p.items1, st);
+  if (s != SMOE_OK) return s;
+  return launch_stage<WK, G, 2, NC>(p.a2, p.lds2, p.items2, st);
+}
+
+smoe_status check_common(const char* who, const void* x, int T, int k, int E, int H, int I,
+                         const int32_t* sorted_slots, const int32_t* offsets, int shared_I,
+                         const void* swg, const void* swu, const void* swd, const void* workspace,
+                         size_t ws_bytes, const float* slot_out, const float* shared_out) {
+  SMOE_REQUIRE(T >= 0 && k > 0 && E > 0 && H > 0 && I > 0 && shared_I >= 0, SMOE_EINVAL,
+               "%s: need T, shared_I >= 0 and k, E, H, I > 0 (T=%d k=%d E=%d H=%d I=%d "
+               "shared_I=%d)", who, T, k, E, H, I, shared_I);
+  SMOE_REQUIRE(E <= kMaxE && k <= kMaxK && k <= E, SMOE_EUNSUPPORTED,
+               "%s: need E <= 256 and k <= min(8, E) (E=%d k=%d)", who, E, k);
+  SMOE_REQUIRE(H % 128 == 0 && I % 128 == 0 && shared_I % 128 == 0, SMOE_EUNSUPPORTED,
+               "%s: H, I and shared_I must be multiples of 128 (H=%d I=%d shared_I=%d)", who, H,
+               I, shared_I);
+  SMOE_REQUIRE(H <= 16384 && I <= 32768 && shared_I <= 32768, SMOE_EUNSUPPORTED,
+               "%s: need H <= 16384 and I, shared_I <= 32768 (H=%d I=%d shared_I=%d)", who, H,
+               I, shared_I);
+  const long long S = static_cast<long long>(T) * k;
+  SMOE_REQUIRE(S < (1ll << 24) && S * std::max(H, I) < (1ll << 31) &&
+                   static_cast<long long>(T) * std::max(H, shared_I) < (1ll << 31),
+               SMOE_EUNSUPPORTED,
+               "%s: T*k must be below 2^24, T*k*max(H, I) and T*max(H, shared_I) below 2^31",
+               who);
+  if (T == 0) return SMOE_OK;
+  SMOE_REQUIRE(x && sorted_slots && offsets && workspace && slot_out, SMOE_EINVAL,
+               "%s: null pointer", who);
+  const size_t need = workspace_bytes(T, k, I, shared_I);
+  SMOE_REQUIRE(ws_bytes >= need, SMOE_EINVAL, "%s: workspace of %zu bytes is below the %zu needed",
+               who, ws_bytes, need);
+  SMOE_REQUIRE(aligned16(x) && (reinterpret_cast<uintptr_t>(workspace) & 255u) == 0 &&
+                   aligned16(slot_out),
+               SMOE_EINVAL,
+               "%s: x and slot_out must be 16-byte aligned, the workspace 256-byte aligned", who);
+  if (shared_I > 0) {
+    SMOE_REQUIRE(swg && swu && swd && shared_out, SMOE_EINVAL,
+                 "%s: null shared-expert pointer", who);
+    SMOE_REQUIRE(aligned16(swg) && aligned16(swu) && aligned16(swd) && aligned16(shared_out),
+                 SMOE_EINVAL, "%s: shared-expert weights and output must be 16-byte aligned",
+                 who);
+  }
+  return SMOE_OK;
+}
+
+// Both groups as the entry points describe them; the work list must fit int.
+smoe_status build_plans(const char* who, StagePlans& p, const void* x, int T, int k, int H,
+                        const int32_t* sorted_slots, const int32_t* offsets, void* workspace,
+                        GroupWeights routed, int shared_I, const void* swg, const void* swu,
+                        const void* swd, float* slot_out, float* shared_out) {
+  GroupWeights gw[2];
+  routed.csz = chunk_slots(T, k, routed.E);
+  routed.rows = T * k;
+  routed.out = slot_out;
+  routed.gu_off = 0;
+  gw[0] = routed;
+  int n = 1;
+  if (shared_I > 0) {
+    GroupWeights& s = gw[1];
+    s = GroupWeights{};
+    s.fmt = kFp16;
+    s.wg = swg; s.wu = swu; s.wd = swd;
+    s.E = 1; s.I = shared_I; s.G = 0;
+    s.csz = std::min(T, kMaxChunk);
+    s.rows = T;
+    s.out = shared_out;
+    s.gu_off = 2ll * T * k * routed.I;
+    n = 2;
+  }
+  make_plans(p, x, T, k, H, sorted_slots, offsets, workspace, gw, n);
+  SMOE_REQUIRE(p.lds1 <= kLdsBudget && p.lds2 <= kLdsBudget, SMOE_EUNSUPPORTED,
+               "%s: staged rows need %d / %d bytes of LDS, above %d", who, p.lds1, p.lds2,
+               kLdsBudget);
+  SMOE_REQUIRE(p.items1 < (1ll << 31) && p.items2 < (1ll << 31), SMOE_EUNSUPPORTED,
+               "%s: the work list exceeds 2^31 items (T=%d k=%d H=%d)", who, T, k, H);
+  return SMOE_OK;
 }
 
 }  // namespace
@@ -784,61 +927,46 @@ void fill_args(int D, FfnArgs& a1, FfnArgs& a2, StagePlan& p1, StagePlan& p2, in
 
 using namespace smoe;
 
-extern "C" size_t smoe_ffn_workspace_bytes(int T, int k, int E, int H, int I) {
-  if (T <= 0 || k <= 0 || E <= 0 || H <= 0 || I <= 0) return 0;
-  return workspace_bytes(T, k, I);
+extern "C" size_t smoe_ffn_workspace_bytes(int T, int k, int E, int H, int I, int shared_I) {
+  if (T <= 0 || k <= 0 || E <= 0 || H <= 0 || I <= 0 || shared_I < 0) return 0;
+  return workspace_bytes(T, k, I, shared_I);
 }
 
-extern "C" smoe_status smoe_w4a16_expert_ffn(const void* x, int T, int k, int E, int H, int I,
-                                             int group_size, const uint32_t* wg_q,
-                                             const void* wg_s, const uint32_t* wu_q,
-                                             const void* wu_s, const uint32_t* wd_q,
-                                             const void* wd_s, const int32_t* sorted_slots,
-                                             const int32_t* expert_offsets, void* workspace,
-                                             size_t workspace_bytes_, float* slot_out,
-                                             void* stream) {
+extern "C" smoe_status smoe_w4a16_expert_ffn(
+    const void* x, int T, int k, int E, int H, int I, int group_size, const uint32_t* wg_q,
+    const void* wg_s, const uint32_t* wu_q, const void* wu_s, const uint32_t* wd_q,
+    const void* wd_s, const int32_t* sorted_slots, const int32_t* expert_offsets, int shared_I,
+    const void* shared_wg, const void* shared_wu, const void* shared_wd, void* workspace,
+    size_t workspace_bytes_, float* slot_out, float* shared_out, void* stream) {
   clear_error();
+  const char* who = "w4a16_expert_ffn";
   SMOE_REQUIRE(group_size == 32 || group_size == 64 || group_size == 128, SMOE_EUNSUPPORTED,
-               "w4a16_expert_ffn: group size must be 32, 64 or 128 (got %d)", group_size);
-  smoe_status st = check_common("w4a16_expert_ffn", x, T, k, E, H, I, sorted_slots,
-                                expert_offsets, workspace, workspace_bytes_, slot_out);
+               "%s: group size must be 32, 64 or 128 (got %d)", who, group_size);
+  smoe_status st = check_common(who, x, T, k, E, H, I, sorted_slots, expert_offsets, shared_I,
+                                shared_wg, shared_wu, shared_wd, workspace, workspace_bytes_,
+                                slot_out, shared_out);
   if (st != SMOE_OK) return st;
   if (T == 0) return SMOE_OK;
   SMOE_REQUIRE(wg_q && wg_s && wu_q && wu_s && wd_q && wd_s, SMOE_EINVAL,
-               "w4a16_expert_ffn: null weight pointer");
+               "%s: null weight pointer", who);
   SMOE_REQUIRE(aligned16(wg_q) && aligned16(wu_q) && aligned16(wd_q), SMOE_EINVAL,
-               "w4a16_expert_ffn: packed weights must be 16-byte aligned");
+               "%s: packed weights must be 16-byte aligned", who);
   SMOE_REQUIRE(((reinterpret_cast<uintptr_t>(wg_s) | reinterpret_cast<uintptr_t>(wu_s) |
                  reinterpret_cast<uintptr_t>(wd_s)) & 7u) == 0,
-               SMOE_EINVAL, "w4a16_expert_ffn: scales must be 8-byte aligned");
+               SMOE_EINVAL, "%s: scales must be 8-byte aligned", who);
 
-  FfnArgs a1, a2;
-  StagePlan p1, p2;
-  int nc;
-  fill_args(kDInt4, a1, a2, p1, p2, nc, x, T, k, E, H, I, sorted_slots, expert_offsets,
-            workspace, slot_out);
-  a1.w0 = reinterpret_cast<const uint8_t*>(wg_q);
-  a1.w1 = reinterpret_cast<const uint8_t*>(wu_q);
-  a1.s0 = static_cast<const uint16_t*>(wg_s);
-  a1.s1 = static_cast<const uint16_t*>(wu_s);
-  a1.w_rstride = H / 2;
-  a1.w_estride = static_cast<long long>(a1.w_rstride) * I;
-  a1.s_rstride = H / group_size;
-  a1.s_estride = static_cast<long long>(a1.s_rstride) * I;
-
-  a2.w0 = reinterpret_cast<const uint8_t*>(wd_q);
-  a2.w1 = nullptr;
-  a2.s0 = static_cast<const uint16_t*>(wd_s);
-  a2.s1 = nullptr;
-  a2.w_rstride = I / 2;
-  a2.w_estride = static_cast<long long>(a2.w_rstride) * H;
-  a2.s_rstride = I / group_size;
-  a2.s_estride = static_cast<long long>(a2.s_rstride) * H;
-
+  GroupWeights r{};
+  r.fmt = kInt4;
+  r.wg = wg_q; r.wu = wu_q; r.wd = wd_q;
+  r.sg = wg_s; r.su = wu_s; r.sd = wd_s;
+  r.E = E; r.I = I; r.G = group_size;
+  StagePlans p;
+  st = build_plans(who, p, x, T, k, H, sorted_slots, expert_offsets, workspace, r, shared_I,
+                   shared_wg, shared_wu, shared_wd, slot_out, shared_out);
+  if (st != SMOE_OK) return st;
   hipStream_t s = as_stream(stream);
-#define SMOE_FFN_NC(G)                                  \
-  (nc == 2 ? launch_ffn<kInt4, G, 2>(a1, a2, p1, p2, s) \
-           : launch_ffn<kInt4, G, 1>(a1, a2, p1, p2, s))
+#define SMOE_FFN_NC(G) \
+  (p.nc == 2 ? launch_ffn<kInt4, G, 2>(p, s) : launch_ffn<kInt4, G, 1>(p, s))
   switch (group_size) {
     case 32: return SMOE_FFN_NC(32);
     case 64: return SMOE_FFN_NC(64);
@@ -847,35 +975,29 @@ extern "C" smoe_status smoe_w4a16_expert_ffn(const void* x, int T, int k, int E,
 #undef SMOE_FFN_NC
 }
 
-extern "C" smoe_status smoe_fp16_expert_ffn(const void* x, int T, int k, int E, int H, int I,
-                                            const void* wg, const void* wu, const void* wd,
-                                            const int32_t* sorted_slots,
-                                            const int32_t* expert_offsets, void* workspace,
-                                            size_t workspace_bytes_, float* slot_out,
-                                            void* stream) {
+extern "C" smoe_status smoe_fp16_expert_ffn(
+    const void* x, int T, int k, int E, int H, int I, const void* wg, const void* wu,
+    const void* wd, const int32_t* sorted_slots, const int32_t* expert_offsets, int shared_I,
+    const void* shared_wg, const void* shared_wu, const void* shared_wd, void* workspace,
+    size_t workspace_bytes_, float* slot_out, float* shared_out, void* stream) {
   clear_error();
-  smoe_status st = check_common("fp16_expert_ffn", x, T, k, E, H, I, sorted_slots,
-                                expert_offsets, workspace, workspace_bytes_, slot_out);
+  const char* who = "fp16_expert_ffn";
+  smoe_status st = check_common(who, x, T, k, E, H, I, sorted_slots, expert_offsets, shared_I,
+                                shared_wg, shared_wu, shared_wd, workspace, workspace_bytes_,
+                                slot_out, shared_out);
   if (st != SMOE_OK) return st;
   if (T == 0) return SMOE_OK;
-  SMOE_REQUIRE(wg && wu && wd, SMOE_EINVAL, "fp16_expert_ffn: null weight pointer");
+  SMOE_REQUIRE(wg && wu && wd, SMOE_EINVAL, "%s: null weight pointer", who);
   SMOE_REQUIRE(aligned16(wg) && aligned16(wu) && aligned16(wd), SMOE_EINVAL,
-               "fp16_expert_ffn: weights must be 16-byte aligned");
-
-  FfnArgs a1, a2;
-  StagePlan p1, p2;
-  int nc;
-  fill_args(kDFp16, a1, a2, p1, p2, nc, x, T, k, E, H, I, sorted_slots, expert_offsets,
-            workspace, slot_out);
-  a1.w0 = static_cast<const uint8_t*>(wg);
-  a1.w1 = static_cast<const uint8_t*>(wu);
-  a1.w_rstride = H * 2;
-  a1.w_estride = static_cast<long long>(a1.w_rstride) * I;
-  a2.w0 = static_cast<const uint8_t*>(wd);
-  a2.w1 = nullptr;
-  a2.w_rstride = I * 2;
-  a2.w_estride = static_cast<long long>(a2.w_rstride) * H;
+               "%s: weights must be 16-byte aligned", who);
+  GroupWeights r{};
+  r.fmt = kFp16;
+  r.wg = wg; r.wu = wu; r.wd = wd;
+  r.E = E; r.I = I; r.G = 0;
+  StagePlans p;
+  st = build_plans(who, p, x, T, k, H, sorted_slots, expert_offsets, workspace, r, shared_I,
+                   shared_wg, shared_wu, shared_wd, slot_out, shared_out);
+  if (st != SMOE_OK) return st;
   hipStream_t s = as_stream(stream);
-  return nc == 2 ? launch_ffn<kFp16, 128, 2>(a1, a2, p1, p2, s)
-                 : launch_ffn<kFp16, 128, 1>(a1, a2, p1, p2, s);
+  return p.nc == 2 ? launch_ffn<kFp16, 128, 2>(p, s) : launch_ffn<kFp16, 128, 1>(p, s);
 }

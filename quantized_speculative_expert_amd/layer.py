@@ -1,17 +1,19 @@
-"""One MoE layer on the device: the six libsmoe calls in order.
+"""One MoE layer on the device: the libsmoe calls in order.
 
 DeviceLayer holds the device copies of one layer's inputs (any object with
 the attributes of workload.LayerInputs) and the output / scratch buffers,
-and enqueues route -> align -> [ELB] -> routed expert FFN -> shared expert
-FFN -> combine on a stream. It only sequences calls of the HIP library and
-allocates buffers; all arithmetic happens in the library.
+and enqueues route -> align -> [ELB] -> expert FFN -> combine on a stream.
+It only sequences calls of the HIP library and allocates buffers; all
+arithmetic happens in the library.
 
 Draft pass: INT4 (W4A16) routed experts (Specter paper, fused multi-expert
 draft kernel paragraph). Target pass: FP16 routed experts with the same
 expert-centric gather/scatter (expert-wise verification paragraphs). The
-always-on shared experts are FP16 in both (hybrid-precision layout); they
-depend only on x, so with a side stream they run concurrently with routing
-and the routed experts.
+always-on shared experts are FP16 in both (hybrid-precision layout). By
+default they run inside the routed FFN's two launches, so one weight stream
+covers routed and shared experts; run(fuse_shared=False) runs them as a
+call of their own instead, optionally on a side stream (they depend only on
+x).
 """
 
 from __future__ import annotations
@@ -56,6 +58,8 @@ class DeviceLayer:
         self.wd16 = _dev(inp.wd16, d) if with_target else None
         self.sg16, self.su16, self.sd16 = (_dev(inp.sg16, d), _dev(inp.su16, d),
                                           _dev(inp.sd16, d))
+        Is = self.sg16.shape[0] if self.sg16 is not None else 0
+        self.shared_I = Is
 
         i32 = dict(dtype=torch.int32, device=d)
         f32 = dict(dtype=torch.float32, device=d)
@@ -67,15 +71,15 @@ class DeviceLayer:
         self.sorted_slots = torch.empty(S, **i32)
         self.active = torch.empty(E, **i32)
         self.n_active = torch.empty(1, **i32)
-        ws = _lib.smoe_ffn_workspace_bytes(T, k, E, H, I)
+        # zero-filled once; the FFN calls keep it consistent from then on
+        ws = _lib.smoe_ffn_workspace_bytes(T, k, E, H, I, Is)
         self.workspace = torch.zeros(ws, dtype=torch.uint8, device=d)
         self.slot_out = torch.empty((S, H), **f32)
         self.y = torch.empty((T, H), dtype=torch.float16, device=d)
         self.shared_gate = torch.empty(T, **f32) if self.shared_gate_w is not None else None
-        if self.sg16 is not None:
-            Is = self.sg16.shape[0]
-            self.shared_I = Is
+        if Is:
             self.shared_out = torch.empty((T, H), **f32)
+            # for the separate shared-expert call (E = 1, every token once)
             self.shared_ws = torch.zeros(_lib.smoe_ffn_workspace_bytes(T, 1, 1, H, Is),
                                          dtype=torch.uint8, device=d)
             self.shared_slots = torch.arange(T, **i32)
@@ -126,19 +130,29 @@ class DeviceLayer:
                                       self.plan_ids if M > 0 else None,
                                       self.plan_counts if M > 0 else None, flags, stream=stream)
 
-    def routed_ffn(self, target: bool = False, stream=None) -> None:
+    def routed_ffn(self, target: bool = False, with_shared: bool = True, stream=None) -> None:
+        """Routed experts (INT4 draft, or FP16 target) and, with_shared, the
+        shared experts in the same two launches."""
         c = self.cfg
+        shared = shared_out = None
+        if with_shared and self.shared_out is not None:
+            shared = (self.sg16, self.su16, self.sd16)
+            shared_out = self.shared_out
         if target:
             _lib.smoe_fp16_expert_ffn(self.x, c.k, c.E, c.I, self.wg16, self.wu16, self.wd16,
                                       self.sorted_slots, self.offsets, self.workspace,
-                                      self.slot_out, stream=stream)
+                                      self.slot_out, shared=shared, shared_out=shared_out,
+                                      stream=stream)
         else:
             _lib.smoe_w4a16_expert_ffn(self.x, c.k, c.E, c.I, c.G, self.wg_q, self.wg_s,
                                        self.wu_q, self.wu_s, self.wd_q, self.wd_s,
                                        self.sorted_slots, self.offsets, self.workspace,
-                                       self.slot_out, stream=stream)
+                                       self.slot_out, shared=shared, shared_out=shared_out,
+                                       stream=stream)
 
     def shared_ffn(self, stream=None) -> None:
+        """The shared experts alone: an FP16 FFN call with one expert that
+        every token uses once."""
         if self.shared_out is None:
             return
         _lib.smoe_fp16_expert_ffn(self.x, 1, 1, self.shared_I, self.sg16, self.su16, self.sd16,
@@ -150,28 +164,33 @@ class DeviceLayer:
                           self.y, stream=stream)
 
     # ---------------------------------------------------------------- whole layer
-    def run(self, target: bool = False, elb: bool = True, side_stream=None) -> None:
+    def run(self, target: bool = False, elb: bool = True, fuse_shared: bool = True,
+            side_stream=None) -> None:
         """Enqueue the whole layer on the current stream.
 
-        With side_stream, the shared expert runs there, ordered after the
-        current stream's prior work and joined before the combine.
+        fuse_shared runs the shared experts inside the routed FFN call.
+        Otherwise they get a call of their own; with side_stream it runs
+        there, ordered after the current stream's prior work and joined
+        before the combine.
         """
+        separate = not fuse_shared and self.shared_out is not None
         main = torch.cuda.current_stream(self.device)
-        if side_stream is not None and self.shared_out is not None:
-            fork = torch.cuda.Event()
-            fork.record(main)
-            side_stream.wait_event(fork)
-            self.shared_ffn(stream=side_stream)
-            join = torch.cuda.Event()
-            join.record(side_stream)
-        else:
-            join = None
-            self.shared_ffn()
+        join = None
+        if separate:
+            if side_stream is not None:
+                fork = torch.cuda.Event()
+                fork.record(main)
+                side_stream.wait_event(fork)
+                self.shared_ffn(stream=side_stream)
+                join = torch.cuda.Event()
+                join.record(side_stream)
+            else:
+                self.shared_ffn()
         self.route()
         self.align()
         if elb and self.cfg.elb_M > 0 and not target:
             self.elb()
-        self.routed_ffn(target=target)
+        self.routed_ffn(target=target, with_shared=not separate)
         if join is not None:
             main.wait_event(join)
         self.combine()

@@ -51,7 +51,7 @@ def test_binding_signatures_cover_header():
 
 
 def test_status_strings(lib):
-    assert lib.smoe_abi_version() == 1
+    assert lib.smoe_abi_version() == 2
     assert lib.smoe_status_string(0) == b"SMOE_OK"
     assert b"EINVAL" in lib.smoe_status_string(EINVAL)
     assert b"EUNSUPPORTED" in lib.smoe_status_string(EUNSUPPORTED)
@@ -60,14 +60,17 @@ def test_status_strings(lib):
 
 def test_workspace_bytes(lib):
     f = lib.smoe_ffn_workspace_bytes
-    f.argtypes = [ctypes.c_int] * 5
-    # holds at least the fp16 intermediate activations of every slot, grows
-    # with the window, and an empty window needs none
-    need = f(17, 6, 64, 2048, 1408)
+    f.argtypes = [ctypes.c_int] * 6
+    # holds at least the intermediate activations of every routed slot and
+    # shared-expert token, grows with the window, and an empty window needs none
+    need = f(17, 6, 64, 2048, 1408, 0)
     assert need >= 17 * 6 * 1408 * 2 and need % 256 == 0
-    assert f(544, 6, 64, 2048, 1408) >= need + (544 - 17) * 6 * 1408 * 2
-    assert f(-1, 6, 64, 2048, 1408) == 0
-    assert f(0, 6, 64, 2048, 1408) == 0
+    assert f(544, 6, 64, 2048, 1408, 0) >= need + (544 - 17) * 6 * 1408 * 2
+    with_shared = f(17, 6, 64, 2048, 1408, 2816)
+    assert with_shared >= need + 17 * 2816 * 2 and with_shared % 256 == 0
+    assert f(-1, 6, 64, 2048, 1408, 0) == 0
+    assert f(0, 6, 64, 2048, 1408, 0) == 0
+    assert f(17, 6, 64, 2048, 1408, -128) == 0
 
 
 N = None
@@ -107,18 +110,35 @@ def test_elb_argument_checks(lib):
 
 def test_ffn_argument_checks(lib):
     f = lib.smoe_w4a16_expert_ffn
-    f.argtypes = ([ctypes.c_void_p] + [ctypes.c_int] * 6 + [ctypes.c_void_p] * 9 +
-                  [ctypes.c_size_t, ctypes.c_void_p, ctypes.c_void_p])
-    args = [16, 16, 16, 16, 16, 16, 16, 16, 16]
-    assert f(16, 17, 6, 64, 2048, 1408, 96, *args, 1 << 20, 16, N) == EUNSUPPORTED  # G=96
-    assert f(16, 17, 6, 64, 2048, 1400, 128, *args, 1 << 20, 16, N) == EUNSUPPORTED  # I%128
-    assert f(16, 17, 6, 64, 2048, 1408, 128, *args, 10, 16, N) == EINVAL  # workspace too small
-    assert f(16, 17, 6, 64, 2048, 1408, 128, *args[:-1], 8, 1 << 20, 16, N) == EINVAL  # align
+    f.argtypes = ([ctypes.c_void_p] + [ctypes.c_int] * 6 + [ctypes.c_void_p] * 8 +
+                  [ctypes.c_int] + [ctypes.c_void_p] * 4 +
+                  [ctypes.c_size_t, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p])
+    w = [16] * 8                   # weights, scales, sorted slots, offsets
+    ns = [0, N, N, N]              # no shared expert
+    ws = 1 << 30
+    assert f(16, 17, 6, 64, 2048, 1408, 96, *w, *ns, 256, ws, 16, N, N) == EUNSUPPORTED  # G
+    assert f(16, 17, 6, 64, 2048, 1400, 128, *w, *ns, 256, ws, 16, N, N) == EUNSUPPORTED  # I
+    assert f(16, 17, 6, 64, 2048, 1408, 128, *w, *ns, 256, 10, 16, N, N) == EINVAL  # small ws
+    assert f(16, 17, 6, 64, 2048, 1408, 128, *w, *ns, 8, ws, 16, N, N) == EINVAL  # ws align
+    # shared expert: size checks, pointers and alignment
+    sh = [16, 16, 16]
+    assert f(16, 17, 6, 64, 2048, 1408, 128, *w, -128, *sh, 256, ws, 16, 16, N) == EINVAL
+    assert f(16, 17, 6, 64, 2048, 1408, 128, *w, 100, *sh, 256, ws, 16, 16, N) == EUNSUPPORTED
+    assert f(16, 17, 6, 64, 2048, 1408, 128, *w, 2816, *sh, 256, ws, 16, N, N) == EINVAL
+    assert b"shared" in lib.smoe_last_error()
+    assert f(16, 17, 6, 64, 2048, 1408, 128, *w, 2816, 16, 16, 8, 256, ws, 16, 16,
+             N) == EINVAL
+    small = lib.smoe_ffn_workspace_bytes(17, 6, 64, 2048, 1408, 0)
+    assert f(16, 17, 6, 64, 2048, 1408, 128, *w, 2816, *sh, 256, small, 16, 16,
+             N) == EINVAL  # workspace without room for the shared expert
     g = lib.smoe_fp16_expert_ffn
-    g.argtypes = ([ctypes.c_void_p] + [ctypes.c_int] * 5 + [ctypes.c_void_p] * 6 +
-                  [ctypes.c_size_t, ctypes.c_void_p, ctypes.c_void_p])
-    assert g(N, 17, 6, 64, 2048, 1408, 16, 16, 16, 16, 16, 16, 1 << 20, 16, N) == EINVAL
-    assert g(16, 17, 0, 64, 2048, 1408, 16, 16, 16, 16, 16, 16, 1 << 20, 16, N) == EINVAL
+    g.argtypes = ([ctypes.c_void_p] + [ctypes.c_int] * 5 + [ctypes.c_void_p] * 5 +
+                  [ctypes.c_int] + [ctypes.c_void_p] * 4 +
+                  [ctypes.c_size_t, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p])
+    w16 = [16] * 5
+    assert g(N, 17, 6, 64, 2048, 1408, *w16, *ns, 256, ws, 16, N, N) == EINVAL
+    assert g(16, 17, 0, 64, 2048, 1408, *w16, *ns, 256, ws, 16, N, N) == EINVAL
+    assert g(16, 17, 6, 64, 2048, 1408, *w16, 2816, *sh, 256, ws, 16, N, N) == EINVAL
 
 
 def test_combine_argument_checks(lib):

@@ -245,17 +245,35 @@ def oracle_slots_int4(L, ids, slots=None):
     return oracle.routed_ffn_expertwise(L.x, ids, load)
 
 
-def run_w4a16(smoe, x, ids, E, I, G, wg_q, wg_s, wu_q, wu_s, wd_q, wd_s):
+def _shared_dev(shared, T, H):
+    if shared is None:
+        return None, None, 0
+    sg, su, sd = shared
+    out = torch.full((T, H), float("nan"), dtype=torch.float32, device="cuda")
+    return (dev(sg), dev(su), dev(sd)), out, sg.shape[0]
+
+
+def run_w4a16(smoe, x, ids, E, I, G, wg_q, wg_s, wu_q, wu_s, wd_q, wd_s, shared=None, calls=1):
+    """slot_out (and shared_out when shared = (sg, su, sd) fp16 is given);
+    with calls > 1 the same workspace serves that many calls in a row and
+    the last call's outputs are returned."""
     T, k = ids.shape
     H = x.shape[1]
     al = oracle.align_by_expert(ids, E)
-    ws = torch.zeros(smoe.smoe_ffn_workspace_bytes(T, k, E, H, I), dtype=torch.uint8,
+    sh, sh_out, Is = _shared_dev(shared, T, H)
+    ws = torch.zeros(smoe.smoe_ffn_workspace_bytes(T, k, E, H, I, Is), dtype=torch.uint8,
                      device="cuda")
-    out = torch.full((T * k, H), float("nan"), dtype=torch.float32, device="cuda")
-    smoe.smoe_w4a16_expert_ffn(dev(x), k, E, I, G, dev(wg_q), dev(wg_s), dev(wu_q), dev(wu_s),
-                               dev(wd_q), dev(wd_s), dev(al["sorted_slots"]),
-                               dev(al["offsets"]), ws, out)
-    return host(out)
+    args = [dev(a) for a in (x, wg_q, wg_s, wu_q, wu_s, wd_q, wd_s, al["sorted_slots"],
+                             al["offsets"])]
+    for _ in range(calls):
+        out = torch.full((T * k, H), float("nan"), dtype=torch.float32, device="cuda")
+        if sh_out is not None:
+            sh_out.fill_(float("nan"))
+        smoe.smoe_w4a16_expert_ffn(args[0], k, E, I, G, *args[1:7], args[7], args[8], ws, out,
+                                   shared=sh, shared_out=sh_out)
+    if shared is None:
+        return host(out)
+    return host(out), host(sh_out)
 
 
 @pytest.mark.parametrize("name", ["tiny", "dsv2", "qwen"])
@@ -318,16 +336,23 @@ def test_w4a16_ffn_one_hot_expert(smoe):
     assert row_rel_err(got, oracle.routed_ffn_expertwise(x, ids, load)) <= ROW_TOL
 
 
-def run_fp16(smoe, x, ids, E, I, wg, wu, wd):
+def run_fp16(smoe, x, ids, E, I, wg, wu, wd, shared=None, calls=1):
     T, k = ids.shape
     H = x.shape[1]
     al = oracle.align_by_expert(ids, E)
-    ws = torch.zeros(smoe.smoe_ffn_workspace_bytes(T, k, E, H, I), dtype=torch.uint8,
+    sh, sh_out, Is = _shared_dev(shared, T, H)
+    ws = torch.zeros(smoe.smoe_ffn_workspace_bytes(T, k, E, H, I, Is), dtype=torch.uint8,
                      device="cuda")
-    out = torch.full((T * k, H), float("nan"), dtype=torch.float32, device="cuda")
-    smoe.smoe_fp16_expert_ffn(dev(x), k, E, I, dev(wg), dev(wu), dev(wd),
-                              dev(al["sorted_slots"]), dev(al["offsets"]), ws, out)
-    return host(out)
+    args = [dev(a) for a in (x, wg, wu, wd, al["sorted_slots"], al["offsets"])]
+    for _ in range(calls):
+        out = torch.full((T * k, H), float("nan"), dtype=torch.float32, device="cuda")
+        if sh_out is not None:
+            sh_out.fill_(float("nan"))
+        smoe.smoe_fp16_expert_ffn(args[0], k, E, I, *args[1:4], args[4], args[5], ws, out,
+                                  shared=sh, shared_out=sh_out)
+    if shared is None:
+        return host(out)
+    return host(out), host(sh_out)
 
 
 def test_fp16_ffn_shared_expert_dsv2(smoe):
@@ -337,6 +362,57 @@ def test_fp16_ffn_shared_expert_dsv2(smoe):
     got = run_fp16(smoe, L.x, ids, 1, L.sg16.shape[0], L.sg16[None], L.su16[None], L.sd16[None])
     ref = oracle.shared_ffn(L.x, L.sg16, L.su16, L.sd16)
     assert row_rel_err(got, ref) <= ROW_TOL
+
+
+@pytest.mark.parametrize("name", ["dsv2", "qwen"])
+def test_w4a16_ffn_with_shared_expert(smoe, name):
+    # routed INT4 experts and the FP16 shared expert(s) in the same launches,
+    # three calls in a row on one workspace
+    L = layer(name)
+    cfg = L.cfg
+    ids = oracle.topk_experts(oracle.router_logits_f32(L.x, L.w_router, L.router_bias), cfg.k)
+    got, got_sh = run_w4a16(smoe, L.x, ids, cfg.E, cfg.I, cfg.G, L.wg_q, L.wg_s, L.wu_q,
+                            L.wu_s, L.wd_q, L.wd_s, shared=(L.sg16, L.su16, L.sd16), calls=3)
+    assert np.isfinite(got).all() and np.isfinite(got_sh).all()
+    assert row_rel_err(got, oracle_slots_int4(L, ids)) <= ROW_TOL
+    assert row_rel_err(got_sh, oracle.shared_ffn(L.x, L.sg16, L.su16, L.sd16)) <= ROW_TOL
+
+
+@pytest.mark.parametrize("E,k,T,H,I,G,Is", [
+    (8, 2, 40, 256, 384, 64, 640),   # shared expert over two token chunks (32 + 8)
+    (16, 1, 1, 384, 256, 128, 256),  # a single token
+    (6, 3, 17, 128, 128, 32, 3072),  # shared rows staged in several k phases
+])
+def test_w4a16_ffn_with_shared_shapes(smoe, E, k, T, H, I, G, Is):
+    rng = np.random.default_rng(T + Is)
+    x = rng.standard_normal((T, H)).astype(np.float16)
+    q = _synthetic_int4(E, H, I, G, seed=E + Is)
+    sg = (rng.standard_normal((Is, H)) * 0.02).astype(np.float16)
+    su = (rng.standard_normal((Is, H)) * 0.02).astype(np.float16)
+    sd = (rng.standard_normal((H, Is)) * 0.02).astype(np.float16)
+    ids = np.stack([rng.permutation(E)[:k] for _ in range(T)]).astype(np.int32)
+    got, got_sh = run_w4a16(smoe, x, ids, E, I, G, q["wg_q"], q["wg_s"], q["wu_q"], q["wu_s"],
+                            q["wd_q"], q["wd_s"], shared=(sg, su, sd), calls=2)
+
+    def load(e):
+        return tuple(oracle.dequant_int4(q[n + "_q"][e], q[n + "_s"][e], G) for n in ("wg", "wu", "wd"))
+    assert row_rel_err(got, oracle.routed_ffn_expertwise(x, ids, load)) <= ROW_TOL
+    assert row_rel_err(got_sh, oracle.shared_ffn(x, sg, su, sd)) <= ROW_TOL
+
+
+def test_fp16_ffn_with_shared_expert(smoe):
+    E, k, T, H, I, Is = 8, 2, 17, 256, 512, 768
+    rng = np.random.default_rng(5)
+    x = rng.standard_normal((T, H)).astype(np.float16)
+    wg, wu = [(rng.standard_normal((E, I, H)) * 0.02).astype(np.float16) for _ in range(2)]
+    wd = (rng.standard_normal((E, H, I)) * 0.02).astype(np.float16)
+    sg, su = [(rng.standard_normal((Is, H)) * 0.02).astype(np.float16) for _ in range(2)]
+    sd = (rng.standard_normal((H, Is)) * 0.02).astype(np.float16)
+    ids = np.stack([rng.permutation(E)[:k] for _ in range(T)]).astype(np.int32)
+    got, got_sh = run_fp16(smoe, x, ids, E, I, wg, wu, wd, shared=(sg, su, sd), calls=2)
+    ref = oracle.routed_ffn_expertwise(x, ids, lambda e: (wg[e], wu[e], wd[e]))
+    assert row_rel_err(got, ref) <= ROW_TOL
+    assert row_rel_err(got_sh, oracle.shared_ffn(x, sg, su, sd)) <= ROW_TOL
 
 
 @pytest.mark.parametrize("E,k,T,H,I", [(8, 2, 17, 256, 512), (4, 2, 150, 256, 256),
@@ -400,13 +476,14 @@ def test_combine_matches_oracle(smoe):
 # ------------------------------------------------------------------ whole layer
 
 @pytest.mark.parametrize("name", ["tiny", "dsv2", "qwen"])
-@pytest.mark.parametrize("side", [False, True])
-def test_layer_draft_matches_oracle(smoe, name, side):
+@pytest.mark.parametrize("mode", ["fused", "separate", "side"])
+def test_layer_draft_matches_oracle(smoe, name, mode):
     from quantized_speculative_expert_amd.layer import DeviceLayer
     L = layer(name)
     ref = oracle.moe_layer(L, "draft")
     d = DeviceLayer(L)
-    d.run(side_stream=torch.cuda.Stream() if side else None)
+    d.run(fuse_shared=mode == "fused",
+          side_stream=torch.cuda.Stream() if mode == "side" else None)
     assert np.array_equal(host(d.topk_ids), ref["ids"])
     assert np.array_equal(host(d.sorted_slots), ref["sorted_slots"])
     assert int(host(d.n_active)[0]) == int(ref["n_active"])
@@ -419,19 +496,20 @@ def test_layer_draft_matches_oracle(smoe, name, side):
         assert np.array_equal(host(d.plan_ids), pid) and np.array_equal(host(d.plan_counts), pc)
 
 
-def test_layer_graph_replay_matches_eager(smoe):
+@pytest.mark.parametrize("fused", [True, False])
+def test_layer_graph_replay_matches_eager(smoe, fused):
     from quantized_speculative_expert_amd.layer import DeviceLayer
     L = layer("dsv2")
     d = DeviceLayer(L)
-    d.run(elb=False)
+    d.run(elb=False, fuse_shared=fused)
     eager = host(d.y).copy()
-    side = torch.cuda.Stream()
+    side = None if fused else torch.cuda.Stream()
     g = torch.cuda.CUDAGraph()
     s = torch.cuda.Stream()
     s.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(s):
         with torch.cuda.graph(g, stream=s):
-            d.run(elb=False, side_stream=side)
+            d.run(elb=False, fuse_shared=fused, side_stream=side)
     torch.cuda.current_stream().wait_stream(s)
     ids_eager = host(d.topk_ids).copy()
     for _ in range(3):
