@@ -53,9 +53,12 @@ def parse_args():
     p.add_argument("--config", default="dsv2", help="workload shape (default dsv2)")
     p.add_argument("--copies", type=int, default=0,
                    help="weight copies to rotate (0 = enough for >= 1 GiB)")
-    p.add_argument("--shared", choices=("fused", "separate", "side"), default="fused",
-                   help="shared experts inside the routed FFN launches (fused), as a call of "
-                        "their own on the main stream (separate) or on a side stream (side)")
+    p.add_argument("--shared", choices=("fused", "separate"), default="fused",
+                   help="shared experts inside the routed FFN launches (fused) or as a call "
+                        "of their own (separate)")
+    p.add_argument("--side-stream", action="store_true",
+                   help="run the ELB update (and a separate shared-expert call) on a side "
+                        "stream branch of the step graph instead of in line")
     p.add_argument("--cpu-reps", type=int, default=2,
                    help="full layers the CPU reference runs for cpu_baseline (0 = skip)")
     return p.parse_args()
@@ -200,7 +203,7 @@ def main() -> int:
     log(f"{copies} weight copies x {wbytes / 2**20:.1f} MiB resident")
 
     fused = args.shared == "fused"
-    side = torch.cuda.Stream(device=dev) if args.shared == "side" else None
+    side = torch.cuda.Stream(device=dev) if args.side_stream else None
     use_elb = cfg.elb_M > 0
 
     def step(d):
@@ -299,6 +302,7 @@ def main() -> int:
             "T": cfg.T, "E": cfg.E, "k": cfg.k, "H": cfg.H, "I": cfg.I, "G": cfg.G,
             "shared_I": cfg.shared_I, "elb_M": cfg.elb_M, "weights": "int4 g%d + fp16 scales" % cfg.G,
             "shared_experts": args.shared,
+            "side_stream": side is not None,
         },
         "hbm_gbps": round(layer_gbps, 1),
         "hbm_frac": round(layer_gbps / PEAK_HBM_GBPS, 4),

@@ -76,12 +76,12 @@ const char* smoe_last_error(void);
  * shared_gate[t] = 1 / (1 + exp(-x[t] . shared_gate_w)) when both pointers
  * are non-NULL (sigmoid gate of a shared expert).
  *
- *   x            fp16 [T][H]
+ *   x            fp16 [T][H], 16-byte aligned
  *   w_router     float [E][H]
  *   logit_bias   float [E] or NULL
  *   topk_ids     int32 [T][k]   (out)
  *   topk_w       float [T][k]   (out)
- *   logits       float [T][E]   (out, optional, NULL to skip)
+ *   logits       float [T][E]   (out; the top-k is taken from it)
  *   shared_gate_w float [H] or NULL; shared_gate float [T] (out) or NULL
  * T = 0 enqueues nothing. Non-finite logits give an unspecified selection.
  */

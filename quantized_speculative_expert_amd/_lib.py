@@ -114,8 +114,8 @@ def _shared_args(shared, shared_out):
             _ptr(sd, torch.float16, "shared_wd"), _ptr(shared_out, torch.float32, "shared_out"))
 
 
-def smoe_route_topk(x, w_router, logit_bias, k: int, flags: int, topk_ids, topk_w,
-                    logits=None, shared_gate_w=None, shared_gate=None, stream=None) -> None:
+def smoe_route_topk(x, w_router, logit_bias, k: int, flags: int, topk_ids, topk_w, logits,
+                    shared_gate_w=None, shared_gate=None, stream=None) -> None:
     T, H = x.shape
     E = w_router.shape[0]
     _check("smoe_route_topk", _lib.smoe_route_topk(

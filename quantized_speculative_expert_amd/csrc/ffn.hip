@@ -28,9 +28,12 @@
 //   (stage 2): 16 / 32 rows per wave of an 8-wave workgroup. The reduction
 //   dim K is cut into parts of D blocks. An item is (chunk, row tile, part);
 //   the routed experts' items come first, the shared expert's after them.
-//   The persistent grid gives every busy workgroup the same count
-//   q = ceil(n / nwg) of consecutive items. The list is built on the device
-//   from expert_offsets (nothing is read back).
+//   The list is built on the device from expert_offsets (nothing is read
+//   back). Each workgroup of the persistent grid first takes a run of
+//   consecutive items (nine tenths of an even share); the rest goes out
+//   in units of two consecutive items through a few device-scope ticket
+//   counters, so workgroups that stream faster take more of it and the
+//   grid finishes together instead of waiting on its slowest members.
 // * Split K. A workgroup adds the consecutive parts of a tile in registers.
 //   A tile it holds whole is stored; a tile shared with other workgroups is
 //   added into the output with device-scope float atomics (no return value,
@@ -39,7 +42,9 @@
 //   next call. The workspace keeps two g/u buffers and a two-word call
 //   counter that picks the current one: stage 1 reads word 0 and writes
 //   word 1, stage 2 reads word 1 and writes word 0, so no word is written
-//   while another workgroup of the same launch may still read it.
+//   while another workgroup of the same launch may still read it. Each
+//   stage likewise resets the other stage's ticket counters for its next
+//   launch.
 // * Activations in LDS. The sorted slots and expert offsets come in with the
 //   first round trip. A chunk's activation rows (x rows of its tokens in
 //   stage 1, SiLU(g) * u of its positions in stage 2) are staged into LDS
@@ -97,7 +102,13 @@ constexpr int kWavesPerWg = 8;             // 4 waves per SIMD at two workgroups
 constexpr int kThreads = kWavesPerWg * kWave;
 constexpr int kMaxChunk = 32;              // slots per chunk (two MFMA column groups)
 constexpr int kCpOff = (kMaxE + 1 + 3) / 4 * 4;  // chunk prefix table, 16-byte aligned
-constexpr int kTabInts = kCpOff + kMaxE + 1;
+constexpr int kTkOff = kCpOff + kMaxE + 1;     // work-ticket slots (2 words)
+constexpr int kTabInts = kTkOff + 2;
+constexpr int kPools = 8;                  // work-ticket counters per stage
+constexpr int kUnit = 2;                   // consecutive items per ticket
+constexpr int kStaticPermille = 900;       // share of the even split taken up front
+constexpr int kHdrCtr1 = 8;                // header words of the stage-1 counters
+constexpr int kHdrCtr2 = kHdrCtr1 + kPools;
 constexpr int kTabBytes = (kTabInts * 4 + 15) / 16 * 16;  // offsets, chunk prefix
 static_assert(kTabBytes % 16 == 0, "staged rows must start 16-byte aligned");
 constexpr int kMaxSlotsLds = 1024;         // sorted slots kept whole in LDS up to this many
@@ -137,7 +148,8 @@ struct FfnArgs {
   const int32_t* sorted_slots;  // [S]
   const int32_t* offsets;       // [E+1]
   float* gu;                    // two g/u buffers
-  int* epoch;                   // [2] call counter words
+  int* hdr;                     // words 0, 1: call counter; then the work-ticket counters
+                                // of stage 1 and of stage 2
   long long gu_buf;             // floats per g/u buffer
   int E, k, S, T, H;
   int chunks_upper;             // routed chunks the work list can hold
@@ -207,6 +219,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
   extern __shared__ __align__(16) uint8_t smem[];
   int* s_off = reinterpret_cast<int*>(smem);
   int* s_cp = s_off + kCpOff;
+  int* s_tk = s_off + kTkOff;
   int* s_slots = reinterpret_cast<int*>(smem + kTabBytes);  // all slots, or the chunk's
   uint8_t* xs = smem + a.xs_off;
 
@@ -231,7 +244,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
       slv[j] = i < a.S ? a.sorted_slots[i] : -1;
     }
   }
-  const int ep = a.epoch[STAGE == 1 ? 0 : 1];
+  const int ep = a.hdr[STAGE == 1 ? 0 : 1];
   float* gu = a.gu + ((STAGE == 1 ? ep : ep - 1) & 1) * a.gu_buf;  // this call's g/u
   if (tid <= E) s_off[tid] = min(max(offv, 0), a.S);  // clamped to [0, S]
   if (a.slots_lds) {
@@ -239,7 +252,13 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
     for (int j = 0; j < kSlotsPer; ++j)
       if (tid + j * kThreads < a.S) s_slots[tid + j * kThreads] = slv[j];
   }
-  if (b == 0 && tid == 0) a.epoch[STAGE == 1 ? 1 : 0] = STAGE == 1 ? ep + 1 : ep;
+  if (b == 0) {
+    if (tid == 0) a.hdr[STAGE == 1 ? 1 : 0] = STAGE == 1 ? ep + 1 : ep;
+    // the other stage's ticket counters start its next launch at zero
+    if (tid < kPools)
+      __hip_atomic_store(a.hdr + (STAGE == 1 ? kHdrCtr2 : kHdrCtr1) + tid, 0, __ATOMIC_RELAXED,
+                         __HIP_MEMORY_SCOPE_AGENT);
+  }
   __syncthreads();
 
   // ---- work list: chunk prefix over the routed experts
@@ -270,11 +289,45 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
                       ? (a.T + a.grp[1].csz - 1) / a.grp[1].csz * a.grp[1].tiles * a.grp[1].parts
                       : 0;
   const int n_items = n_r + n_s;
-  // q items per workgroup and only ceil(n_items / q) workgroups busy, so
-  // every busy workgroup streams the same number of bytes
-  const int q = (n_items + gridDim.x - 1) / gridDim.x;
-  const int i0 = b * q;
-  const int i1 = min(n_items, i0 + q);
+  // Work split. Every workgroup first takes q0 consecutive items (nine
+  // tenths of an even share, rounded down; none when that is under two).
+  // The rest is cut into units of two consecutive items dealt out in
+  // kPools pools:
+  // pool p holds units p, p + kPools, ..., and workgroup b takes tickets
+  // from the counter of pool b % kPools. A ticket for the unit that starts
+  // at position pos + 2 of the workgroup's sequence is taken while it
+  // works on position pos, so it is back long before it is needed. The
+  // workgroups that stream faster take more units and all finish close
+  // together.
+  const int nwg = gridDim.x;
+  int q0 = static_cast<int>(static_cast<long long>(n_items) * kStaticPermille / 1000 / nwg);
+  if (q0 < 2) q0 = 0;
+  const int s0 = b * q0;
+  const int dyn_base = nwg * q0;
+  const int n_units = (n_items - dyn_base + kUnit - 1) / kUnit;
+  const int pool = b & (kPools - 1);
+  int* ctr = a.hdr + (STAGE == 1 ? kHdrCtr1 : kHdrCtr2) + pool;
+  // first item of the unit of ticket t (-1: no such unit)
+  auto unit_item = [&](int t) {
+    const long long u = pool + static_cast<long long>(kPools) * t;
+    return u < n_units ? dyn_base + kUnit * static_cast<int>(u) : -1;
+  };
+  // the item after `i` in its unit (-1 past the end of the list)
+  auto next_in_unit = [&](int i) { return i >= 0 && i + 1 < n_items ? i + 1 : -1; };
+  int cur, nxt;
+  if (q0 > 0) {
+    cur = s0;
+    nxt = s0 + 1;
+  } else {  // no static run: tickets for positions 0 and 1 now
+    if (tid == 0)
+      s_tk[0] = __hip_atomic_fetch_add(ctr, kUnit > 1 ? 1 : 2, __ATOMIC_RELAXED,
+                                       __HIP_MEMORY_SCOPE_AGENT);
+    __syncthreads();
+    const int t = s_tk[0];
+    cur = uniform(unit_item(t));
+    nxt = uniform(kUnit > 1 ? next_in_unit(cur) : (cur >= 0 ? unit_item(t + 1) : -1));
+    __syncthreads();  // the slot is free again
+  }
 
   // Stage 1 clears what split tiles will add into: the stage-2 outputs and
   // the other g/u buffer (for the next call). Each workgroup clears its
@@ -294,7 +347,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
       *dst = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
     }
   };
-  if (i0 >= i1) {  // whole workgroup
+  if (cur < 0) {  // whole workgroup
     clear_share();
     return;
   }
@@ -589,44 +642,50 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
   };
 
   auto kblk_of = [&](int fmt) { return (WK == kInt4 && fmt == kInt4) ? 128 : 32; };
-  // k window to stage for item `it` (number `item`): if this workgroup's
-  // remaining items all lie in the item's tile, just the k they cover;
-  // else the LDS phase holding the item (the rows then serve the next
-  // tiles of the chunk too). At most kph wide.
+  // k window to stage for item `it` (number `item`), whose run of
+  // consecutive items in this workgroup ends before run_end: if the run
+  // stays in the item's tile, just the k it covers; else the LDS phase
+  // holding the item (the rows then serve the next tiles of the chunk
+  // too). At most kph wide.
   int st_lo = 0, st_hi = 0;
-  auto window = [&](const Item& it, int item) {
+  auto window = [&](const Item& it, int item, int run_end) {
     const Group& gr = a.grp[it.grp];
     const int kpart = D * kblk_of(WK == kInt4 ? gr.fmt : kFp16);
     const int k0 = it.part * kpart;
     const int left_in_tile = gr.parts - 1 - it.part;  // items after this one in its tile
-    if (i1 - 1 - item <= left_in_tile) {
+    if (run_end - 1 - item <= left_in_tile) {
       st_lo = k0;
-      st_hi = min(gr.K, min(k0 + a.kph, (it.part + i1 - item) * kpart));
+      st_hi = min(gr.K, min(k0 + a.kph, (it.part + run_end - item) * kpart));
     } else {
       st_lo = k0 / a.kph * a.kph;
       st_hi = min(gr.K, st_lo + a.kph);
     }
   };
+  // end of the run of consecutive items that `item` (at position pos) starts
+  auto run_end_of = [&](int pos, int item, int next) {
+    return pos < q0 ? s0 + q0 : (next == item + 1 ? item + 2 : item + 1);
+  };
 
   // ---- prologue: stage the first chunk, the first item's blocks in flight
-  Item ci = decode(i0);
+  Item ci = decode(cur);
   set_load_item(ci);
   u32x4 ring[D][2];
   int c_fmt = l_fmt, c_nblk = l_nblk;
   int staged_id = ci.grp * (1 << 24) + ci.chunk;
-  window(ci, i0);
+  window(ci, cur, run_end_of(0, cur, nxt));
   stage_rows(ci, st_lo, st_hi, std::integral_constant<int, STAGE == 1 ? 4 : 2>(), [&]() {
     if (WK == kInt4 && l_fmt == kInt4) load_scales(l_blk0);
 #pragma unroll
     for (int d = 0; d < D; ++d) load(ring[d], min(l_blk0 + d, l_nblk - 1));
   });
   int seg_pa = ci.part;  // first part of the tile accumulated so far
+  int prev = -2;         // the item before cur
 
-  for (int item = i0; item < i1; ++item) {
+  for (int pos = 0;; ++pos) {
     const int P = a.grp[ci.grp].parts;
     const int blk0 = ci.part * D;
     const int kblk = kblk_of(c_fmt);
-    if (item == i0 || ci.part == 0) {
+    if (cur != prev + 1 || ci.part == 0) {
       seg_pa = ci.part;
 #pragma unroll
       for (int m = 0; m < 2; ++m)
@@ -637,23 +696,37 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
     const int k0 = blk0 * kblk;
     const int k1 = min(a.grp[ci.grp].K, k0 + D * kblk);
     if (id != staged_id || k0 < st_lo || k1 > st_hi) {
-      window(ci, item);
+      window(ci, cur, run_end_of(pos, cur, nxt));
       stage_rows(ci, st_lo, st_hi, std::integral_constant<int, STAGE == 1 ? 2 : 1>(), []() {});
       staged_id = id;
     }
 
-    // the load cursor moves to the next item
-    const bool l_live = item + 1 < i1;
+    // position pos + 2 starts a unit: take its ticket now
+    const int r = pos + 2 - q0;
+    const bool grab = r >= 0 && r % kUnit == 0 && nxt >= 0;
+    int tk_new = 0;
+    if (grab && tid == 0) {
+      // the address goes through a VGPR so the compiler issues the plain
+      // returning atomic (no cross-lane combining that waits on its result
+      // right away); the result is first needed at the end of the item
+      typedef __attribute__((address_space(1))) int global_int;
+      global_int* cp = (global_int*)ctr;
+      asm volatile("" : "+v"(cp));
+      tk_new = __hip_atomic_fetch_add(cp, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+
+    // the load cursor moves to the next item (or reloads this one's blocks)
+    const bool l_live = nxt >= 0;
     if (WK == kInt4) {
 #pragma unroll
       for (int m = 0; m < 2; ++m)
 #pragma unroll
         for (int t = 0; t < NS; ++t) scur[m][t] = sring[m][t];
     }
-    Item nxt = ci;
+    Item ni = ci;
     if (l_live) {
-      nxt = decode(item + 1);
-      set_load_item(nxt);
+      ni = decode(nxt);
+      set_load_item(ni);
       if (WK == kInt4 && l_fmt == kInt4) load_scales(l_blk0);
     }
 
@@ -674,15 +747,28 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
             compute_fp16(ring[d], kk0 + d * 32, std::integral_constant<int, 1>());
         }
       }
-      if (l_live) load(ring[d], min(l_blk0 + d, l_nblk - 1));
+      load(ring[d], min(l_blk0 + d, l_nblk - 1));
     }
 
-    if (item + 1 == i1 || ci.part == P - 1) write_tile(ci, seg_pa == 0 && ci.part == P - 1);
-    if (l_live) {
-      ci = nxt;
-      c_fmt = l_fmt;
-      c_nblk = l_nblk;
+    if (nxt != cur + 1 || ci.part == P - 1) write_tile(ci, seg_pa == 0 && ci.part == P - 1);
+    if (!l_live) break;
+    if (grab) {
+      if (tid == 0) s_tk[(r / kUnit) & 1] = tk_new;  // slots alternate between tickets
+      __syncthreads();  // the new ticket is visible
     }
+    int nn;
+    if (r < 0)
+      nn = s0 + pos + 2;
+    else if (r % kUnit != 0)
+      nn = next_in_unit(nxt);
+    else
+      nn = uniform(unit_item(s_tk[(r / kUnit) & 1]));
+    prev = cur;
+    cur = nxt;
+    nxt = nn;
+    ci = ni;
+    c_fmt = l_fmt;
+    c_nblk = l_nblk;
   }
   clear_share();
 }
@@ -790,7 +876,7 @@ void make_plans(StagePlans& p, const void* x, int T, int k, int H, const int32_t
   a1.x = static_cast<const uint16_t*>(x);
   a1.sorted_slots = sorted_slots;
   a1.offsets = offsets;
-  a1.epoch = reinterpret_cast<int*>(wsb);
+  a1.hdr = reinterpret_cast<int*>(wsb);
   a1.gu = reinterpret_cast<float*>(wsb + kEpochBytes);
   a1.gu_buf = gu_floats(T, k, gw[0].I, n_groups > 1 ? gw[1].I : 0);
   a1.E = gw[0].E; a1.k = k; a1.S = S; a1.T = T; a1.H = H;

@@ -168,29 +168,49 @@ class DeviceLayer:
             side_stream=None) -> None:
         """Enqueue the whole layer on the current stream.
 
-        fuse_shared runs the shared experts inside the routed FFN call.
-        Otherwise they get a call of their own; with side_stream it runs
-        there, ordered after the current stream's prior work and joined
-        before the combine.
+        fuse_shared runs the shared experts inside the routed FFN call;
+        otherwise they get a call of their own. With side_stream, the work
+        off the layer's critical path runs there: the ELB update (it needs
+        only the routing) and a separate shared-expert call (it needs only
+        x). The side stream forks from the current stream and joins it again
+        before the layer ends (before the combine for the shared experts).
         """
         separate = not fuse_shared and self.shared_out is not None
+        use_elb = elb and self.cfg.elb_M > 0 and not target
         main = torch.cuda.current_stream(self.device)
-        join = None
+        side = side_stream
+
+        def fork():
+            ev = torch.cuda.Event()
+            ev.record(main)
+            side.wait_event(ev)
+
+        def join():
+            ev = torch.cuda.Event()
+            ev.record(side)
+            main.wait_event(ev)
+
         if separate:
-            if side_stream is not None:
-                fork = torch.cuda.Event()
-                fork.record(main)
-                side_stream.wait_event(fork)
-                self.shared_ffn(stream=side_stream)
-                join = torch.cuda.Event()
-                join.record(side_stream)
+            if side is not None:
+                fork()
+                self.shared_ffn(stream=side)
             else:
                 self.shared_ffn()
+        shared_done = None
+        if separate and side is not None:
+            shared_done = torch.cuda.Event()
+            shared_done.record(side)
         self.route()
+        if use_elb:
+            if side is not None:
+                fork()
+                self.elb(stream=side)
+            else:
+                self.elb()
         self.align()
-        if elb and self.cfg.elb_M > 0 and not target:
-            self.elb()
         self.routed_ffn(target=target, with_shared=not separate)
-        if join is not None:
-            main.wait_event(join)
+        if shared_done is not None:
+            main.wait_event(shared_done)
         self.combine()
+        if side is not None and (separate or use_elb):
+            join()

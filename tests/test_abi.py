@@ -86,6 +86,8 @@ def test_route_argument_checks(lib):
     assert f(N, N, N, 17, 2048, 64, 6, 4, N, N, N, N, N, N) == EINVAL       # bad flag
     assert f(N, N, N, 17, 2048, 64, 6, 0, N, N, N, N, N, N) == EINVAL       # null x
     assert b"null" in lib.smoe_last_error()
+    assert f(16, 16, N, 17, 2048, 64, 6, 0, 16, 16, N, N, N, N) == EINVAL   # logits required
+    assert f(8, 16, N, 17, 2048, 64, 6, 0, 16, 16, 16, N, N, N) == EINVAL   # x alignment
     assert f(N, N, N, 0, 2048, 64, 6, 0, N, N, N, N, N, N) == 0             # empty window
 
 

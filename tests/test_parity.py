@@ -476,14 +476,14 @@ def test_combine_matches_oracle(smoe):
 # ------------------------------------------------------------------ whole layer
 
 @pytest.mark.parametrize("name", ["tiny", "dsv2", "qwen"])
-@pytest.mark.parametrize("mode", ["fused", "separate", "side"])
+@pytest.mark.parametrize("mode", ["fused", "fused-side", "separate", "separate-side"])
 def test_layer_draft_matches_oracle(smoe, name, mode):
     from quantized_speculative_expert_amd.layer import DeviceLayer
     L = layer(name)
     ref = oracle.moe_layer(L, "draft")
     d = DeviceLayer(L)
-    d.run(fuse_shared=mode == "fused",
-          side_stream=torch.cuda.Stream() if mode == "side" else None)
+    d.run(fuse_shared=mode.startswith("fused"),
+          side_stream=torch.cuda.Stream() if mode.endswith("side") else None)
     assert np.array_equal(host(d.topk_ids), ref["ids"])
     assert np.array_equal(host(d.sorted_slots), ref["sorted_slots"])
     assert int(host(d.n_active)[0]) == int(ref["n_active"])
@@ -503,22 +503,26 @@ def test_layer_graph_replay_matches_eager(smoe, fused):
     d = DeviceLayer(L)
     d.run(elb=False, fuse_shared=fused)
     eager = host(d.y).copy()
-    side = None if fused else torch.cuda.Stream()
+    side = torch.cuda.Stream()
     g = torch.cuda.CUDAGraph()
     s = torch.cuda.Stream()
     s.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(s):
         with torch.cuda.graph(g, stream=s):
-            d.run(elb=False, fuse_shared=fused, side_stream=side)
+            # the ELB update runs on the side branch of the graph
+            d.run(elb=True, fuse_shared=fused, side_stream=side)
     torch.cuda.current_stream().wait_stream(s)
     ids_eager = host(d.topk_ids).copy()
-    for _ in range(3):
+    once = np.bincount(ids_eager.ravel(), minlength=L.cfg.E)
+    d.elb_counts.zero_()
+    for rep in range(3):
         d.y.zero_()
         d.topk_ids.fill_(-1)
         torch.cuda.synchronize()
         g.replay()
         torch.cuda.synchronize()
         assert np.array_equal(host(d.topk_ids), ids_eager)
+        assert np.array_equal(host(d.elb_counts)[0], (rep + 1) * once)
         # split-K tiles add fp32 partial sums with device atomics, so the
         # float output may differ from the eager run in the last bits
         assert row_rel_err(host(d.y), eager) <= 1e-3
