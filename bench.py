@@ -36,6 +36,7 @@ if ROOT not in sys.path:
 METRIC = "W4A16 MoE-layer tokens/sec + achieved HBM GB/s fraction, K=16 window"
 PEAK_HBM_GBPS = 8000.0          # MI355X HBM3E, vendor figure
 MIN_ROTATION_BYTES = 1 << 30    # rotate weight copies over at least this many bytes
+FFN_CALLS_PER_GRAPH = 8         # expert-FFN calls per timing graph
 PROFILES = os.path.join(ROOT, "profiles")
 FFN_SOURCES = [os.path.join(ROOT, "quantized_speculative_expert_amd", "csrc", f)
                for f in ("ffn.hip", "smoe_internal.hpp")]
@@ -59,7 +60,10 @@ def parse_args():
     p.add_argument("--side-stream", action="store_true",
                    help="run the ELB update (and a separate shared-expert call) on a side "
                         "stream branch of the step graph instead of in line")
-    p.add_argument("--cpu-reps", type=int, default=2,
+    p.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                   help="only run a plain device copy of MIB MiB `steps` times (reads MIB, "
+                        "writes MIB): the reference that scales the HBM traffic counters")
+    p.add_argument("--cpu-reps", type=int, default=10,
                    help="full layers the CPU reference runs for cpu_baseline (0 = skip)")
     return p.parse_args()
 
@@ -162,6 +166,21 @@ def cpu_baseline(cfg_name: str, reps: int):
 
 # ----------------------------------------------------------------------------- GPU leg
 
+def copy_calibration(mib: int, calls: int) -> int:
+    """A plain elementwise copy kernel (dst = src * 1) of known size."""
+    import torch
+    n = mib << 20
+    src = torch.ones(n // 4, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(calls):
+        torch.mul(src, 1.0, out=dst)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration": {"bytes_read": n, "bytes_written": n, "calls": calls}}),
+          flush=True)
+    return 0
+
+
 def percentiles(xs):
     import numpy as np
     a = np.asarray(xs, dtype=float)
@@ -183,6 +202,8 @@ def main() -> int:
     if not torch.cuda.is_available():
         print("bench.py needs a GPU (torch.cuda.is_available() is False)", file=sys.stderr)
         return 1
+    if args.copy_calibration > 0:
+        return copy_calibration(args.copy_calibration, args.steps)
     from quantized_speculative_expert_amd.layer import DeviceLayer
     from workload import get_config, make_layer
 
@@ -215,17 +236,20 @@ def main() -> int:
     torch.cuda.synchronize()
     cap = torch.cuda.Stream(device=dev)
     cap.wait_stream(torch.cuda.current_stream())
-    step_graphs, ffn_graphs = [], []
+    step_graphs = []
+    # the FFN alone: FFN_CALLS_PER_GRAPH back-to-back calls cycling over the
+    # weight copies in one graph, so the per-call time is that of the two
+    # launches and the gap between them, not of a graph launch
+    ffn_graph = torch.cuda.CUDAGraph()
     with torch.cuda.stream(cap):
         for d in layers:
             g = torch.cuda.CUDAGraph()
             with torch.cuda.graph(g, stream=cap):
                 step(d)
             step_graphs.append(g)
-            g2 = torch.cuda.CUDAGraph()
-            with torch.cuda.graph(g2, stream=cap):
-                d.routed_ffn(with_shared=fused)
-            ffn_graphs.append(g2)
+        with torch.cuda.graph(ffn_graph, stream=cap):
+            for i in range(FFN_CALLS_PER_GRAPH):
+                layers[i % copies].routed_ffn(with_shared=fused)
     torch.cuda.current_stream().wait_stream(cap)
     torch.cuda.synchronize()
 
@@ -258,15 +282,17 @@ def main() -> int:
 
     # ---- dominant call: W4A16 expert FFN (two launches; with the shared
     # experts when fused), HIP events on the stream it runs on
-    log(f"timing {K} W4A16 expert-FFN calls")
-    fe = [torch.cuda.Event(enable_timing=True) for _ in range(K + 1)]
+    R = max(1, K // FFN_CALLS_PER_GRAPH)
+    log(f"timing {R * FFN_CALLS_PER_GRAPH} W4A16 expert-FFN calls")
+    ffn_graph.replay()
+    fe = [torch.cuda.Event(enable_timing=True) for _ in range(R + 1)]
     torch.cuda.synchronize()
     fe[0].record(stream)
-    for i in range(K):
-        ffn_graphs[i % copies].replay()
+    for i in range(R):
+        ffn_graph.replay()
         fe[i + 1].record(stream)
     torch.cuda.synchronize()
-    ffn_us = [1e3 * fe[i].elapsed_time(fe[i + 1]) for i in range(K)]
+    ffn_us = [1e3 * fe[i].elapsed_time(fe[i + 1]) / FFN_CALLS_PER_GRAPH for i in range(R)]
     ffn_stats = percentiles(ffn_us)
     fb = ffn_bytes(base, n_active, fused)
     achieved = fb / (ffn_stats["mean"] * 1e3)  # bytes/ns = GB/s

@@ -44,18 +44,32 @@ __global__ __launch_bounds__(kAlignThreads) void align_kernel(
   const int c_begin = wave * per_wave;
   const int c_end = min(nchunks, c_begin + per_wave);
 
+  // the first kCached chunks of a wave's run stay in registers for pass 2
+  constexpr int kCached = 4;
+  int cached[kCached];
+#pragma unroll
+  for (int j = 0; j < kCached; ++j) {
+    const int s = (c_begin + j) * kWave + lane;
+    cached[j] = (c_begin + j < c_end && s < S) ? ids[s] : -1;
+  }
+
   // pass 1: counts per (wave, expert)
-  for (int c = c_begin; c < c_end; ++c) {
-    const int s = c * kWave + lane;
-    const int e = s < S ? ids[s] : -1;
+  auto count = [&](int e) {
     if (e >= 0 && e < E) atomicAdd(&wave_cnt[wave][e], 1);
+  };
+#pragma unroll
+  for (int j = 0; j < kCached; ++j) count(cached[j]);
+  for (int c = c_begin + kCached; c < c_end; ++c) {
+    const int s = c * kWave + lane;
+    count(s < S ? ids[s] : -1);
   }
   __syncthreads();
 
-  // per expert: total, per-wave bases
+  // per expert: total, per-wave bases (only waves that own slots count)
+  const int busy_waves = per_wave > 0 ? min(kAlignWaves, (nchunks + per_wave - 1) / per_wave) : 0;
   for (int e = threadIdx.x; e < E; e += kAlignThreads) {
     int run = 0;
-    for (int w = 0; w < kAlignWaves; ++w) {
+    for (int w = 0; w < busy_waves; ++w) {
       wave_base[w][e] = run;
       run += wave_cnt[w][e];
     }
@@ -113,9 +127,8 @@ __global__ __launch_bounds__(kAlignThreads) void align_kernel(
   for (int i = lane; i < E; i += kWave) wave_cnt[wave][i] = 0;
   __builtin_amdgcn_wave_barrier();
   __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup");
-  for (int c = c_begin; c < c_end; ++c) {
+  auto place = [&](int c, int e) {
     const int s = c * kWave + lane;
-    const int e = s < S ? ids[s] : -1;
     const bool valid = e >= 0 && e < E;
     const uint64_t same = match_key8(valid ? e : 0, valid);
     const int rank = __popcll(same & lanes_below_mask());
@@ -130,6 +143,13 @@ __global__ __launch_bounds__(kAlignThreads) void align_kernel(
     if (last) wave_cnt[wave][e] += rank + 1;
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup");
+  };
+#pragma unroll
+  for (int j = 0; j < kCached; ++j)
+    if (c_begin + j < c_end) place(c_begin + j, cached[j]);
+  for (int c = c_begin + kCached; c < c_end; ++c) {
+    const int s = c * kWave + lane;
+    place(c, s < S ? ids[s] : -1);
   }
 }
 

@@ -27,18 +27,40 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(
   float acc[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) acc[i] = 0.0f;
-  for (int j = 0; j < k; ++j) {
-    const float wj = w[static_cast<size_t>(t) * k + j];
-    const float4* src =
-        reinterpret_cast<const float4*>(slot_out + (static_cast<size_t>(t) * k + j) * H + h0);
-    const float4 a = src[0], b = src[1];
-    acc[0] += wj * a.x; acc[1] += wj * a.y; acc[2] += wj * a.z; acc[3] += wj * a.w;
-    acc[4] += wj * b.x; acc[5] += wj * b.y; acc[6] += wj * b.z; acc[7] += wj * b.w;
+  // every slot's loads (and the shared row's) go out before the first is
+  // used (k <= kMaxK)
+  float4 sa = {0.0f, 0.0f, 0.0f, 0.0f}, sb = sa;
+  float sg = 1.0f;
+  if (shared_out != nullptr) {
+    const float4* src = reinterpret_cast<const float4*>(shared_out + static_cast<size_t>(t) * H + h0);
+    sa = src[0];
+    sb = src[1];
+    if (gate != nullptr) sg = gate[t];
+  }
+  float4 va[kMaxK], vb[kMaxK];
+  float wv[kMaxK];
+#pragma unroll
+  for (int j = 0; j < kMaxK; ++j) {
+    if (j < k) {
+      wv[j] = w[static_cast<size_t>(t) * k + j];
+      const float4* src =
+          reinterpret_cast<const float4*>(slot_out + (static_cast<size_t>(t) * k + j) * H + h0);
+      va[j] = src[0];
+      vb[j] = src[1];
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < kMaxK; ++j) {
+    if (j < k) {
+      const float wj = wv[j];
+      const float4 a = va[j], b = vb[j];
+      acc[0] += wj * a.x; acc[1] += wj * a.y; acc[2] += wj * a.z; acc[3] += wj * a.w;
+      acc[4] += wj * b.x; acc[5] += wj * b.y; acc[6] += wj * b.z; acc[7] += wj * b.w;
+    }
   }
   if (shared_out != nullptr) {
-    const float g = gate != nullptr ? gate[t] : 1.0f;
-    const float4* src = reinterpret_cast<const float4*>(shared_out + static_cast<size_t>(t) * H + h0);
-    const float4 a = src[0], b = src[1];
+    const float g = sg;
+    const float4 a = sa, b = sb;
     acc[0] += g * a.x; acc[1] += g * a.y; acc[2] += g * a.z; acc[3] += g * a.w;
     acc[4] += g * b.x; acc[5] += g * b.y; acc[6] += g * b.z; acc[7] += g * b.w;
   }
