@@ -142,6 +142,32 @@ smoe_status smoe_elb_accumulate_topm(int32_t* elb_counts, int L, int E,
                                      int flags, void* stream);
 
 /*
+ * Routing, alignment and the ELB update of one layer in one call.
+ * Computes exactly what these calls made one after the other compute:
+ *   smoe_route_topk(x, w_router, logit_bias, T, H, E, k, flags, topk_ids,
+ *                   topk_w, logits, shared_gate_w, shared_gate)
+ *   smoe_align_by_expert(topk_ids, T, k, E, expert_counts, expert_offsets,
+ *                        sorted_slots, active_experts, n_active)
+ *   and, when elb_counts is not NULL,
+ *   smoe_elb_accumulate_topm(elb_counts, L, E, topk_ids, layer, 1, T, k, M,
+ *                            plan_ids, plan_counts, elb_flags)
+ * with the same arguments, checks and errors. For windows of at most 512
+ * slots (T*k) the top-k, the alignment and the ELB update run in a single
+ * workgroup after the router logits, which saves two launches on the
+ * layer's critical path; larger windows run the three calls.
+ */
+smoe_status smoe_route_align_elb(const void* x, const float* w_router, const float* logit_bias,
+                                 int T, int H, int E, int k, int flags,
+                                 int32_t* topk_ids, float* topk_w, float* logits,
+                                 const float* shared_gate_w, float* shared_gate,
+                                 int32_t* expert_counts, int32_t* expert_offsets,
+                                 int32_t* sorted_slots, int32_t* active_experts,
+                                 int32_t* n_active,
+                                 int32_t* elb_counts, int L, int layer, int M,
+                                 int32_t* plan_ids, int32_t* plan_counts, int elb_flags,
+                                 void* stream);
+
+/*
  * Device workspace (bytes) that the expert FFN calls need for a window of
  * T tokens, k slots per token, routed intermediate size I and shared
  * intermediate size shared_I (0 = no shared expert): two fp32 buffers of

@@ -35,6 +35,8 @@ _SIGNATURES = {
     "smoe_last_error": (ctypes.c_char_p, []),
     "smoe_route_topk": (_i, [_p, _p, _p, _i, _i, _i, _i, _i, _p, _p, _p, _p, _p, _p]),
     "smoe_align_by_expert": (_i, [_p, _i, _i, _i, _p, _p, _p, _p, _p, _p]),
+    "smoe_route_align_elb": (_i, [_p, _p, _p, _i, _i, _i, _i, _i, _p, _p, _p, _p, _p,
+                                  _p, _p, _p, _p, _p, _p, _i, _i, _i, _p, _p, _i, _p]),
     "smoe_elb_accumulate_topm": (_i, [_p, _i, _i, _p, _i, _i, _i, _i, _i, _p, _p, _i, _p]),
     "smoe_ffn_workspace_bytes": (_sz, [_i, _i, _i, _i, _i, _i]),
     "smoe_w4a16_expert_ffn": (_i, [_p, _i, _i, _i, _i, _i, _i, _p, _p, _p, _p, _p, _p,
@@ -125,6 +127,33 @@ def smoe_route_topk(x, w_router, logit_bias, k: int, flags: int, topk_ids, topk_
         _ptr(logits, torch.float32, "logits"),
         _ptr(shared_gate_w, torch.float32, "shared_gate_w"),
         _ptr(shared_gate, torch.float32, "shared_gate"), _stream(stream)))
+
+
+def smoe_route_align_elb(x, w_router, logit_bias, k: int, flags: int, topk_ids, topk_w, logits,
+                         shared_gate_w, shared_gate, expert_counts, expert_offsets, sorted_slots,
+                         active_experts, n_active, elb_counts=None, layer: int = 0, M: int = 0,
+                         plan_ids=None, plan_counts=None, elb_flags: int = 0,
+                         stream=None) -> None:
+    """smoe_route_topk, smoe_align_by_expert and (with elb_counts [L][E])
+    smoe_elb_accumulate_topm for layer `layer`, in one call."""
+    T, H = x.shape
+    E = w_router.shape[0]
+    L = elb_counts.shape[0] if elb_counts is not None else 0
+    _check("smoe_route_align_elb", _lib.smoe_route_align_elb(
+        _ptr(x, torch.float16, "x"), _ptr(w_router, torch.float32, "w_router"),
+        _ptr(logit_bias, torch.float32, "logit_bias"), T, H, E, k, flags,
+        _ptr(topk_ids, torch.int32, "topk_ids"), _ptr(topk_w, torch.float32, "topk_w"),
+        _ptr(logits, torch.float32, "logits"),
+        _ptr(shared_gate_w, torch.float32, "shared_gate_w"),
+        _ptr(shared_gate, torch.float32, "shared_gate"),
+        _ptr(expert_counts, torch.int32, "expert_counts"),
+        _ptr(expert_offsets, torch.int32, "expert_offsets"),
+        _ptr(sorted_slots, torch.int32, "sorted_slots"),
+        _ptr(active_experts, torch.int32, "active_experts"),
+        _ptr(n_active, torch.int32, "n_active"),
+        _ptr(elb_counts, torch.int32, "elb_counts"), L, layer, M,
+        _ptr(plan_ids, torch.int32, "plan_ids"), _ptr(plan_counts, torch.int32, "plan_counts"),
+        elb_flags, _stream(stream)))
 
 
 def smoe_align_by_expert(topk_ids, E: int, expert_counts, expert_offsets, sorted_slots,

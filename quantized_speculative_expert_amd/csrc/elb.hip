@@ -16,7 +16,7 @@
 // one pass over the LDS copy of the row; experts placed below M write
 // themselves into the plan. Integer only, so the result is exact and
 // independent of thread timing.
-#include "smoe_internal.hpp"
+#include "smoe_blocks.hpp"
 
 namespace smoe {
 namespace {
@@ -30,43 +30,13 @@ __global__ __launch_bounds__(kElbThreads) void elb_kernel(
   __shared__ int hist[kMaxE];
   __shared__ int row[kMaxE];
   const int l = blockIdx.x;
-  int32_t* crow = cnt + static_cast<size_t>(l) * E;
-
-  for (int e = threadIdx.x; e < E; e += kElbThreads) hist[e] = 0;
-  __syncthreads();
   const int i = l - layer_begin;
-  if (ids != nullptr && i >= 0 && i < n_layers) {
-    const int32_t* lid = ids + static_cast<size_t>(i) * S;
-    for (int s = threadIdx.x; s < S; s += kElbThreads) {
-      const int e = lid[s];
-      if (e >= 0 && e < E) atomicAdd(&hist[e], 1);
-    }
-  }
-  __syncthreads();
-  for (int e = threadIdx.x; e < E; e += kElbThreads) {
-    const int v = crow[e] + hist[e];
-    row[e] = v;
-    if (hist[e] != 0) crow[e] = v;
-  }
-  __syncthreads();
-
-  if (M > 0) {
-    for (int e = threadIdx.x; e < E; e += kElbThreads) {
-      const int c = row[e];
-      int place = 0;
-      for (int f = 0; f < E; ++f) {
-        const int cf = row[f];
-        place += (cf > c || (cf == c && f < e)) ? 1 : 0;
-      }
-      if (place < M) {
-        plan_ids[static_cast<size_t>(l) * M + place] = e;
-        if (plan_counts != nullptr) plan_counts[static_cast<size_t>(l) * M + place] = c;
-      }
-    }
-  }
-  if (clear) {
-    for (int e = threadIdx.x; e < E; e += kElbThreads) crow[e] = 0;
-  }
+  const int32_t* lid =
+      (ids != nullptr && i >= 0 && i < n_layers) ? ids + static_cast<size_t>(i) * S : nullptr;
+  elb_block(cnt + static_cast<size_t>(l) * E, E, lid, S, M,
+            plan_ids + static_cast<size_t>(l) * M,
+            plan_counts != nullptr ? plan_counts + static_cast<size_t>(l) * M : nullptr, clear,
+            hist, row);
 }
 
 }  // namespace
@@ -74,12 +44,11 @@ __global__ __launch_bounds__(kElbThreads) void elb_kernel(
 
 using namespace smoe;
 
-extern "C" smoe_status smoe_elb_accumulate_topm(int32_t* elb_counts, int L, int E,
-                                                const int32_t* topk_ids, int layer_begin,
-                                                int n_layers, int T, int k, int M,
-                                                int32_t* plan_ids, int32_t* plan_counts,
-                                                int flags, void* stream) {
-  clear_error();
+namespace smoe {
+
+smoe_status elb_check(const int32_t* elb_counts, int L, int E, const int32_t* topk_ids,
+                      int layer_begin, int n_layers, int T, int k, int M, const int32_t* plan_ids,
+                      int flags) {
   SMOE_REQUIRE(L > 0 && E > 0 && M >= 0, SMOE_EINVAL,
                "elb_accumulate_topm: need L > 0, E > 0, M >= 0 (L=%d E=%d M=%d)", L, E, M);
   SMOE_REQUIRE(E <= kMaxE, SMOE_EUNSUPPORTED, "elb_accumulate_topm: E must be <= 256 (E=%d)", E);
@@ -88,7 +57,6 @@ extern "C" smoe_status smoe_elb_accumulate_topm(int32_t* elb_counts, int L, int 
                "elb_accumulate_topm: unknown flags %d", flags);
   SMOE_REQUIRE(elb_counts != nullptr, SMOE_EINVAL, "elb_accumulate_topm: null counter");
   SMOE_REQUIRE(M == 0 || plan_ids != nullptr, SMOE_EINVAL, "elb_accumulate_topm: null plan_ids");
-  int S = 0;
   if (topk_ids != nullptr) {
     SMOE_REQUIRE(T >= 0 && k > 0 && n_layers >= 0, SMOE_EINVAL,
                  "elb_accumulate_topm: need T >= 0, k > 0, n_layers >= 0");
@@ -98,8 +66,22 @@ extern "C" smoe_status smoe_elb_accumulate_topm(int32_t* elb_counts, int L, int 
                  layer_begin + n_layers, L);
     SMOE_REQUIRE(static_cast<long long>(T) * k < (1ll << 24), SMOE_EUNSUPPORTED,
                  "elb_accumulate_topm: T*k must be below 2^24");
-    S = T * k;
   }
+  return SMOE_OK;
+}
+
+}  // namespace smoe
+
+extern "C" smoe_status smoe_elb_accumulate_topm(int32_t* elb_counts, int L, int E,
+                                                const int32_t* topk_ids, int layer_begin,
+                                                int n_layers, int T, int k, int M,
+                                                int32_t* plan_ids, int32_t* plan_counts,
+                                                int flags, void* stream) {
+  clear_error();
+  const smoe_status st =
+      elb_check(elb_counts, L, E, topk_ids, layer_begin, n_layers, T, k, M, plan_ids, flags);
+  if (st != SMOE_OK) return st;
+  const int S = topk_ids != nullptr ? T * k : 0;
   hipLaunchKernelGGL(elb_kernel, dim3(L), dim3(kElbThreads), 0, as_stream(stream), elb_counts, E,
                      topk_ids, layer_begin, topk_ids ? n_layers : 0, S, M, plan_ids, plan_counts,
                      (flags & SMOE_ELB_CLEAR_AFTER) ? 1 : 0);

@@ -21,7 +21,7 @@
 // all E logits and the sigmoid of the shared-gate dot.
 #include <algorithm>
 
-#include "smoe_internal.hpp"
+#include "smoe_blocks.hpp"
 
 namespace smoe {
 namespace {
@@ -44,54 +44,72 @@ struct RouteArgs {
   int T, H, E, k, flags, tok_tile;
 };
 
-// Increasing map float -> uint32 with -0.0 and +0.0 sent to the same key.
-__device__ __forceinline__ uint32_t order_key(float f) {
-  if (f == 0.0f) f = 0.0f;
-  const uint32_t u = __float_as_uint(f);
-  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-}
+// Staged x of a token tile, transposed so that lane l finds its terms
+// h = 64c + l at consecutive c: xs[(t * 64 + l) * ncp + c], with the row
+// padded to ncp = round_up(H / 64, 4) + 4 floats (16-byte aligned rows,
+// conflict-free 16-byte reads across a quarter wave).
+__host__ __device__ inline int logits_ncp(int H) { return (H / kWave + 3) / 4 * 4 + 4; }
 
 __global__ __launch_bounds__(kLogitThreads) void logits_kernel(RouteArgs a) {
 #pragma clang fp contract(off)
-  extern __shared__ float xs[];             // [tok_tile][H]
+  extern __shared__ __align__(16) float xs[];
   const int H = a.H, E = a.E;
   const int t0 = blockIdx.y * a.tok_tile;
   const int tt = min(a.tok_tile, a.T - t0);
   const int wave = threadIdx.x / kWave;
   const int lane = threadIdx.x % kWave;
+  const int nc = H / kWave;
+  const int ncp = logits_ncp(H);
 
-  // x rows of the tile, 8 halves per load
+  const bool want_gate = a.gate_w != nullptr && a.gate != nullptr;
+  const int r = blockIdx.x * kRowsPerWg + wave;
+  const bool live = r < E + (want_gate ? 1 : 0);
+  // (a wave past the last row reads row 0 and writes nothing)
+  const float* wr = !live ? a.w : r < E ? a.w + static_cast<size_t>(r) * H : a.gate_w;
+  // the row's first slice is requested before x is staged: the two round
+  // trips overlap
+  float w[kSlice];
+#pragma unroll
+  for (int j = 0; j < kSlice; ++j) w[j] = wr[min(j, nc - 1) * kWave + lane];
+
+  // x rows of the tile, 8 halves per load, stored transposed
   const int n8 = tt * H / 8;
   const _Float16* xt = a.x + static_cast<size_t>(t0) * H;
   for (int i = threadIdx.x; i < n8; i += kLogitThreads) {
     typedef _Float16 h8 __attribute__((ext_vector_type(8)));
     const h8 v = *reinterpret_cast<const h8*>(xt + 8 * i);
+    const int t = i / (H / 8);
+    const int h = 8 * i - t * H;
+    const int c = h / kWave, l = h % kWave;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) xs[8 * i + j] = static_cast<float>(v[j]);
+    for (int j = 0; j < 8; ++j) xs[(t * kWave + l + j) * ncp + c] = static_cast<float>(v[j]);
   }
   __syncthreads();
+  if (!live) return;
 
-  const bool want_gate = a.gate_w != nullptr && a.gate != nullptr;
-  const int r = blockIdx.x * kRowsPerWg + wave;
-  if (r >= E + (want_gate ? 1 : 0)) return;
-  const float* wr = r < E ? a.w + static_cast<size_t>(r) * H : a.gate_w;
-  const int nc = H / kWave;
   float p[kMaxTokTile];
 #pragma unroll
   for (int t = 0; t < kMaxTokTile; ++t) p[t] = 0.0f;
   for (int c0 = 0; c0 < nc; c0 += kSlice) {
-    float w[kSlice];
+    if (c0 > 0) {
 #pragma unroll
-    for (int j = 0; j < kSlice; ++j) w[j] = wr[min(c0 + j, nc - 1) * kWave + lane];
+      for (int j = 0; j < kSlice; ++j) w[j] = wr[min(c0 + j, nc - 1) * kWave + lane];
+    }
 #pragma unroll
     for (int t = 0; t < kMaxTokTile; ++t) {
       if (t < tt) {
-        const float* xr = xs + t * H + lane;
+        const float* xr = xs + (t * kWave + lane) * ncp + c0;
 #pragma unroll
-        for (int j = 0; j < kSlice; ++j) {
-          if (c0 + j < nc) {
-            const float prod = xr[(c0 + j) * kWave] * w[j];
-            p[t] = p[t] + prod;
+        for (int j4 = 0; j4 < kSlice; j4 += 4) {
+          if (c0 + j4 >= nc) break;  // (reads stay within the padded row)
+          const float4 xv = *reinterpret_cast<const float4*>(xr + j4);
+          const float xa[4] = {xv.x, xv.y, xv.z, xv.w};
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            if (c0 + j4 + q < nc) {
+              const float prod = xa[q] * w[j4 + q];
+              p[t] = p[t] + prod;
+            }
           }
         }
       }
@@ -122,59 +140,92 @@ __global__ __launch_bounds__(kLogitThreads) void logits_kernel(RouteArgs a) {
 }
 
 __global__ __launch_bounds__(kTopkWaves * kWave) void topk_kernel(RouteArgs a) {
+  __shared__ uint64_t keys[kTopkWaves][kMaxE];
+  __shared__ int sel[kTopkWaves][kMaxK];
+  const int wave = threadIdx.x / kWave;
   const int lane = threadIdx.x % kWave;
-  const int t = blockIdx.x * kTopkWaves + threadIdx.x / kWave;
+  const int t = blockIdx.x * kTopkWaves + wave;
   if (t >= a.T) return;
-  const int E = a.E;
-  const float* l = a.logits + static_cast<size_t>(t) * E;
-
-  float lv[kMaxE / kWave];
-  uint64_t key[kMaxE / kWave];
-#pragma unroll
-  for (int i = 0; i < kMaxE / kWave; ++i) {
-    const int e = lane + i * kWave;
-    lv[i] = e < E ? l[e] : 0.0f;
-    key[i] = e < E ? (static_cast<uint64_t>(order_key(lv[i])) << 32) |
-                         static_cast<uint32_t>(0xFFFFFFFFu - static_cast<uint32_t>(e))
-                   : 0ull;
-  }
-  int my_sel = 0;
-  uint64_t first = 0ull;
-  for (int j = 0; j < a.k; ++j) {
-    uint64_t best = 0ull;
-#pragma unroll
-    for (int i = 0; i < kMaxE / kWave; ++i) best = key[i] > best ? key[i] : best;
-    best = wave_max_u64(best);
-    const int e = static_cast<int>(0xFFFFFFFFu - static_cast<uint32_t>(best & 0xFFFFFFFFull));
-    if (j == 0) first = best;
-    if (lane == j) my_sel = e;
-#pragma unroll
-    for (int i = 0; i < kMaxE / kWave; ++i)
-      if (lane + i * kWave == e) key[i] = 0ull;
-  }
-
-  // softmax over all E logits, evaluated at the selected experts
-  const int e_first =
-      static_cast<int>(0xFFFFFFFFu - static_cast<uint32_t>(first & 0xFFFFFFFFull));
-  const float mx = l[e_first];
-  float s = 0.0f;
-#pragma unroll
-  for (int i = 0; i < kMaxE / kWave; ++i) {
-    const int e = lane + i * kWave;
-    if (e < E) s += expf(lv[i] - mx);
-  }
-  s = wave_sum_f(s);
-  float wj = lane < a.k ? expf(l[my_sel] - mx) / s : 0.0f;
-  if (a.flags & SMOE_ROUTE_RENORM) {
-    const float tot = wave_sum_f(wj);
-    wj = wj / tot;
-  }
+  int id;
+  float w;
+  wave_topk(a.logits + static_cast<size_t>(t) * a.E, a.E, a.k, a.flags, keys[wave], sel[wave],
+            &id, &w);
   if (lane < a.k) {
-    a.ids[static_cast<size_t>(t) * a.k + lane] = my_sel;
-    a.wout[static_cast<size_t>(t) * a.k + lane] = wj;
+    a.ids[static_cast<size_t>(t) * a.k + lane] = id;
+    a.wout[static_cast<size_t>(t) * a.k + lane] = w;
   }
   if (a.gate != nullptr && a.gate_w != nullptr && lane == 0)
     a.gate[t] = 1.0f / (1.0f + expf(-a.gate[t]));
+}
+
+// Top-k, alignment and the ELB update of one layer in one workgroup, for
+// windows of at most kFusedMaxSlots slots: wave w takes the top-k of tokens
+// w, w + 16, ... (the IDs also go to LDS), then align_block sorts the
+// slots from LDS, then elb_block updates the layer's counter row and ranks
+// every layer. The results equal those of the three separate kernels.
+constexpr int kFusedMaxSlots = 512;
+constexpr int kFusedMaxLogits = 4096;  // logits staged in LDS up to this many
+
+struct FusedArgs {
+  RouteArgs r;
+  int32_t* counts;
+  int32_t* offsets;
+  int32_t* sorted_slots;
+  int32_t* active;
+  int32_t* n_active;
+  int32_t* elb_counts;  // [L][E] or null (no ELB update)
+  int32_t* plan_ids;
+  int32_t* plan_counts;
+  int L, layer, M, elb_clear;
+};
+
+__global__ __launch_bounds__(kAlignThreads) void topk_align_elb_kernel(FusedArgs f) {
+  __shared__ AlignSmem sm;
+  __shared__ int ids_lds[kFusedMaxSlots];
+  __shared__ int hist[kMaxE];
+  __shared__ int row[kMaxE];
+  __shared__ float lg_lds[kFusedMaxLogits];
+  const RouteArgs& a = f.r;
+  const int wave = threadIdx.x / kWave;
+  const int lane = threadIdx.x % kWave;
+  // the top-k's per-wave LDS words live in the alignment's scratch, which is
+  // not in use yet
+  static_assert(sizeof(sm.wave_cnt) + sizeof(sm.wave_base) >= kAlignWaves * kMaxE * 8,
+                "per-wave top-k keys fit the alignment scratch");
+  static_assert(sizeof(sm.exp_off) >= kAlignWaves * kMaxK * 4, "per-wave picks fit");
+  uint64_t* keys = reinterpret_cast<uint64_t*>(&sm.wave_cnt[0][0]) + wave * kMaxE;
+  int* sel = &sm.exp_off[0] + wave * kMaxK;
+  // all logits in one round trip when they fit, then the top-k from LDS
+  const int n_lg = a.T * a.E;
+  const bool lg_in_lds = n_lg <= kFusedMaxLogits;
+  if (lg_in_lds) {
+    for (int i = threadIdx.x; i < n_lg; i += kAlignThreads) lg_lds[i] = a.logits[i];
+    __syncthreads();
+  }
+  for (int t = wave; t < a.T; t += kAlignWaves) {
+    int id;
+    float w;
+    const float* lrow = (lg_in_lds ? lg_lds : a.logits) + static_cast<size_t>(t) * a.E;
+    wave_topk(lrow, a.E, a.k, a.flags, keys, sel, &id, &w);
+    if (lane < a.k) {
+      a.ids[static_cast<size_t>(t) * a.k + lane] = id;
+      a.wout[static_cast<size_t>(t) * a.k + lane] = w;
+      ids_lds[t * a.k + lane] = id;
+    }
+    if (a.gate != nullptr && a.gate_w != nullptr && lane == 0)
+      a.gate[t] = 1.0f / (1.0f + expf(-a.gate[t]));
+  }
+  __syncthreads();
+  const int S = a.T * a.k;
+  align_block(ids_lds, S, a.E, f.counts, f.offsets, f.sorted_slots, f.active, f.n_active, sm);
+  if (f.elb_counts == nullptr) return;
+  for (int l = 0; l < f.L; ++l) {
+    __syncthreads();
+    elb_block(f.elb_counts + static_cast<size_t>(l) * a.E, a.E, l == f.layer ? ids_lds : nullptr,
+              S, f.M, f.plan_ids + static_cast<size_t>(l) * f.M,
+              f.plan_counts != nullptr ? f.plan_counts + static_cast<size_t>(l) * f.M : nullptr,
+              f.elb_clear, hist, row);
+  }
 }
 
 }  // namespace
@@ -182,12 +233,13 @@ __global__ __launch_bounds__(kTopkWaves * kWave) void topk_kernel(RouteArgs a) {
 
 using namespace smoe;
 
-extern "C" smoe_status smoe_route_topk(const void* x, const float* w_router,
-                                       const float* logit_bias, int T, int H, int E, int k,
-                                       int flags, int32_t* topk_ids, float* topk_w,
-                                       float* logits, const float* shared_gate_w,
-                                       float* shared_gate, void* stream) {
-  clear_error();
+namespace smoe {
+namespace {
+
+smoe_status route_check(const void* x, const float* w_router, const float* logit_bias, int T,
+                        int H, int E, int k, int flags, int32_t* topk_ids, float* topk_w,
+                        float* logits, const float* shared_gate_w, float* shared_gate,
+                        RouteArgs& a) {
   SMOE_REQUIRE(T >= 0 && H > 0 && E > 0 && k > 0, SMOE_EINVAL,
                "route_topk: need T >= 0, H > 0, E > 0, k > 0 (T=%d H=%d E=%d k=%d)", T, H, E, k);
   SMOE_REQUIRE(E <= kMaxE && k <= kMaxK && k <= E, SMOE_EUNSUPPORTED,
@@ -197,14 +249,14 @@ extern "C" smoe_status smoe_route_topk(const void* x, const float* w_router,
   SMOE_REQUIRE((flags & ~SMOE_ROUTE_RENORM) == 0, SMOE_EINVAL, "route_topk: unknown flags %d", flags);
   SMOE_REQUIRE((shared_gate_w == nullptr) == (shared_gate == nullptr), SMOE_EINVAL,
                "route_topk: shared_gate_w and shared_gate must both be set or both NULL");
-  if (T == 0) return SMOE_OK;
-  SMOE_REQUIRE(x && w_router && topk_ids && topk_w && logits, SMOE_EINVAL,
-               "route_topk: null pointer (x, w_router, topk_ids, topk_w and logits are required)");
-  SMOE_REQUIRE(aligned16(x), SMOE_EINVAL, "route_topk: x must be 16-byte aligned");
-  SMOE_REQUIRE(static_cast<long long>(T) * k < (1ll << 24), SMOE_EUNSUPPORTED,
-               "route_topk: T*k must be below 2^24");
-
-  RouteArgs a;
+  if (T > 0) {
+    SMOE_REQUIRE(x && w_router && topk_ids && topk_w && logits, SMOE_EINVAL,
+                 "route_topk: null pointer (x, w_router, topk_ids, topk_w and logits are "
+                 "required)");
+    SMOE_REQUIRE(aligned16(x), SMOE_EINVAL, "route_topk: x must be 16-byte aligned");
+    SMOE_REQUIRE(static_cast<long long>(T) * k < (1ll << 24), SMOE_EUNSUPPORTED,
+                 "route_topk: T*k must be below 2^24");
+  }
   a.x = static_cast<const _Float16*>(x);
   a.w = w_router;
   a.bias = logit_bias;
@@ -218,16 +270,86 @@ extern "C" smoe_status smoe_route_topk(const void* x, const float* w_router,
   a.E = E;
   a.k = k;
   a.flags = flags;
-  // tokens per logits workgroup: up to four, x tile within 64 KB of LDS
-  a.tok_tile = std::max(1, std::min(kMaxTokTile, 65536 / (H * 4)));
-  const int nrows = E + (shared_gate_w != nullptr ? 1 : 0);
-  const dim3 grid((nrows + kRowsPerWg - 1) / kRowsPerWg, (T + a.tok_tile - 1) / a.tok_tile);
-  const size_t lds = static_cast<size_t>(a.tok_tile) * H * sizeof(float);
-  hipStream_t st = as_stream(stream);
+  // tokens per logits workgroup: up to four, staged x tile within 64 KB of LDS
+  a.tok_tile = std::max(1, std::min(kMaxTokTile, 65536 / (kWave * logits_ncp(H) * 4)));
+  return SMOE_OK;
+}
+
+smoe_status launch_logits(const RouteArgs& a, hipStream_t st) {
+  const int nrows = a.E + (a.gate_w != nullptr ? 1 : 0);
+  const dim3 grid((nrows + kRowsPerWg - 1) / kRowsPerWg, (a.T + a.tok_tile - 1) / a.tok_tile);
+  const size_t lds = static_cast<size_t>(a.tok_tile) * kWave * logits_ncp(a.H) * sizeof(float);
   hipLaunchKernelGGL(logits_kernel, grid, dim3(kLogitThreads), lds, st, a);
-  smoe_status s = check_launch("route_topk logits");
+  return check_launch("route_topk logits");
+}
+
+}  // namespace
+}  // namespace smoe
+
+extern "C" smoe_status smoe_route_topk(const void* x, const float* w_router,
+                                       const float* logit_bias, int T, int H, int E, int k,
+                                       int flags, int32_t* topk_ids, float* topk_w,
+                                       float* logits, const float* shared_gate_w,
+                                       float* shared_gate, void* stream) {
+  clear_error();
+  RouteArgs a;
+  smoe_status s = route_check(x, w_router, logit_bias, T, H, E, k, flags, topk_ids, topk_w,
+                              logits, shared_gate_w, shared_gate, a);
+  if (s != SMOE_OK || T == 0) return s;
+  hipStream_t st = as_stream(stream);
+  s = launch_logits(a, st);
   if (s != SMOE_OK) return s;
   hipLaunchKernelGGL(topk_kernel, dim3((T + kTopkWaves - 1) / kTopkWaves),
                      dim3(kTopkWaves * kWave), 0, st, a);
   return check_launch("route_topk");
+}
+
+extern "C" smoe_status smoe_route_align_elb(
+    const void* x, const float* w_router, const float* logit_bias, int T, int H, int E, int k,
+    int flags, int32_t* topk_ids, float* topk_w, float* logits, const float* shared_gate_w,
+    float* shared_gate, int32_t* expert_counts, int32_t* expert_offsets, int32_t* sorted_slots,
+    int32_t* active_experts, int32_t* n_active, int32_t* elb_counts, int L, int layer, int M,
+    int32_t* plan_ids, int32_t* plan_counts, int elb_flags, void* stream) {
+  clear_error();
+  RouteArgs a;
+  smoe_status s = route_check(x, w_router, logit_bias, T, H, E, k, flags, topk_ids, topk_w,
+                              logits, shared_gate_w, shared_gate, a);
+  if (s != SMOE_OK) return s;
+  s = align_check(topk_ids, T, k, E, expert_counts, expert_offsets, sorted_slots,
+                  active_experts, n_active);
+  if (s != SMOE_OK) return s;
+  if (elb_counts != nullptr) {
+    s = elb_check(elb_counts, L, E, topk_ids, layer, 1, T, k, M, plan_ids, elb_flags);
+    if (s != SMOE_OK) return s;
+  }
+  if (T == 0 || T * k > kFusedMaxSlots) {  // the three calls one after the other
+    s = smoe_route_topk(x, w_router, logit_bias, T, H, E, k, flags, topk_ids, topk_w, logits,
+                        shared_gate_w, shared_gate, stream);
+    if (s == SMOE_OK)
+      s = smoe_align_by_expert(topk_ids, T, k, E, expert_counts, expert_offsets, sorted_slots,
+                               active_experts, n_active, stream);
+    if (s == SMOE_OK && elb_counts != nullptr)
+      s = smoe_elb_accumulate_topm(elb_counts, L, E, topk_ids, layer, 1, T, k, M, plan_ids,
+                                   plan_counts, elb_flags, stream);
+    return s;
+  }
+  hipStream_t st = as_stream(stream);
+  s = launch_logits(a, st);
+  if (s != SMOE_OK) return s;
+  FusedArgs f;
+  f.r = a;
+  f.counts = expert_counts;
+  f.offsets = expert_offsets;
+  f.sorted_slots = sorted_slots;
+  f.active = active_experts;
+  f.n_active = n_active;
+  f.elb_counts = elb_counts;
+  f.plan_ids = plan_ids;
+  f.plan_counts = plan_counts;
+  f.L = L;
+  f.layer = layer;
+  f.M = elb_counts != nullptr ? M : 0;
+  f.elb_clear = (elb_flags & SMOE_ELB_CLEAR_AFTER) ? 1 : 0;
+  hipLaunchKernelGGL(topk_align_elb_kernel, dim3(1), dim3(kAlignThreads), 0, st, f);
+  return check_launch("route_align_elb");
 }

@@ -21,6 +21,15 @@ inline hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s);
 // Check the launch that was just enqueued.
 smoe_status check_launch(const char* what);
 
+// Argument checks of smoe_align_by_expert and smoe_elb_accumulate_topm
+// (SMOE_OK, or the status those calls return, with the error text set).
+smoe_status align_check(const int32_t* topk_ids, int T, int k, int E, const int32_t* expert_counts,
+                        const int32_t* expert_offsets, const int32_t* sorted_slots,
+                        const int32_t* active_experts, const int32_t* n_active);
+smoe_status elb_check(const int32_t* elb_counts, int L, int E, const int32_t* topk_ids,
+                      int layer_begin, int n_layers, int T, int k, int M, const int32_t* plan_ids,
+                      int flags);
+
 #define SMOE_REQUIRE(cond, code, ...)      \
   do {                                     \
     if (!(cond)) {                         \

@@ -120,6 +120,18 @@ class DeviceLayer:
                              self.topk_ids, self.topk_w, self.logits,
                              self.shared_gate_w, self.shared_gate, stream=stream)
 
+    def route_align_elb(self, elb: bool = True, layer: int = 0, stream=None) -> None:
+        """route, align and (with elb) the ELB update of `layer` in one call."""
+        M = self.cfg.elb_M if elb else 0
+        _lib.smoe_route_align_elb(self.x, self.w_router, self.router_bias, self.cfg.k, 0,
+                                  self.topk_ids, self.topk_w, self.logits,
+                                  self.shared_gate_w, self.shared_gate, self.counts,
+                                  self.offsets, self.sorted_slots, self.active, self.n_active,
+                                  elb_counts=self.elb_counts if elb else None, layer=layer, M=M,
+                                  plan_ids=self.plan_ids if M > 0 else None,
+                                  plan_counts=self.plan_counts if M > 0 else None,
+                                  stream=stream)
+
     def align(self, stream=None) -> None:
         _lib.smoe_align_by_expert(self.topk_ids, self.cfg.E, self.counts, self.offsets,
                                   self.sorted_slots, self.active, self.n_active, stream=stream)
@@ -165,15 +177,18 @@ class DeviceLayer:
 
     # ---------------------------------------------------------------- whole layer
     def run(self, target: bool = False, elb: bool = True, fuse_shared: bool = True,
-            side_stream=None) -> None:
+            fuse_routing: bool = True, side_stream=None) -> None:
         """Enqueue the whole layer on the current stream.
 
-        fuse_shared runs the shared experts inside the routed FFN call;
-        otherwise they get a call of their own. With side_stream, the work
-        off the layer's critical path runs there: the ELB update (it needs
-        only the routing) and a separate shared-expert call (it needs only
-        x). The side stream forks from the current stream and joins it again
-        before the layer ends (before the combine for the shared experts).
+        fuse_routing makes routing, alignment and the ELB update one call
+        (smoe_route_align_elb); otherwise they are three. fuse_shared runs
+        the shared experts inside the routed FFN call; otherwise they get a
+        call of their own. With side_stream, the work off the layer's
+        critical path runs there: the ELB update when routing is not fused
+        (it needs only the routing) and a separate shared-expert call (it
+        needs only x). The side stream forks from the current stream and
+        joins it again before the layer ends (before the combine for the
+        shared experts).
         """
         separate = not fuse_shared and self.shared_out is not None
         use_elb = elb and self.cfg.elb_M > 0 and not target
@@ -200,17 +215,22 @@ class DeviceLayer:
         if separate and side is not None:
             shared_done = torch.cuda.Event()
             shared_done.record(side)
-        self.route()
-        if use_elb:
-            if side is not None:
-                fork()
-                self.elb(stream=side)
-            else:
-                self.elb()
-        self.align()
+        side_elb = False
+        if fuse_routing:
+            self.route_align_elb(elb=use_elb)
+        else:
+            self.route()
+            if use_elb:
+                if side is not None:
+                    fork()
+                    self.elb(stream=side)
+                    side_elb = True
+                else:
+                    self.elb()
+            self.align()
         self.routed_ffn(target=target, with_shared=not separate)
         if shared_done is not None:
             main.wait_event(shared_done)
         self.combine()
-        if side is not None and (separate or use_elb):
+        if side is not None and (separate or side_elb):
             join()

@@ -91,6 +91,22 @@ def test_route_argument_checks(lib):
     assert f(N, N, N, 0, 2048, 64, 6, 0, N, N, N, N, N, N) == 0             # empty window
 
 
+def test_route_align_elb_argument_checks(lib):
+    f = lib.smoe_route_align_elb
+    f.argtypes = ([ctypes.c_void_p] * 3 + [ctypes.c_int] * 5 + [ctypes.c_void_p] * 11 +
+                  [ctypes.c_int] * 3 + [ctypes.c_void_p] * 2 + [ctypes.c_int, ctypes.c_void_p])
+    r = [16, 16, N]                      # x, w_router, bias
+    o = [16, 16, 16, N, N]               # ids, weights, logits, gate_w, gate
+    al = [16, 16, 16, 16, 16]            # counts, offsets, sorted, active, n_active
+    assert f(*r, 17, 2048, 300, 6, 0, *o, *al, N, 0, 0, 0, N, N, 0, N) == EUNSUPPORTED
+    assert f(*r, 17, 2048, 64, 6, 0, 16, 16, N, N, N, *al, N, 0, 0, 0, N, N, 0, N) == EINVAL
+    assert f(*r, 17, 2048, 64, 6, 0, *o, 16, N, 16, 16, 16, N, 0, 0, 0, N, N, 0, N) == EINVAL
+    assert b"align_by_expert" in lib.smoe_last_error()
+    assert f(*r, 17, 2048, 64, 6, 0, *o, *al, 16, 1, 1, 0, N, N, 0, N) == EINVAL  # layer >= L
+    assert b"elb_accumulate_topm" in lib.smoe_last_error()
+    assert f(*r, 17, 2048, 64, 6, 0, *o, *al, 16, 1, 0, 32, N, N, 0, N) == EINVAL  # plan_ids
+
+
 def test_align_argument_checks(lib):
     f = lib.smoe_align_by_expert
     f.argtypes = [ctypes.c_void_p] + [ctypes.c_int] * 3 + [ctypes.c_void_p] * 6

@@ -160,6 +160,82 @@ def test_route_single_token_and_large_E(smoe):
     assert np.array_equal(ids, oracle.topk_experts(ref_lg, 8))
 
 
+# ------------------------------------------------------------------ fused routing call
+
+def _routing_buffers(T, k, E, gated, L, M):
+    i32 = dict(dtype=torch.int32, device="cuda")
+    f32 = dict(dtype=torch.float32, device="cuda")
+    b = dict(ids=torch.full((T, k), -7, **i32), w=torch.full((T, k), -7.0, **f32),
+             lg=torch.full((T, E), -7.0, **f32),
+             gate=torch.full((T,), -7.0, **f32) if gated else None,
+             counts=torch.full((E,), -7, **i32), offsets=torch.full((E + 1,), -7, **i32),
+             sorted=torch.full((max(T * k, 1),), -7, **i32), active=torch.full((E,), -7, **i32),
+             n_active=torch.full((1,), -7, **i32))
+    if L:
+        b["cnt"] = torch.arange(L * E, **i32).reshape(L, E) % 5   # non-zero starting counts
+        b["plan"] = torch.full((L, max(M, 1)), -7, **i32)
+        b["plan_cnt"] = torch.full((L, max(M, 1)), -7, **i32)
+    return b
+
+
+def _run_routing(smoe, fused, x, w, bias, k, flags, gate_w, elb):
+    T, E = x.shape[0], w.shape[0]
+    L, layer, M, clear = elb if elb else (0, 0, 0, 0)
+    b = _routing_buffers(T, k, E, gate_w is not None, L, M)
+    S = T * k
+    xd, wd = dev(x), dev(w)
+    bd = None if bias is None else dev(bias)
+    gd = None if gate_w is None else dev(gate_w)
+    if fused:
+        smoe.smoe_route_align_elb(xd, wd, bd, k, flags, b["ids"], b["w"], b["lg"], gd, b["gate"],
+                                  b["counts"], b["offsets"], b["sorted"][:S], b["active"],
+                                  b["n_active"], elb_counts=b.get("cnt"), layer=layer, M=M,
+                                  plan_ids=b["plan"] if L and M else None,
+                                  plan_counts=b["plan_cnt"] if L and M else None,
+                                  elb_flags=clear)
+    else:
+        smoe.smoe_route_topk(xd, wd, bd, k, flags, b["ids"], b["w"], b["lg"], gd, b["gate"])
+        smoe.smoe_align_by_expert(b["ids"], E, b["counts"], b["offsets"], b["sorted"][:S],
+                                  b["active"], b["n_active"])
+        if L:
+            smoe.smoe_elb_accumulate_topm(b["cnt"], b["ids"][None], layer, M,
+                                          b["plan"] if M else None, b["plan_cnt"] if M else None,
+                                          clear)
+    return {k_: host(v) for k_, v in b.items() if v is not None}
+
+
+@pytest.mark.parametrize("name,elb", [("tiny", None), ("dsv2", (1, 0, 32, 0)),
+                                      ("qwen", (3, 1, 8, 1)), ("phi", (2, 1, 4, 0)),
+                                      ("batch", (26, 3, 32, 0))])
+def test_route_align_elb_equals_separate_calls(smoe, name, elb):
+    # one call == route_topk, align_by_expert, elb_accumulate_topm one after
+    # the other, bit for bit (the batch window takes the three-call path)
+    L = layer(name, layer_idx=3 if name == "batch" else 0)
+    cfg = L.cfg
+    args = (L.x, L.w_router, L.router_bias, cfg.k, 0, L.shared_gate_w, elb)
+    got = _run_routing(smoe, True, *args)
+    ref = _run_routing(smoe, False, *args)
+    assert got.keys() == ref.keys()
+    for key in ref:
+        assert np.array_equal(got[key].view(np.uint32) if got[key].dtype == np.float32 else got[key],
+                              ref[key].view(np.uint32) if ref[key].dtype == np.float32 else ref[key]), key
+    assert np.array_equal(got["ids"], oracle.topk_experts(
+        oracle.router_logits_f32(L.x, L.w_router, L.router_bias), cfg.k))
+
+
+def test_route_align_elb_ties_and_renorm(smoe):
+    rng = np.random.default_rng(11)
+    x = rng.standard_normal((33, 256)).astype(np.float16)
+    w = (rng.standard_normal((8, 256)) * 0.02).astype(np.float32)
+    w[5] = w[2]
+    for k, flags in ((1, 0), (3, 1), (8, 0)):
+        args = (x, w, None, k, flags, None, (2, 0, 4, 1))
+        got = _run_routing(smoe, True, *args)
+        ref = _run_routing(smoe, False, *args)
+        for key in ref:
+            assert np.array_equal(got[key], ref[key]), (k, key)
+
+
 # ------------------------------------------------------------------ alignment
 
 @pytest.mark.parametrize("E,k,T,seed", [(8, 2, 17, 0), (64, 6, 17, 1), (60, 4, 9, 2),
@@ -476,13 +552,15 @@ def test_combine_matches_oracle(smoe):
 # ------------------------------------------------------------------ whole layer
 
 @pytest.mark.parametrize("name", ["tiny", "dsv2", "qwen"])
-@pytest.mark.parametrize("mode", ["fused", "fused-side", "separate", "separate-side"])
+@pytest.mark.parametrize("mode", ["fused", "fused-side", "separate", "separate-side",
+                                  "three-routing-calls"])
 def test_layer_draft_matches_oracle(smoe, name, mode):
     from quantized_speculative_expert_amd.layer import DeviceLayer
     L = layer(name)
     ref = oracle.moe_layer(L, "draft")
     d = DeviceLayer(L)
-    d.run(fuse_shared=mode.startswith("fused"),
+    d.run(fuse_shared=not mode.startswith("separate"),
+          fuse_routing=mode != "three-routing-calls",
           side_stream=torch.cuda.Stream() if mode.endswith("side") else None)
     assert np.array_equal(host(d.topk_ids), ref["ids"])
     assert np.array_equal(host(d.sorted_slots), ref["sorted_slots"])
