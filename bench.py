@@ -8,10 +8,11 @@ experts, and the activation counter (ELB) with a top-32 plan.
 
 One step = one pass of the whole hot path over one window, every stage in the
 HIP library: FP16 shared experts, router top-k, alignment by expert, ELB
-accumulate + top-M, fused W4A16 routed-expert FFN, weighted combine. A step is
-captured as one HIP graph per weight copy; the copies are rotated (more than
-1 GiB in total, above the 256 MB last-level cache) so every step streams its
-weights from HBM. Inputs are resident in HBM before the timed region starts.
+accumulate + top-M, fused W4A16 routed-expert FFN, weighted combine. The
+steps are captured in one HIP graph that runs one step on each of several
+weight copies (more than 1 GiB in total, above the 256 MB last-level cache),
+so every step streams its weights from HBM, as the layers of a model's
+decode step would. Inputs are resident in HBM before the timed region starts.
 
 Printed: one JSON line with tokens/s (whole job), ms per step, the layer's
 achieved HBM bandwidth, a roofline entry for the dominant call (the fused
@@ -230,23 +231,24 @@ def main() -> int:
     def step(d):
         d.run(elb=use_elb, fuse_shared=fused, side_stream=side)
 
-    # eager run once (checks every call), then capture one graph per copy
+    # eager run once (checks every call), then capture the graphs
     for d in layers:
         step(d)
     torch.cuda.synchronize()
     cap = torch.cuda.Stream(device=dev)
     cap.wait_stream(torch.cuda.current_stream())
-    step_graphs = []
+    # one graph holds one layer step on each weight copy, as a model's decode
+    # step would be captured; every step still runs every call
+    steps_per_graph = copies
+    step_graph = torch.cuda.CUDAGraph()
     # the FFN alone: FFN_CALLS_PER_GRAPH back-to-back calls cycling over the
     # weight copies in one graph, so the per-call time is that of the two
     # launches and the gap between them, not of a graph launch
     ffn_graph = torch.cuda.CUDAGraph()
     with torch.cuda.stream(cap):
-        for d in layers:
-            g = torch.cuda.CUDAGraph()
-            with torch.cuda.graph(g, stream=cap):
+        with torch.cuda.graph(step_graph, stream=cap):
+            for d in layers:
                 step(d)
-            step_graphs.append(g)
         with torch.cuda.graph(ffn_graph, stream=cap):
             for i in range(FFN_CALLS_PER_GRAPH):
                 layers[i % copies].routed_ffn(with_shared=fused)
@@ -255,24 +257,26 @@ def main() -> int:
 
     stream = torch.cuda.current_stream()
     log(f"warmup {args.warmup} steps")
-    for i in range(args.warmup):
-        step_graphs[i % copies].replay()
+    for i in range(-(-args.warmup // steps_per_graph)):
+        step_graph.replay()
     torch.cuda.synchronize()
 
-    # ---- timed region: exactly `steps` layer steps
-    K = args.steps
-    evs = [torch.cuda.Event(enable_timing=True) for _ in range(K + 1)]
+    # ---- timed region: exactly `steps` layer steps (rounded up to whole
+    # graphs)
+    R = -(-args.steps // steps_per_graph)
+    K = R * steps_per_graph
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(R + 1)]
     log(f"timing {K} steps")
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     evs[0].record(stream)
-    for i in range(K):
-        step_graphs[i % copies].replay()
+    for i in range(R):
+        step_graph.replay()
         evs[i + 1].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    step_us = [1e3 * evs[i].elapsed_time(evs[i + 1]) for i in range(K)]
-    gpu_total_ms = evs[0].elapsed_time(evs[K])
+    step_us = [1e3 * evs[i].elapsed_time(evs[i + 1]) / steps_per_graph for i in range(R)]
+    gpu_total_ms = evs[0].elapsed_time(evs[R])
 
     n_active = int(base.n_active.item())
     lb = layer_bytes(base, n_active)
@@ -323,7 +327,7 @@ def main() -> int:
         "dtype": "f16",
         "data": "synthetic",
         "config": {
-            "workload": (f"{cfg.name}: {cfg.description}; seed 0; one graph per step, "
+            "workload": (f"{cfg.name}: {cfg.description}; seed 0; {steps_per_graph} steps per graph, "
                          f"{copies} rotated weight copies"),
             "T": cfg.T, "E": cfg.E, "k": cfg.k, "H": cfg.H, "I": cfg.I, "G": cfg.G,
             "shared_I": cfg.shared_I, "elb_M": cfg.elb_M, "weights": "int4 g%d + fp16 scales" % cfg.G,

@@ -26,7 +26,8 @@
 //   (one chunk per expert when every token picks an expert at most once). A
 //   row tile is 128 rows of gate and up (stage 1) or 256 rows of down
 //   (stage 2): 16 / 32 rows per wave of an 8-wave workgroup. The reduction
-//   dim K is cut into parts of D blocks. An item is (chunk, row tile, part);
+//   dim K is cut into parts of D blocks (4 in stage 1, 3 in stage 2, whose
+//   work is smaller and so is cut finer). An item is (chunk, row tile, part);
 //   the routed experts' items come first, the shared expert's after them.
 //   The list is built on the device from expert_offsets (nothing is read
 //   back). Each workgroup of the persistent grid first takes a run of
@@ -115,8 +116,11 @@ constexpr int kMaxSlotsLds = 1024;         // sorted slots kept whole in LDS up 
 constexpr int kLdsPerCu = 160 * 1024;      // gfx950
 constexpr int kLdsBudget = kLdsPerCu / 2;  // per workgroup: two workgroups per CU
 constexpr int kRowPad = 16;                // bytes of padding per staged row
-constexpr int kD = 4;                      // blocks per item (8 KB per wave)
-constexpr int kPhaseK = kD * 128;          // staged phases are whole INT4 items
+constexpr int kD1 = 4;                     // blocks per item, stage 1 (8 KB per wave)
+constexpr int kD2 = 3;                     // blocks per item, stage 2 (finer: fewer items per WG)
+constexpr int stage_d(int stage) { return stage == 1 ? kD1 : kD2; }
+// staged phases are whole INT4 items of the stage
+constexpr int phase_k(int stage) { return stage_d(stage) * 128; }
 #ifndef SMOE_FFN_MAX_WG
 #define SMOE_FFN_MAX_WG 512
 #endif
@@ -154,7 +158,7 @@ struct FfnArgs {
   int E, k, S, T, H;
   int chunks_upper;             // routed chunks the work list can hold
   int n_groups;                 // 1, or 2 with a shared expert
-  int kph;                      // k per staged phase (a multiple of kPhaseK)
+  int kph;                      // k per staged phase (a multiple of the stage's INT4 item)
   int stride;                   // LDS bytes per staged row
   int slots_lds;                // all S sorted slots copied to LDS at start
   int xs_off;                   // LDS byte offset of the staged rows
@@ -214,7 +218,7 @@ struct Item {
 template <int WK, int G, int STAGE, int NC>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) void ffn_kernel(
     FfnArgs a) {
-  constexpr int D = kD;
+  constexpr int D = stage_d(STAGE);
   constexpr int NQ = WK == kInt4 ? 128 / G : 1;  // INT4 group scales per block
   extern __shared__ __align__(16) uint8_t smem[];
   int* s_off = reinterpret_cast<int*>(smem);
@@ -436,7 +440,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
   // INT4 group scales of an item, one load per matrix: lane group g holds
   // the scales of block blk0 + g of its row (NS words); block d reads them
   // from lane (d, row) with a cross-lane shuffle.
-  static_assert(D == 4, "one INT4 scale block per lane group");
+  static_assert(D <= 4, "one INT4 scale block per lane group");
   constexpr int NS = NQ == 4 ? 2 : 1;
   uint32_t sring[2][NS], scur[2][NS];
   auto load_scales = [&](int blk0) {
@@ -827,7 +831,8 @@ struct GroupWeights {
 };
 
 // Row geometry of a [E][N][K] weight tensor in the group's format.
-void set_matrix(Group& g, const GroupWeights& w, int N, int K, const void* wq, const void* ws) {
+void set_matrix(Group& g, const GroupWeights& w, int N, int K, const void* wq, const void* ws,
+                int D) {
   g.fmt = w.fmt;
   g.N = N;
   g.K = K;
@@ -838,7 +843,7 @@ void set_matrix(Group& g, const GroupWeights& w, int N, int K, const void* wq, c
   g.s_estride = static_cast<long long>(g.s_rstride) * N;
   g.w0 = static_cast<const uint8_t*>(wq);
   g.s0 = static_cast<const uint16_t*>(ws);
-  g.parts = (g.nblk + kD - 1) / kD;
+  g.parts = (g.nblk + D - 1) / D;
   g.csz = w.csz;
   g.rows = w.rows;
   g.out = w.out;
@@ -855,14 +860,14 @@ struct StagePlans {
 // LDS layout of a stage: the table, the sorted slots, then rows_lds staged
 // rows of the phase length (a multiple of whole INT4 items, balanced over
 // the phases that the longest K needs).
-int plan_lds(FfnArgs& a, int kmax) {
+int plan_lds(FfnArgs& a, int kmax, int kunit) {
   a.slots_lds = a.S <= kMaxSlotsLds ? 1 : 0;
   a.xs_off = kTabBytes + ((a.slots_lds ? a.S : kMaxChunk) * 4 + 15) / 16 * 16;
   const int per_row = (kLdsBudget - a.xs_off) / a.rows_lds;
-  const int kph_cap = std::max(kPhaseK, (per_row - kRowPad) / 2 / kPhaseK * kPhaseK);
+  const int kph_cap = std::max(kunit, (per_row - kRowPad) / 2 / kunit * kunit);
   const int phases = (kmax + kph_cap - 1) / kph_cap;
   const int per_phase = (kmax + phases - 1) / phases;
-  a.kph = (per_phase + kPhaseK - 1) / kPhaseK * kPhaseK;
+  a.kph = (per_phase + kunit - 1) / kunit * kunit;
   a.stride = std::min(a.kph, kmax) * 2 + kRowPad;
   return a.xs_off + a.rows_lds * a.stride;
 }
@@ -892,20 +897,20 @@ void make_plans(StagePlans& p, const void* x, int T, int k, int H, const int32_t
   for (int i = 0; i < n_groups; ++i) {
     const GroupWeights& w = gw[i];
     const long long chunks = i == 0 ? a1.chunks_upper : (T + w.csz - 1) / w.csz;
-    set_matrix(a1.grp[i], w, w.I, H, w.wg, w.sg);
+    set_matrix(a1.grp[i], w, w.I, H, w.wg, w.sg, stage_d(1));
     a1.grp[i].w1 = static_cast<const uint8_t*>(w.wu);
     a1.grp[i].s1 = static_cast<const uint16_t*>(w.su);
     a1.grp[i].tiles = tiles_of(w.I, 16);
     p.items1 += chunks * a1.grp[i].tiles * a1.grp[i].parts;
-    set_matrix(a2.grp[i], w, H, w.I, w.wd, w.sd);
+    set_matrix(a2.grp[i], w, H, w.I, w.wd, w.sd, stage_d(2));
     a2.grp[i].w1 = nullptr;
     a2.grp[i].s1 = nullptr;
     a2.grp[i].tiles = tiles_of(H, 32);
     p.items2 += chunks * a2.grp[i].tiles * a2.grp[i].parts;
     kmax2 = std::max(kmax2, w.I);
   }
-  p.lds1 = plan_lds(a1, H);
-  p.lds2 = plan_lds(a2, kmax2);
+  p.lds1 = plan_lds(a1, H, phase_k(1));
+  p.lds2 = plan_lds(a2, kmax2, phase_k(2));
 }
 
 template <int WK, int G, int STAGE, int NC>
