@@ -574,6 +574,52 @@ def test_layer_draft_matches_oracle(smoe, name, mode):
         assert np.array_equal(host(d.plan_ids), pid) and np.array_equal(host(d.plan_counts), pc)
 
 
+def test_batch_layer_full_size_sampled(smoe):
+    # the batched window (544 tokens, Zipf-skewed router, 32-slot chunks) at
+    # full size through the whole layer; the oracle checks every slot of
+    # three experts and the outputs of two tokens, computed one by one
+    from quantized_speculative_expert_amd.layer import DeviceLayer
+    L = layer("batch", layer_idx=3)
+    cfg = L.cfg
+    d = DeviceLayer(L, elb_layers=cfg.layers)
+    d.run()
+    lg = oracle.router_logits_f32(L.x, L.w_router, L.router_bias)
+    ids = oracle.topk_experts(lg, cfg.k)
+    assert np.array_equal(host(d.topk_ids), ids)
+    al = oracle.align_by_expert(ids, cfg.E)
+    assert np.array_equal(host(d.sorted_slots), al["sorted_slots"])
+    slot_out = host(d.slot_out)
+    flat = ids.ravel()
+
+    def expert(e):
+        return (oracle.dequant_int4(L.wg_q[e], L.wg_s[e], cfg.G),
+                oracle.dequant_int4(L.wu_q[e], L.wu_s[e], cfg.G),
+                oracle.dequant_int4(L.wd_q[e], L.wd_s[e], cfg.G))
+    counts = np.bincount(flat, minlength=cfg.E)
+    busiest = int(np.argmax(counts))                  # more than one 32-slot chunk
+    for e in sorted({busiest, int(np.argmin(np.where(counts > 0, counts, 1 << 30))), 7}):
+        sl = np.flatnonzero(flat == e)
+        if len(sl) == 0:
+            continue
+        ref = oracle.swiglu(L.x[sl // cfg.k].astype(np.float64), *expert(e))
+        assert row_rel_err(slot_out[sl], ref) <= ROW_TOL, e
+    assert counts[busiest] > 32
+    w = oracle.routing_weights(lg, ids)
+    y = host(d.y)
+    for t in (0, 543):
+        so = np.stack([oracle.swiglu(L.x[t:t + 1].astype(np.float64), *expert(int(e)))[0]
+                       for e in ids[t]])
+        sh = oracle.shared_ffn(L.x[t:t + 1], L.sg16, L.su16, L.sd16)
+        ref = (w[t][:, None] * so).sum(0) + sh[0]
+        assert row_rel_err(y[t:t + 1], ref[None]) <= ROW_TOL, t
+    # the layer's row of the 26-layer activation counter and its top-32 plan
+    cnt = np.zeros((cfg.layers, cfg.E), np.int32)
+    cnt[0] = np.bincount(flat, minlength=cfg.E)
+    pid, pc = oracle.elb_topm(cnt, cfg.elb_M)
+    assert np.array_equal(host(d.elb_counts), cnt)
+    assert np.array_equal(host(d.plan_ids), pid) and np.array_equal(host(d.plan_counts), pc)
+
+
 @pytest.mark.parametrize("fused", [True, False])
 def test_layer_graph_replay_matches_eager(smoe, fused):
     from quantized_speculative_expert_amd.layer import DeviceLayer
