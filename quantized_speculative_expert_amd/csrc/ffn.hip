@@ -28,7 +28,9 @@
 //   (stage 2): 16 / 32 rows per wave of an 8-wave workgroup. The reduction
 //   dim K is cut into parts of D blocks (4 in stage 1, 3 in stage 2, whose
 //   work is smaller and so is cut finer). An item is (chunk, row tile, part);
-//   the routed experts' items come first, the shared expert's after them.
+//   the shared expert's items come first, the routed experts' after them,
+//   so the static runs below hold the shared tiles (every token: the
+//   widest items) and the dynamic tail is made of routed items.
 //   The list is built on the device from expert_offsets (nothing is read
 //   back). Each workgroup of the persistent grid first takes a run of
 //   consecutive items (nine tenths of an even share); the rest goes out
@@ -292,7 +294,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
   const int n_s = a.n_groups > 1
                       ? (a.T + a.grp[1].csz - 1) / a.grp[1].csz * a.grp[1].tiles * a.grp[1].parts
                       : 0;
-  const int n_items = n_r + n_s;
+  const int n_items = n_s + n_r;
   // Work split. Every workgroup first takes q0 consecutive items (nine
   // tenths of an even share, rounded down; none when that is under two).
   // The rest is cut into units of two consecutive items dealt out in
@@ -358,11 +360,12 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
 
   auto decode = [&](int item) {
     Item it;
-    if (item < n_r) {
+    if (item >= n_s) {
       const int P = a.grp[0].parts, tiles = a.grp[0].tiles;
-      const int ct = item / P;
+      const int ri = item - n_s;
+      const int ct = ri / P;
       it.grp = 0;
-      it.part = item - ct * P;
+      it.part = ri - ct * P;
       it.chunk = ct / tiles;
       it.tile = ct - it.chunk * tiles;
       // s_cp is non-decreasing, so the chunk's expert is the number of
@@ -376,10 +379,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
       it.m = min(csz0, s_off[it.e + 1] - it.seg0);
     } else {
       const int P = a.grp[1].parts, tiles = a.grp[1].tiles, csz = a.grp[1].csz;
-      const int i = item - n_r;
-      const int ct = i / P;
+      const int ct = item / P;
       it.grp = 1;
-      it.part = i - ct * P;
+      it.part = item - ct * P;
       it.chunk = ct / tiles;
       it.tile = ct - it.chunk * tiles;
       it.e = 0;
