@@ -36,6 +36,7 @@ if ROOT not in sys.path:
 
 METRIC = "W4A16 MoE-layer tokens/sec + achieved HBM GB/s fraction, K=16 window"
 PEAK_HBM_GBPS = 8000.0          # MI355X HBM3E, vendor figure
+PEAK_F16_TFLOPS = 2500.0        # MI355X dense fp16 MFMA, vendor figure
 MIN_ROTATION_BYTES = 1 << 30    # rotate weight copies over at least this many bytes
 FFN_CALLS_PER_GRAPH = 8         # expert-FFN calls per timing graph
 PROFILES = os.path.join(ROOT, "profiles")
@@ -64,6 +65,11 @@ def parse_args():
     p.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                    help="only run a plain device copy of MIB MiB `steps` times (reads MIB, "
                         "writes MIB): the reference that scales the HBM traffic counters")
+    p.add_argument("--eager-steps", type=int, default=400,
+                   help="layer steps also timed eagerly, one library call after another (0 = skip)")
+    p.add_argument("--compare", action="store_true",
+                   help="also time the same routed-expert work as one W4A16 call per active "
+                        "expert and as one batched call over FP16 weights")
     p.add_argument("--cpu-reps", type=int, default=10,
                    help="full layers the CPU reference runs for cpu_baseline (0 = skip)")
     return p.parse_args()
@@ -106,6 +112,16 @@ def ffn_bytes(d, n_active: int, with_shared: bool) -> int:
     if with_shared and d.shared_out is not None:
         b += sum(_nbytes(t) for t in (d.sg16, d.su16, d.sd16)) + c.T * c.H * 4
     return b
+
+
+def ffn_flops(d, with_shared: bool) -> int:
+    """Useful MFMA flops of one expert-FFN call: gate, up and down for every
+    routed slot, and for every token through the shared experts."""
+    c = d.cfg
+    f = 2 * 3 * c.H * c.I * c.S
+    if with_shared and d.shared_out is not None:
+        f += 2 * 3 * c.H * d.shared_I * c.T
+    return f
 
 
 # ----------------------------------------------------------------------------- traffic
@@ -182,6 +198,73 @@ def copy_calibration(mib: int, calls: int) -> int:
     return 0
 
 
+def compare_ffn(base, layers, fused: bool, stream, batched_us: float) -> dict:
+    """The routed experts' work of one window done three ways, each cycling
+    over the weight copies inside one HIP graph: the batched W4A16 call (all
+    active experts in two launches), one W4A16 call per active expert (E = 1
+    on that expert's slots, plus one call for the shared experts), and the
+    batched call over FP16 weights of the same shapes (the target format)."""
+    import torch
+    from quantized_speculative_expert_amd import _lib
+
+    c = base.cfg
+    off = base.offsets.cpu().tolist()
+    act = [e for e in range(c.E) if off[e + 1] > off[e]]
+    offs = [torch.tensor([off[e], off[e + 1]], dtype=torch.int32, device=base.device)
+            for e in act]
+    ws = torch.zeros(_lib.smoe_ffn_workspace_bytes(c.T, c.k, 1, c.H, c.I),
+                     dtype=torch.uint8, device=base.device)
+
+    def per_expert(d):
+        for e, o in zip(act, offs):
+            sl = slice(e, e + 1)
+            _lib.smoe_w4a16_expert_ffn(d.x, c.k, 1, c.I, c.G, d.wg_q[sl], d.wg_s[sl],
+                                       d.wu_q[sl], d.wu_s[sl], d.wd_q[sl], d.wd_s[sl],
+                                       d.sorted_slots, o, ws, d.slot_out)
+        if fused:
+            d.shared_ffn()
+
+    def fp16(d):
+        d.routed_ffn(target=True, with_shared=fused)
+
+    def time_graph(body, reps: int = 50) -> float:
+        cap = torch.cuda.Stream(device=base.device)
+        cap.wait_stream(torch.cuda.current_stream())
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.stream(cap):
+            for d in layers:
+                body(d)  # eager once: every call checked before capture
+            torch.cuda.synchronize()
+            with torch.cuda.graph(g, stream=cap):
+                for d in layers:
+                    body(d)
+        torch.cuda.current_stream().wait_stream(cap)
+        torch.cuda.synchronize()
+        g.replay()
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
+        torch.cuda.synchronize()
+        ev[0].record(stream)
+        for i in range(reps):
+            g.replay()
+            ev[i + 1].record(stream)
+        torch.cuda.synchronize()
+        return percentiles([1e3 * ev[i].elapsed_time(ev[i + 1]) / len(layers)
+                            for i in range(reps)])["median"]
+
+    log(f"compare: one W4A16 call per active expert ({len(act)})")
+    seq_us = time_graph(per_expert)
+    log("compare: batched FP16 call")
+    f16_us = time_graph(fp16)
+    return {"batched_w4a16_us": round(batched_us, 2),
+            "per_expert_w4a16_us": round(seq_us, 2),
+            "batched_fp16_us": round(f16_us, 2),
+            "active_experts": len(act),
+            "shared_experts": "included" if fused else "excluded",
+            "note": ("per graph replay over the rotated weight copies; per-expert = "
+                     f"{len(act)} W4A16 calls of E = 1 (2 launches each) + the shared call; "
+                     "FP16 = the batched call over FP16 routed weights (4x the bytes)")}
+
+
 def percentiles(xs):
     import numpy as np
     a = np.asarray(xs, dtype=float)
@@ -209,17 +292,17 @@ def main() -> int:
     from workload import get_config, make_layer
 
     cfg = get_config(args.config)
-    if cfg.layers != 1:
-        print(f"config {cfg.name} is a {cfg.layers}-layer stack; bench.py times single layers",
-              file=sys.stderr)
-        return 2
+    # a stack of several layers is timed on its layer 0, with the ELB
+    # counters of every layer (each step ranks all of them)
     log(f"generating {cfg.name} inputs (seed 0)")
-    inp = make_layer(cfg, seed=0, want_fp16=False)
+    inp = make_layer(cfg, seed=0, layer=0, want_fp16=args.compare)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    base = DeviceLayer(inp, device=dev, with_target=False)
+    base = DeviceLayer(inp, device=dev, with_target=args.compare, elb_layers=cfg.layers)
     del inp
-    wbytes = base.weight_bytes()
+    # rotation sized on the draft path's weights (the FP16 routed copies that
+    # --compare adds are read only by the comparison)
+    wbytes = base.weight_bytes() - sum(_nbytes(t) for t in (base.wg16, base.wu16, base.wd16))
     copies = args.copies or max(2, -(-MIN_ROTATION_BYTES // wbytes))
     layers = [base] + [base.with_weight_copy() for _ in range(copies - 1)]
     log(f"{copies} weight copies x {wbytes / 2**20:.1f} MiB resident")
@@ -308,6 +391,29 @@ def main() -> int:
                            + (" + shared experts)" if fused else " experts)")),
                 "bytes_per_launch": fb, "us_per_launch": round(ffn_stats["mean"], 2)}
 
+    flops = ffn_flops(base, fused)
+    mfma = {"flops_per_call": flops,
+            "achieved_tflops": round(flops / (ffn_stats["mean"] * 1e6), 2),
+            "peak_tflops": PEAK_F16_TFLOPS,
+            "frac": round(flops / (ffn_stats["mean"] * 1e6) / PEAK_F16_TFLOPS, 4)}
+
+    # ---- the same layer step enqueued eagerly, call after call
+    eager = None
+    if args.eager_steps > 0:
+        n = args.eager_steps
+        log(f"timing {n} eager steps")
+        ee = [torch.cuda.Event(enable_timing=True) for _ in range(n + 1)]
+        torch.cuda.synchronize()
+        ee[0].record(stream)
+        for i in range(n):
+            step(layers[i % copies])
+            ee[i + 1].record(stream)
+        torch.cuda.synchronize()
+        eager = {k_: round(v, 2) for k_, v in
+                 percentiles([1e3 * ee[i].elapsed_time(ee[i + 1]) for i in range(n)]).items()}
+
+    compare = compare_ffn(base, layers, fused, stream, ffn_stats["mean"]) if args.compare else None
+
     cpu = None
     if args.cpu_reps > 0:
         log(f"CPU reference on {args.cpu_reps} layers")
@@ -327,8 +433,9 @@ def main() -> int:
         "dtype": "f16",
         "data": "synthetic",
         "config": {
-            "workload": (f"{cfg.name}: {cfg.description}; seed 0; {steps_per_graph} steps per graph, "
-                         f"{copies} rotated weight copies"),
+            "workload": (f"{cfg.name}: {cfg.description}; seed 0; "
+                         + (f"layer 0 of the {cfg.layers}-layer stack; " if cfg.layers > 1 else "")
+                         + f"{steps_per_graph} steps per graph, {copies} rotated weight copies"),
             "T": cfg.T, "E": cfg.E, "k": cfg.k, "H": cfg.H, "I": cfg.I, "G": cfg.G,
             "shared_I": cfg.shared_I, "elb_M": cfg.elb_M, "weights": "int4 g%d + fp16 scales" % cfg.G,
             "shared_experts": args.shared,
@@ -338,12 +445,16 @@ def main() -> int:
         "hbm_frac": round(layer_gbps / PEAK_HBM_GBPS, 4),
         "layer_us": {k_: round(v, 2) for k_, v in percentiles(step_us).items()},
         "layer_us_gpu_mean": round(1e3 * gpu_total_ms / K, 2),
+        "layer_eager_us": eager,
         "ffn_us": {k_: round(v, 2) for k_, v in ffn_stats.items()},
+        "mfma": mfma,
         "n_active": n_active,
         "layer_bytes": lb,
         "roofline": roofline,
         "cpu_baseline": cpu,
     }
+    if compare is not None:
+        out["compare"] = compare
     print(json.dumps(out), flush=True)
     return 0
 

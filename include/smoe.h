@@ -22,8 +22,10 @@
  *     SMOE_EUNSUPPORTED (outside the kernels' limits) and touches no memory.
  *     A failed launch returns SMOE_EHIP. smoe_last_error() gives the reason
  *     (thread-local text).
- *   - Limits: 1 <= E <= 256; 1 <= k <= min(8, E); H and I multiples of 128;
- *     group size G in {32, 64, 128}; T*k < 2^24; M <= E.
+ *   - Limits: 1 <= E <= 256; 1 <= k <= min(8, E) (the expert FFN calls
+ *     also take k > E: a call may cover a subset of the experts, e.g. one
+ *     expert or one device's share, with the window's k); H and I multiples
+ *     of 128; group size G in {32, 64, 128}; T*k < 2^24; M <= E.
  *   - Layouts are row-major. fp16 = IEEE binary16, passed as void*.
  *   - Packed INT4 weights W[N][K]: codes uint32 [N][K/8], word w of row n
  *     holds the codes for k = 8w .. 8w+7, the code for k = 8w+j in bits

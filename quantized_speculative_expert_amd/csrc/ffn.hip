@@ -948,8 +948,10 @@ smoe_status check_common(const char* who, const void* x, int T, int k, int E, in
   SMOE_REQUIRE(T >= 0 && k > 0 && E > 0 && H > 0 && I > 0 && shared_I >= 0, SMOE_EINVAL,
                "%s: need T, shared_I >= 0 and k, E, H, I > 0 (T=%d k=%d E=%d H=%d I=%d "
                "shared_I=%d)", who, T, k, E, H, I, shared_I);
-  SMOE_REQUIRE(E <= kMaxE && k <= kMaxK && k <= E, SMOE_EUNSUPPORTED,
-               "%s: need E <= 256 and k <= min(8, E) (E=%d k=%d)", who, E, k);
+  // (k may exceed E here: a call can cover a subset of the experts, one of
+  // them or one device's share, with the window's own k)
+  SMOE_REQUIRE(E <= kMaxE && k <= kMaxK, SMOE_EUNSUPPORTED,
+               "%s: need E <= 256 and k <= 8 (E=%d k=%d)", who, E, k);
   SMOE_REQUIRE(H % 128 == 0 && I % 128 == 0 && shared_I % 128 == 0, SMOE_EUNSUPPORTED,
                "%s: H, I and shared_I must be multiples of 128 (H=%d I=%d shared_I=%d)", who, H,
                I, shared_I);

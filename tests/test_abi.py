@@ -136,6 +136,11 @@ def test_ffn_argument_checks(lib):
     ws = 1 << 30
     assert f(16, 17, 6, 64, 2048, 1408, 96, *w, *ns, 256, ws, 16, N, N) == EUNSUPPORTED  # G
     assert f(16, 17, 6, 64, 2048, 1400, 128, *w, *ns, 256, ws, 16, N, N) == EUNSUPPORTED  # I
+    assert f(16, 17, 9, 64, 2048, 1408, 128, *w, *ns, 256, ws, 16, N, N) == EUNSUPPORTED  # k
+    # k > E passes the limits (a call over one expert's slots): the workspace
+    # check after them is what fails here
+    assert f(16, 17, 6, 1, 2048, 1408, 128, *w, *ns, 256, 10, 16, N, N) == EINVAL
+    assert b"workspace" in lib.smoe_last_error()
     assert f(16, 17, 6, 64, 2048, 1408, 128, *w, *ns, 256, 10, 16, N, N) == EINVAL  # small ws
     assert f(16, 17, 6, 64, 2048, 1408, 128, *w, *ns, 8, ws, 16, N, N) == EINVAL  # ws align
     # shared expert: size checks, pointers and alignment

@@ -365,6 +365,36 @@ def test_w4a16_ffn_matches_oracle(smoe, name):
     assert err <= ROW_TOL, err
 
 
+@pytest.mark.parametrize("name", ["tiny", "dsv2"])
+def test_w4a16_ffn_one_expert_per_call(smoe, name):
+    """A call may cover a subset of the experts with the window's k (here
+    E = 1 < k): the expert's weights, the full sorted slot list and the
+    expert's [begin, end) offsets. Its slots' rows equal the oracle's."""
+    L = layer(name)
+    cfg = L.cfg
+    ids = oracle.topk_experts(oracle.router_logits_f32(L.x, L.w_router, L.router_bias), cfg.k)
+    ref = oracle_slots_int4(L, ids)
+    al = oracle.align_by_expert(ids, cfg.E)
+    off = al["offsets"]
+    T, H = L.x.shape
+    ws = torch.zeros(smoe.smoe_ffn_workspace_bytes(T, cfg.k, 1, H, cfg.I), dtype=torch.uint8,
+                     device="cuda")
+    x, ss = dev(L.x), dev(al["sorted_slots"])
+    w = {n: dev(getattr(L, n)) for n in ("wg_q", "wg_s", "wu_q", "wu_s", "wd_q", "wd_s")}
+    active = [e for e in range(cfg.E) if off[e + 1] > off[e]][:8]
+    for e in active:
+        out = torch.full((T * cfg.k, H), float("nan"), dtype=torch.float32, device="cuda")
+        sl = slice(e, e + 1)
+        o = torch.tensor([off[e], off[e + 1]], dtype=torch.int32, device="cuda")
+        smoe.smoe_w4a16_expert_ffn(x, cfg.k, 1, cfg.I, cfg.G, *(w[n][sl] for n in (
+            "wg_q", "wg_s", "wu_q", "wu_s", "wd_q", "wd_s")), ss, o, ws, out)
+        rows = al["sorted_slots"][off[e]:off[e + 1]]
+        got = host(out)[rows]
+        assert np.isfinite(got).all(), e
+        err = row_rel_err(got, ref[rows])
+        assert err <= ROW_TOL, (e, err)
+
+
 def _synthetic_int4(E, H, I, G, seed):
     rng = np.random.default_rng(seed)
     q = {}
