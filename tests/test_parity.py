@@ -206,6 +206,7 @@ def _run_routing(smoe, fused, x, w, bias, k, flags, gate_w, elb):
 
 @pytest.mark.parametrize("name,elb", [("tiny", None), ("dsv2", (1, 0, 32, 0)),
                                       ("qwen", (3, 1, 8, 1)), ("phi", (2, 1, 4, 0)),
+                                      ("dsv2", (26, 20, 32, 1)),   # more layers than waves
                                       ("batch", (26, 3, 32, 0))])
 def test_route_align_elb_equals_separate_calls(smoe, name, elb):
     # one call == route_topk, align_by_expert, elb_accumulate_topm one after
@@ -234,6 +235,20 @@ def test_route_align_elb_ties_and_renorm(smoe):
         ref = _run_routing(smoe, False, *args)
         for key in ref:
             assert np.array_equal(got[key], ref[key]), (k, key)
+
+
+@pytest.mark.parametrize("T,k,E,elb", [(64, 8, 256, (20, 5, 64, 0)),   # 512 slots, E = 256
+                                       (1, 1, 1, (3, 2, 1, 1)),          # one slot, one expert
+                                       (65, 7, 100, (16, 15, 100, 1))])  # M = E, ragged chunks
+def test_route_align_elb_window_limits(smoe, T, k, E, elb):
+    rng = np.random.default_rng(T * 1000 + E)
+    x = rng.standard_normal((T, 256)).astype(np.float16)
+    w = (rng.standard_normal((E, 256)) * 0.02).astype(np.float32)
+    args = (x, w, None, k, 0, None, elb)
+    got = _run_routing(smoe, True, *args)
+    ref = _run_routing(smoe, False, *args)
+    for key in ref:
+        assert np.array_equal(got[key], ref[key]), key
 
 
 # ------------------------------------------------------------------ alignment
@@ -488,6 +503,8 @@ def test_w4a16_ffn_with_shared_expert(smoe, name):
     (8, 2, 40, 256, 384, 64, 640),   # shared expert over two token chunks (32 + 8)
     (16, 1, 1, 384, 256, 128, 256),  # a single token
     (6, 3, 17, 128, 128, 32, 3072),  # shared rows staged in several k phases
+    (8, 3, 200, 256, 384, 128, 512),  # wide chunks (128 slots): routed and shared, 72-row tail
+    (32, 2, 97, 384, 256, 128, 384),  # wide chunks, a 97-token shared chunk (7 column groups)
 ])
 def test_w4a16_ffn_with_shared_shapes(smoe, E, k, T, H, I, G, Is):
     rng = np.random.default_rng(T + Is)
@@ -522,7 +539,7 @@ def test_fp16_ffn_with_shared_expert(smoe):
 
 
 @pytest.mark.parametrize("E,k,T,H,I", [(8, 2, 17, 256, 512), (4, 2, 150, 256, 256),
-                                       (16, 1, 1, 384, 256)])
+                                       (16, 1, 1, 384, 256), (3, 3, 300, 256, 384)])
 def test_fp16_ffn_shapes(smoe, E, k, T, H, I):
     rng = np.random.default_rng(E * T)
     x = rng.standard_normal((T, H)).astype(np.float16)
