@@ -93,7 +93,7 @@ def check_align(got, ref):
 
 # ------------------------------------------------------------------ router
 
-@pytest.mark.parametrize("name", ["tiny", "dsv2", "qwen", "phi"])
+@pytest.mark.parametrize("name", ["tiny", "dsv2", "qwen", "phi", "dsv2_t1"])
 def test_route_matches_oracle(smoe, name):
     L = layer(name)
     cfg = L.cfg
@@ -598,7 +598,7 @@ def test_combine_matches_oracle(smoe):
 
 # ------------------------------------------------------------------ whole layer
 
-@pytest.mark.parametrize("name", ["tiny", "dsv2", "qwen"])
+@pytest.mark.parametrize("name", ["tiny", "dsv2", "qwen", "dsv2_t1"])
 @pytest.mark.parametrize("mode", ["fused", "fused-side", "separate", "separate-side",
                                   "three-routing-calls"])
 def test_layer_draft_matches_oracle(smoe, name, mode):

@@ -1,4 +1,4 @@
-"""The five layer shapes the hot path is measured and checked on.
+"""The layer shapes the hot path is measured and checked on.
 
 Model shapes follow the expert matrix sizes the Specter paper names for
 fine-grained MoE models (2048x1408 and 4096x6400 expert matrices, in the
@@ -7,7 +7,9 @@ paragraph on Marlin and narrow expert GEMMs) and its speculation depths
 paragraph on selecting K). The window holds the K candidates plus the
 uncached corrected/bonus token (Specter paper, State Manager paragraph), so
 T = K + 1. The batched shape follows the batched-execution paragraph
-(B up to 32 requests).
+(B up to 32 requests). The single-token step (dsv2_t1) is one call of the
+autoregressive draft that proposes those K tokens (Specter paper, the
+speculative-decoding paragraphs), and is the latency-bound end of the range.
 """
 
 from dataclasses import dataclass, field
@@ -58,6 +60,11 @@ CONFIGS = {
         description="Phi-3.5-MoE-shaped layer: 16 experts, top-2, hidden 4096, "
                     "intermediate 6400, 17 tokens; INT4 g128 draft pass and FP16 "
                     "target verification pass on the same tokens"),
+    "dsv2_t1": MoEConfig(
+        name="dsv2_t1", E=64, k=6, H=2048, I=1408, G=128, T=1,
+        shared_I=2 * 1408, elb_M=32,
+        description="DeepSeek-V2-Lite-shaped single-token draft step: the dsv2 layer at "
+                    "T=1, one autoregressive draft token"),
     "batch": MoEConfig(
         name="batch", E=64, k=6, H=2048, I=1408, G=128, T=32 * 17,
         shared_I=2 * 1408, layers=26, zipf_s=1.1, elb_M=32,
