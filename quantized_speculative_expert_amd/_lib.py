@@ -89,6 +89,13 @@ def _ptr(t: Optional[torch.Tensor], dtype=None, name: str = "tensor") -> Optiona
     return t.data_ptr() if t.numel() else None
 
 
+def _need(t: Optional[torch.Tensor], n: int, name: str) -> None:
+    """The library reads or writes n elements behind t's pointer: refuse a
+    smaller tensor here, before a kernel could run off its end."""
+    if t is not None and t.numel() < n:
+        raise ValueError(f"{name} holds {t.numel()} elements, the call needs {n}")
+
+
 def _stream(stream) -> Optional[int]:
     if stream is None:
         stream = torch.cuda.current_stream()
@@ -112,14 +119,37 @@ def _shared_args(shared, shared_out):
             raise ValueError("shared_out given without shared-expert weights")
         return 0, None, None, None, None
     sg, su, sd = shared
+    if sg.dim() != 2 or su.shape != sg.shape or sd.dim() != 2 or sd.shape[1] != sg.shape[0]:
+        raise ValueError("shared weights must be wg, wu [shared_I][H] and wd [H][shared_I]")
     return (sg.shape[0], _ptr(sg, torch.float16, "shared_wg"), _ptr(su, torch.float16, "shared_wu"),
             _ptr(sd, torch.float16, "shared_wd"), _ptr(shared_out, torch.float32, "shared_out"))
+
+
+def _route_sizes(T, H, E, k, w_router, logit_bias, topk_ids, topk_w, logits, shared_gate_w,
+                 shared_gate) -> None:
+    _need(w_router, E * H, "w_router")
+    _need(logit_bias, E, "logit_bias")
+    _need(topk_ids, T * k, "topk_ids")
+    _need(topk_w, T * k, "topk_w")
+    _need(logits, T * E, "logits")
+    _need(shared_gate_w, H, "shared_gate_w")
+    _need(shared_gate, T, "shared_gate")
+
+
+def _align_sizes(S, E, counts, offsets, sorted_slots, active, n_active) -> None:
+    _need(counts, E, "expert_counts")
+    _need(offsets, E + 1, "expert_offsets")
+    _need(sorted_slots, S, "sorted_slots")
+    _need(active, E, "active_experts")
+    _need(n_active, 1, "n_active")
 
 
 def smoe_route_topk(x, w_router, logit_bias, k: int, flags: int, topk_ids, topk_w, logits,
                     shared_gate_w=None, shared_gate=None, stream=None) -> None:
     T, H = x.shape
     E = w_router.shape[0]
+    _route_sizes(T, H, E, k, w_router, logit_bias, topk_ids, topk_w, logits, shared_gate_w,
+                 shared_gate)
     _check("smoe_route_topk", _lib.smoe_route_topk(
         _ptr(x, torch.float16, "x"), _ptr(w_router, torch.float32, "w_router"),
         _ptr(logit_bias, torch.float32, "logit_bias"), T, H, E, k, flags,
@@ -139,6 +169,12 @@ def smoe_route_align_elb(x, w_router, logit_bias, k: int, flags: int, topk_ids, 
     T, H = x.shape
     E = w_router.shape[0]
     L = elb_counts.shape[0] if elb_counts is not None else 0
+    _route_sizes(T, H, E, k, w_router, logit_bias, topk_ids, topk_w, logits, shared_gate_w,
+                 shared_gate)
+    _align_sizes(T * k, E, expert_counts, expert_offsets, sorted_slots, active_experts, n_active)
+    _need(elb_counts, L * E, "elb_counts")
+    _need(plan_ids, L * M, "plan_ids")
+    _need(plan_counts, L * M, "plan_counts")
     _check("smoe_route_align_elb", _lib.smoe_route_align_elb(
         _ptr(x, torch.float16, "x"), _ptr(w_router, torch.float32, "w_router"),
         _ptr(logit_bias, torch.float32, "logit_bias"), T, H, E, k, flags,
@@ -159,6 +195,7 @@ def smoe_route_align_elb(x, w_router, logit_bias, k: int, flags: int, topk_ids, 
 def smoe_align_by_expert(topk_ids, E: int, expert_counts, expert_offsets, sorted_slots,
                          active_experts, n_active, stream=None) -> None:
     T, k = topk_ids.shape
+    _align_sizes(T * k, E, expert_counts, expert_offsets, sorted_slots, active_experts, n_active)
     _check("smoe_align_by_expert", _lib.smoe_align_by_expert(
         _ptr(topk_ids, torch.int32, "topk_ids"), T, k, E,
         _ptr(expert_counts, torch.int32, "expert_counts"),
@@ -176,11 +213,23 @@ def smoe_elb_accumulate_topm(elb_counts, topk_ids, layer_begin: int, M: int, pla
         n_layers, T, k = topk_ids.shape
     else:
         n_layers, T, k = 0, 0, 1
+    _need(plan_ids, L * M, "plan_ids")
+    _need(plan_counts, L * M, "plan_counts")
     _check("smoe_elb_accumulate_topm", _lib.smoe_elb_accumulate_topm(
         _ptr(elb_counts, torch.int32, "elb_counts"), L, E,
         _ptr(topk_ids, torch.int32, "topk_ids"), layer_begin, n_layers, T, k, M,
         _ptr(plan_ids, torch.int32, "plan_ids"), _ptr(plan_counts, torch.int32, "plan_counts"),
         flags, _stream(stream)))
+
+
+def _ffn_sizes(T, k, E, H, sI, sorted_slots, expert_offsets, slot_out, shared, shared_out):
+    _need(sorted_slots, T * k, "sorted_slots")
+    _need(expert_offsets, E + 1, "expert_offsets")
+    _need(slot_out, T * k * H, "slot_out")
+    if shared is not None:
+        for name, t in zip(("shared_wg", "shared_wu", "shared_wd"), shared):
+            _need(t, sI * H, name)
+        _need(shared_out, T * H, "shared_out")
 
 
 def smoe_w4a16_expert_ffn(x, k: int, E: int, I: int, group_size: int, wg_q, wg_s, wu_q, wu_s,
@@ -189,6 +238,14 @@ def smoe_w4a16_expert_ffn(x, k: int, E: int, I: int, group_size: int, wg_q, wg_s
     """shared: optional (wg, wu, wd) fp16 weights of the always-on shared expert."""
     T, H = x.shape
     sI, sg, su, sd, so = _shared_args(shared, shared_out)
+    G = max(group_size, 1)
+    for name, t in (("wg_q", wg_q), ("wu_q", wu_q)):
+        _need(t, E * I * H // 8, name)
+    for name, t in (("wg_s", wg_s), ("wu_s", wu_s)):
+        _need(t, E * I * H // G, name)
+    _need(wd_q, E * H * I // 8, "wd_q")
+    _need(wd_s, E * H * I // G, "wd_s")
+    _ffn_sizes(T, k, E, H, sI, sorted_slots, expert_offsets, slot_out, shared, shared_out)
     _check("smoe_w4a16_expert_ffn", _lib.smoe_w4a16_expert_ffn(
         _ptr(x, torch.float16, "x"), T, k, E, H, I, group_size,
         _ptr(wg_q, torch.int32, "wg_q"), _ptr(wg_s, torch.float16, "wg_s"),
@@ -205,6 +262,9 @@ def smoe_fp16_expert_ffn(x, k: int, E: int, I: int, wg, wu, wd, sorted_slots, ex
     """shared: optional (wg, wu, wd) fp16 weights of the always-on shared expert."""
     T, H = x.shape
     sI, sg, su, sd, so = _shared_args(shared, shared_out)
+    for name, t in (("wg", wg), ("wu", wu), ("wd", wd)):
+        _need(t, E * I * H, name)
+    _ffn_sizes(T, k, E, H, sI, sorted_slots, expert_offsets, slot_out, shared, shared_out)
     _check("smoe_fp16_expert_ffn", _lib.smoe_fp16_expert_ffn(
         _ptr(x, torch.float16, "x"), T, k, E, H, I,
         _ptr(wg, torch.float16, "wg"), _ptr(wu, torch.float16, "wu"),
@@ -218,6 +278,10 @@ def smoe_fp16_expert_ffn(x, k: int, E: int, I: int, wg, wu, wd, sorted_slots, ex
 def smoe_combine(slot_out, topk_w, shared_out, shared_gate, y, stream=None) -> None:
     T, k = topk_w.shape
     H = y.shape[1]
+    _need(slot_out, T * k * H, "slot_out")
+    _need(shared_out, T * H, "shared_out")
+    _need(shared_gate, T, "shared_gate")
+    _need(y, T * H, "y")
     _check("smoe_combine", _lib.smoe_combine(
         _ptr(slot_out, torch.float32, "slot_out"), _ptr(topk_w, torch.float32, "topk_w"),
         T, k, H, _ptr(shared_out, torch.float32, "shared_out"),

@@ -172,3 +172,39 @@ def test_combine_argument_checks(lib):
     assert f(N, N, 17, 6, 2048, N, N, N, N) == EINVAL
     assert f(8, 16, 17, 6, 2048, N, N, 16, N) == EINVAL  # misaligned slot_out
     assert f(N, N, 0, 6, 2048, N, N, N, N) == 0
+
+
+def test_binding_refuses_short_tensors(lib):
+    # the Python binding checks every buffer's size against the shapes the
+    # call implies before any pointer reaches the library (CPU tensors: the
+    # size check comes first, so nothing is launched)
+    import torch
+    from quantized_speculative_expert_amd import _lib as smoe
+    i32 = dict(dtype=torch.int32)
+    f16, f32 = dict(dtype=torch.float16), dict(dtype=torch.float32)
+    T, k, E, H, I, G = 17, 2, 8, 256, 512, 64
+    x = torch.zeros((T, H), **f16)
+    codes = torch.zeros(E * I * H // 8, **i32)
+    scales = torch.zeros(E * I * H // G, **f16)
+    ok = dict(sorted_slots=torch.zeros(T * k, **i32), expert_offsets=torch.zeros(E + 1, **i32),
+              workspace=torch.zeros(16, dtype=torch.uint8), slot_out=torch.zeros(T * k * H, **f32))
+
+    def ffn(**over):
+        a = dict(wg_q=codes, wg_s=scales, wu_q=codes, wu_s=scales, wd_q=codes, wd_s=scales, **ok)
+        a.update(over)
+        smoe.smoe_w4a16_expert_ffn(x, k, E, I, G, a["wg_q"], a["wg_s"], a["wu_q"], a["wu_s"],
+                                   a["wd_q"], a["wd_s"], a["sorted_slots"], a["expert_offsets"],
+                                   a["workspace"], a["slot_out"])
+
+    for name, short in (("wg_q", codes[:-1]), ("wd_s", scales[:-1]),
+                        ("sorted_slots", ok["sorted_slots"][:-1]),
+                        ("expert_offsets", ok["expert_offsets"][:E]),
+                        ("slot_out", ok["slot_out"][:-1])):
+        with pytest.raises(ValueError, match=name):
+            ffn(**{name: short})
+    with pytest.raises(ValueError, match="logits"):
+        smoe.smoe_route_topk(x, torch.zeros((E, H), **f32), None, k, 0, torch.zeros(T * k, **i32),
+                             torch.zeros(T * k, **f32), torch.zeros(T * E - 1, **f32))
+    with pytest.raises(ValueError, match="y holds"):
+        smoe.smoe_combine(torch.zeros(T * k * H, **f32), torch.zeros((T, k), **f32), None, None,
+                          torch.zeros((T - 1, H), **f16))
