@@ -162,23 +162,50 @@ def cpu_baseline(cfg_name: str, reps: int):
     import oracle
     from workload import get_config, make_layer
 
+    from threadpoolctl import threadpool_limits
+
     cfg = get_config(cfg_name)
     L = make_layer(cfg, seed=0)
-    t0 = time.perf_counter()
-    for _ in range(reps):
-        r = oracle.moe_layer(L, "draft")
-        if cfg.elb_M:
-            cnt = oracle.elb_accumulate(np.zeros((1, cfg.E), np.int32), r["ids"][None], 0)
-            oracle.elb_topm(cnt, cfg.elb_M)
-    dt = time.perf_counter() - t0
+
+    def layers(n):
+        t0 = time.perf_counter()
+        for _ in range(n):
+            r = oracle.moe_layer(L, "draft")
+            if cfg.elb_M:
+                cnt = oracle.elb_accumulate(np.zeros((1, cfg.E), np.int32), r["ids"][None], 0)
+                oracle.elb_topm(cnt, cfg.elb_M)
+        return time.perf_counter() - t0, r
+
+    dt, r = layers(reps)
     blas = [i.get("num_threads", 1) for i in threadpool_info()]
     cores = max(blas) if blas else 1
+    # one BLAS thread, on a smaller sample
+    reps1 = max(1, reps // 5)
+    with threadpool_limits(limits=1):
+        dt1, _ = layers(reps1)
+    # bytes the layer's algorithm touches, as on the GPU side: the touched
+    # experts' codes and scales, the shared experts, the router, x and y
+    n_active = int(r["n_active"])
+    per_expert = sum(getattr(L, n_)[0].nbytes for n_ in ("wg_q", "wg_s", "wu_q", "wu_s", "wd_q", "wd_s"))
+    shared = sum(t.nbytes for t in (L.sg16, L.su16, L.sd16) if t is not None)
+    router = sum(t.nbytes for t in (L.w_router, L.router_bias, L.shared_gate_w) if t is not None)
+    nbytes = n_active * per_expert + shared + router + 2 * cfg.T * cfg.H * 2
+    model = ""
+    try:
+        with open("/proc/cpuinfo") as f:
+            model = next((ln.split(":", 1)[1].strip() for ln in f if ln.startswith("model name")), "")
+    except OSError:
+        pass
     return {"value": cfg.T * reps / dt, "unit": "tokens/s", "cores": cores, "kind": "oracle",
             "sample": (f"{reps} full {cfg.name} layers of {cfg.T} tokens (route, align, ELB "
                        f"top-{cfg.elb_M}, INT4 dequantise + float64 SwiGLU of the touched "
                        f"experts, shared experts, combine) in {dt:.1f} s; BLAS matmuls on "
-                       f"{cores} threads, the rest single-threaded NumPy"),
-            "ms_per_layer": 1e3 * dt / reps}
+                       f"{cores} threads, the rest single-threaded NumPy; then {reps1} on one "
+                       f"BLAS thread"),
+            "ms_per_layer": 1e3 * dt / reps,
+            "single_thread_value": cfg.T * reps1 / dt1,
+            "gbps": nbytes * reps / dt / 1e9,
+            "cpu_model": model, "os_cpu_count": os.cpu_count()}
 
 
 # ----------------------------------------------------------------------------- GPU leg
