@@ -426,6 +426,7 @@ def _synthetic_int4(E, H, I, G, seed):
     (4, 2, 150, 256, 256, 128),      # 75 slots per expert: 64-slot chunks, several per expert
     (16, 1, 1, 384, 256, 128),       # a single token
     (6, 3, 40, 128, 128, 64),        # minimal sizes, ragged chunks
+    (256, 8, 33, 128, 128, 32),      # the limits: 256 experts, top-8, g32
 ])
 def test_w4a16_ffn_shapes(smoe, E, k, T, H, I, G):
     rng = np.random.default_rng(T * 7 + E)
@@ -594,6 +595,27 @@ def test_combine_matches_oracle(smoe):
         got = host(y).astype(np.float64)
         # fp16 output: within one fp16 rounding step of the float64 sum
         assert np.all(np.abs(got - y64) <= np.abs(y64) * 2.0 ** -10 + 1e-6)
+
+
+def test_empty_window_is_a_noop(smoe):
+    """T = 0: every call returns at once; the fused routing call still ranks
+    the ELB counters, exactly as the separate calls do."""
+    rng = np.random.default_rng(41)
+    x = np.zeros((0, 256), np.float16)
+    w = (rng.standard_normal((8, 256)) * 0.02).astype(np.float32)
+    got = _run_routing(smoe, True, x, w, None, 2, 0, None, (2, 1, 3, 0))
+    ref = _run_routing(smoe, False, x, w, None, 2, 0, None, (2, 1, 3, 0))
+    for key in ref:
+        assert np.array_equal(got[key], ref[key]), key
+    assert not got["offsets"].any() and int(got["n_active"][0]) == 0
+    q = _synthetic_int4(8, 256, 128, 64, seed=5)
+    out = run_w4a16(smoe, x, np.zeros((0, 2), np.int32), 8, 128, 64, q["wg_q"], q["wg_s"],
+                    q["wu_q"], q["wu_s"], q["wd_q"], q["wd_s"])
+    assert out.shape == (0, 256)
+    y = torch.empty((0, 256), dtype=torch.float16, device="cuda")
+    smoe.smoe_combine(torch.empty((0, 256), dtype=torch.float32, device="cuda"),
+                      torch.empty((0, 2), dtype=torch.float32, device="cuda"), None, None, y)
+    torch.cuda.synchronize()
 
 
 # ------------------------------------------------------------------ whole layer
