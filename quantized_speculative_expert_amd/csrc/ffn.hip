@@ -55,6 +55,10 @@
 //   bytes per row so the MFMA operand reads are bank-conflict free. The
 //   first staging issues its loads before the weight prologue, so it never
 //   waits behind it. Rows longer than the LDS budget are staged in phases.
+//   When all T rows of x fit (short windows), stage 1 instead stages x
+//   whole once per launch and an item's A rows are the tokens of its
+//   slots: no item restages, and the FP16 shared weights take the INT4
+//   k-permutation in registers.
 // * Weight ring. Each wave streams its rows through a register ring of D
 //   blocks that runs on across items; weights are the only global loads in
 //   it, so the in-order vector memory counter never waits on anything but
@@ -165,6 +169,7 @@ struct FfnArgs {
   int slots_lds;                // all S sorted slots copied to LDS at start
   int xs_off;                   // LDS byte offset of the staged rows
   int rows_lds;                 // staged rows the LDS holds (largest chunk)
+  int xres;                     // stage 1: all T rows of x held in LDS for the whole launch
   Group grp[2];
 };
 
@@ -217,9 +222,10 @@ struct Item {
 };
 
 
-template <int WK, int G, int STAGE, int NC>
+template <int WK, int G, int STAGE, int NC, int XRES>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) void ffn_kernel(
     FfnArgs a) {
+  static_assert(XRES == 0 || STAGE == 1, "x is resident in stage 1 only");
   constexpr int D = stage_d(STAGE);
   constexpr int NQ = WK == kInt4 ? 128 / G : 1;  // INT4 group scales per block
   extern __shared__ __align__(16) uint8_t smem[];
@@ -253,10 +259,14 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
   const int ep = a.hdr[STAGE == 1 ? 0 : 1];
   float* gu = a.gu + ((STAGE == 1 ? ep : ep - 1) & 1) * a.gu_buf;  // this call's g/u
   if (tid <= E) s_off[tid] = min(max(offv, 0), a.S);  // clamped to [0, S]
+  // (stage 1 with x resident keeps the token of each sorted slot instead)
+  constexpr bool xres = XRES != 0;
   if (a.slots_lds) {
 #pragma unroll
     for (int j = 0; j < kSlotsPer; ++j)
-      if (tid + j * kThreads < a.S) s_slots[tid + j * kThreads] = slv[j];
+      if (tid + j * kThreads < a.S)
+        s_slots[tid + j * kThreads] =
+            !xres ? slv[j] : (slv[j] >= 0 && slv[j] < a.S ? slv[j] / a.k : 0);
   }
   if (b == 0) {
     if (tid == 0) a.hdr[STAGE == 1 ? 1 : 0] = STAGE == 1 ? ep + 1 : ep;
@@ -516,15 +526,20 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
     }
   };
   // One FP16 block (32 k) at k offset kk of the staged rows.
+  // (resident x rows are k-permuted for the INT4 groups; the FP16 weights
+  // then take the same permutation)
+  constexpr bool bperm = WK == kInt4 && xres;
   auto compute_fp16 = [&](const u32x4 (&r)[2], int kk, auto nce_tag) {
     constexpr int NCE = decltype(nce_tag)::value;
+    f16x8 B[2];
+#pragma unroll
+    for (int m = 0; m < 2; ++m) B[m] = bitcast<f16x8>(bperm ? permute_k8(r[m]) : r[m]);
 #pragma unroll
     for (int cg = 0; cg < NCE; ++cg) {
       const f16x8 A = *reinterpret_cast<const f16x8*>(xs + arow[cg] + 2 * (kk + 8 * g));
 #pragma unroll
       for (int m = 0; m < 2; ++m)
-        acc[m][cg] =
-            __builtin_amdgcn_mfma_f32_16x16x32_f16(A, bitcast<f16x8>(r[m]), acc[m][cg], 0, 0, 0);
+        acc[m][cg] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, B[m], acc[m][cg], 0, 0, 0);
     }
   };
 
@@ -611,6 +626,34 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
     __syncthreads();
   };
 
+  // Stage 1 with x resident: all T rows of x, whole, once per launch (row t
+  // at t * stride, k-permuted for INT4 weights), so no item restages.
+  // `mid` runs right after the first batch of loads is issued; a batch
+  // covers a 2048-wide window of 17 tokens, so at those sizes every x load
+  // is out before the weight prologue and none waits behind it.
+  auto stage_x_all = [&](auto&& mid) {
+    constexpr int NB = 9;  // pieces in flight per thread
+    const int npr = a.H / 8;
+    const int tot = a.T * npr;
+    for (int base = 0; base < tot; base += NB * kThreads) {
+      u32x4 v[NB];
+      int dst[NB];
+#pragma unroll
+      for (int j = 0; j < NB; ++j) {
+        const int i = min(base + j * kThreads + tid, tot - 1);
+        const int r = i / npr, c = i - r * npr;
+        v[j] = *reinterpret_cast<const u32x4*>(a.x + static_cast<long long>(r) * a.H + 8 * c);
+        dst[j] = base + j * kThreads + tid < tot ? r * a.stride + 16 * c : -1;
+      }
+      if (base == 0) mid();
+#pragma unroll
+      for (int j = 0; j < NB; ++j)
+        if (dst[j] >= 0)
+          *reinterpret_cast<u32x4*>(xs + dst[j]) = WK == kInt4 ? permute_k8(v[j]) : v[j];
+    }
+    __syncthreads();
+  };
+
   // Write the sums of a tile; a tile split with other workgroups is added
   // into the (zeroed) output with device-scope atomics.
   auto write_tile = [&](const Item& it, bool whole) {
@@ -672,18 +715,27 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
     return pos < q0 ? s0 + q0 : (next == item + 1 ? item + 2 : item + 1);
   };
 
-  // ---- prologue: stage the first chunk, the first item's blocks in flight
+  // ---- prologue: stage the first chunk (or, x resident, all of x), the
+  // first item's blocks in flight
   Item ci = decode(cur);
   set_load_item(ci);
   u32x4 ring[D][2];
   int c_fmt = l_fmt, c_nblk = l_nblk;
   int staged_id = ci.grp * (1 << 24) + ci.chunk;
-  window(ci, cur, run_end_of(0, cur, nxt));
-  stage_rows(ci, st_lo, st_hi, std::integral_constant<int, STAGE == 1 ? 4 : 2>(), [&]() {
+  auto prologue_loads = [&]() {
     if (WK == kInt4 && l_fmt == kInt4) load_scales(l_blk0);
 #pragma unroll
     for (int d = 0; d < D; ++d) load(ring[d], min(l_blk0 + d, l_nblk - 1));
-  });
+  };
+  if constexpr (xres) {
+    st_lo = 0;
+    st_hi = a.H;
+    stage_x_all(prologue_loads);
+  } else {
+    window(ci, cur, run_end_of(0, cur, nxt));
+    stage_rows(ci, st_lo, st_hi, std::integral_constant<int, STAGE == 1 ? 4 : 2>(),
+               prologue_loads);
+  }
   int seg_pa = ci.part;  // first part of the tile accumulated so far
   int prev = -2;         // the item before cur
 
@@ -701,7 +753,16 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
     const int id = ci.grp * (1 << 24) + ci.chunk;
     const int k0 = blk0 * kblk;
     const int k1 = min(a.grp[ci.grp].K, k0 + D * kblk);
-    if (id != staged_id || k0 < st_lo || k1 > st_hi) {
+    if constexpr (xres) {
+      // A operand rows of this item: the tokens of its slots
+#pragma unroll
+      for (int cg = 0; cg < NC; ++cg) {
+        const int rr = max(min(16 * cg + r16, ci.m - 1), 0);
+        const int tok = ci.grp == 0 ? s_slots[min(ci.seg0 + rr, a.S - 1)]
+                                    : min(ci.seg0 + rr, a.T - 1);  // shared: slot t is token t
+        arow[cg] = tok * a.stride;
+      }
+    } else if (id != staged_id || k0 < st_lo || k1 > st_hi) {
       window(ci, cur, run_end_of(pos, cur, nxt));
       stage_rows(ci, st_lo, st_hi, std::integral_constant<int, STAGE == 1 ? 2 : 1>(), []() {});
       staged_id = id;
@@ -736,13 +797,15 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
       if (WK == kInt4 && l_fmt == kInt4) load_scales(l_blk0);
     }
 
+    // (with x resident the routed chunks are at most 16 slots: only the
+    // shared expert's chunks can be wide, and they are FP16)
     const bool wide = NC == 2 && ci.m > 16;
     const int kk0 = k0 - st_lo;
 #pragma unroll
     for (int d = 0; d < D; ++d) {
       if (blk0 + d < c_nblk) {
         if (WK == kInt4 && c_fmt == kInt4) {
-          if (wide)
+          if (!xres && wide)
             compute_int4(ring[d], kk0 + d * 128, d, std::integral_constant<int, NC>());
           else
             compute_int4(ring[d], kk0 + d * 128, d, std::integral_constant<int, 1>());
@@ -913,11 +976,22 @@ void make_plans(StagePlans& p, const void* x, int T, int k, int H, const int32_t
   }
   p.lds1 = plan_lds(a1, H, phase_k(1));
   p.lds2 = plan_lds(a2, kmax2, phase_k(2));
+  // stage 1 keeps all of x in LDS when it fits beside the table and the
+  // sorted slots and the routed chunks are narrow: items then never restage
+  // and the tail goes out one item at a time
+  const long long xres_bytes = a1.xs_off + static_cast<long long>(T) * (2 * H + kRowPad);
+  if (a1.slots_lds && gw[0].csz <= 16 && xres_bytes <= kLdsBudget) {
+    a1.xres = 1;
+    a1.rows_lds = T;
+    a1.kph = H;
+    a1.stride = 2 * H + kRowPad;
+    p.lds1 = static_cast<int>(xres_bytes);
+  }
 }
 
-template <int WK, int G, int STAGE, int NC>
+template <int WK, int G, int STAGE, int NC, int XRES>
 smoe_status launch_stage(const FfnArgs& a, int lds, long long items, hipStream_t st) {
-  auto kern = ffn_kernel<WK, G, STAGE, NC>;
+  auto kern = ffn_kernel<WK, G, STAGE, NC, XRES>;
   static std::atomic<int> attr_done{0};
   if (!attr_done.load(std::memory_order_acquire)) {
     if (hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
@@ -936,9 +1010,10 @@ smoe_status launch_stage(const FfnArgs& a, int lds, long long items, hipStream_t
 
 template <int WK, int G, int NC>
 smoe_status launch_ffn(const StagePlans& p, hipStream_t st) {
-  smoe_status s = launch_stage<WK, G, 1, NC>(p.a1, p.lds1, p.items1, st);
+  smoe_status s = p.a1.xres ? launch_stage<WK, G, 1, NC, 1>(p.a1, p.lds1, p.items1, st)
+                            : launch_stage<WK, G, 1, NC, 0>(p.a1, p.lds1, p.items1, st);
   if (s != SMOE_OK) return s;
-  return launch_stage<WK, G, 2, NC>(p.a2, p.lds2, p.items2, st);
+  return launch_stage<WK, G, 2, NC, 0>(p.a2, p.lds2, p.items2, st);
 }
 
 smoe_status check_common(const char* who, const void* x, int T, int k, int E, int H, int I,

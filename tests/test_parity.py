@@ -427,6 +427,7 @@ def _synthetic_int4(E, H, I, G, seed):
     (16, 1, 1, 384, 256, 128),       # a single token
     (6, 3, 40, 128, 128, 64),        # minimal sizes, ragged chunks
     (256, 8, 33, 128, 128, 32),      # the limits: 256 experts, top-8, g32
+    (8, 2, 17, 256, 512, 64),        # x resident in LDS for the gate/up stage, g64
 ])
 def test_w4a16_ffn_shapes(smoe, E, k, T, H, I, G):
     rng = np.random.default_rng(T * 7 + E)
@@ -506,6 +507,10 @@ def test_w4a16_ffn_with_shared_expert(smoe, name):
     (6, 3, 17, 128, 128, 32, 3072),  # shared rows staged in several k phases
     (8, 3, 200, 256, 384, 128, 512),  # wide chunks (128 slots): routed and shared, 72-row tail
     (32, 2, 97, 384, 256, 128, 384),  # wide chunks, a 97-token shared chunk (7 column groups)
+    (16, 2, 9, 256, 256, 32, 512),   # x resident: g32 routed, FP16 shared in the INT4 k order
+    (12, 3, 18, 512, 256, 64, 384),  # x resident: g64 routed, an 18-token shared chunk (2 groups)
+    (64, 6, 19, 2048, 256, 128, 256),  # the widest window that keeps x resident at H = 2048
+    (64, 6, 20, 2048, 256, 128, 256),  # one token more: x staged per chunk again
 ])
 def test_w4a16_ffn_with_shared_shapes(smoe, E, k, T, H, I, G, Is):
     rng = np.random.default_rng(T + Is)
