@@ -59,6 +59,9 @@ def parse_args():
     p.add_argument("--shared", choices=("fused", "separate"), default="fused",
                    help="shared experts inside the routed FFN launches (fused) or as a call "
                         "of their own (separate)")
+    p.add_argument("--layer", choices=("one-call", "calls"), default="calls",
+                   help="the layer step as one library call (smoe_moe_layer_w4a16) or as "
+                        "the separate calls")
     p.add_argument("--side-stream", action="store_true",
                    help="run the ELB update (and a separate shared-expert call) on a side "
                         "stream branch of the step graph instead of in line")
@@ -338,8 +341,12 @@ def main() -> int:
     side = torch.cuda.Stream(device=dev) if args.side_stream else None
     use_elb = cfg.elb_M > 0
 
+    one_call = args.layer == "one-call"
+    if one_call and (not fused or side is not None):
+        raise SystemExit("--layer one-call runs the shared experts fused and has no side stream")
+
     def step(d):
-        d.run(elb=use_elb, fuse_shared=fused, side_stream=side)
+        d.run(elb=use_elb, fuse_shared=fused, side_stream=side, one_call=one_call)
 
     # eager run once (checks every call), then capture the graphs
     for d in layers:
@@ -467,6 +474,7 @@ def main() -> int:
             "shared_I": cfg.shared_I, "elb_M": cfg.elb_M, "weights": "int4 g%d + fp16 scales" % cfg.G,
             "shared_experts": args.shared,
             "side_stream": side is not None,
+            "layer_call": args.layer,
         },
         "hbm_gbps": round(layer_gbps, 1),
         "hbm_frac": round(layer_gbps / PEAK_HBM_GBPS, 4),

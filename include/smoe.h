@@ -279,6 +279,44 @@ smoe_status smoe_combine(const float* slot_out, const float* topk_w, int T, int 
                          const float* shared_out, const float* shared_gate,
                          void* y, void* stream);
 
+/*
+ * The whole draft layer in one call: routing, alignment and the ELB update
+ * (smoe_route_align_elb), the W4A16 expert FFN with the optional FP16 shared
+ * experts (smoe_w4a16_expert_ffn) and the weighted combine (smoe_combine),
+ * as those calls made one after the other compute them, with the same
+ * arguments, checks and errors; every check runs before anything is
+ * enqueued. Specter paper: the draft MoE layer of the fused multi-expert
+ * draft kernel paragraph, fed by the Incremental Routing Pattern Analyzer.
+ *
+ * Arguments are those of the three calls (one copy of each shared one):
+ * routing and ELB as in smoe_route_align_elb; I, group_size, the routed
+ * INT4 weights, the shared FP16 weights, workspace, slot_out and shared_out
+ * as in smoe_w4a16_expert_ffn (sorted_slots and expert_offsets are this
+ * call's outputs); y [T][H] fp16 as in smoe_combine, whose shared_out is
+ * the FFN's when shared_I > 0 and whose gate is shared_gate. All buffers
+ * are caller-owned device memory.
+ *
+ * The layer takes the launches of the three calls: router logits, the
+ * top-k / alignment / ELB workgroup, the two FFN launches and the combine.
+ * On error nothing is enqueued.
+ */
+smoe_status smoe_moe_layer_w4a16(const void* x, const float* w_router, const float* logit_bias,
+                                 int T, int H, int E, int k, int flags,
+                                 int32_t* topk_ids, float* topk_w, float* logits,
+                                 const float* shared_gate_w, float* shared_gate,
+                                 int32_t* expert_counts, int32_t* expert_offsets,
+                                 int32_t* sorted_slots, int32_t* active_experts,
+                                 int32_t* n_active,
+                                 int32_t* elb_counts, int L, int layer, int M,
+                                 int32_t* plan_ids, int32_t* plan_counts, int elb_flags,
+                                 int I, int group_size,
+                                 const uint32_t* wg_q, const void* wg_s,
+                                 const uint32_t* wu_q, const void* wu_s,
+                                 const uint32_t* wd_q, const void* wd_s,
+                                 int shared_I, const void* shared_wg, const void* shared_wu,
+                                 const void* shared_wd, void* workspace, size_t workspace_bytes,
+                                 float* slot_out, float* shared_out, void* y, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

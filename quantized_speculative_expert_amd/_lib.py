@@ -44,6 +44,13 @@ _SIGNATURES = {
     "smoe_fp16_expert_ffn": (_i, [_p, _i, _i, _i, _i, _i, _p, _p, _p, _p, _p, _i, _p, _p, _p,
                                   _p, _sz, _p, _p, _p]),
     "smoe_combine": (_i, [_p, _p, _i, _i, _i, _p, _p, _p, _p]),
+    "smoe_moe_layer_w4a16": (_i, [_p, _p, _p, _i, _i, _i, _i, _i,      # x .. flags
+                                  _p, _p, _p, _p, _p,                  # topk_ids .. shared_gate
+                                  _p, _p, _p, _p, _p,                  # counts .. n_active
+                                  _p, _i, _i, _i, _p, _p, _i,          # elb_counts .. elb_flags
+                                  _i, _i, _p, _p, _p, _p, _p, _p,      # I, G, routed weights
+                                  _i, _p, _p, _p,                      # shared_I, shared weights
+                                  _p, _sz, _p, _p, _p, _p]),           # workspace .. stream
 }
 
 for _name, (_res, _args) in _SIGNATURES.items():
@@ -292,3 +299,55 @@ def smoe_combine(slot_out, topk_w, shared_out, shared_gate, y, stream=None) -> N
 def raw_library() -> ctypes.CDLL:
     """The loaded CDLL (for tests that call the C ABI directly)."""
     return _lib
+
+
+def smoe_moe_layer_w4a16(x, w_router, logit_bias, k: int, flags: int, topk_ids, topk_w, logits,
+                         shared_gate_w, shared_gate, expert_counts, expert_offsets, sorted_slots,
+                         active_experts, n_active, elb_counts, layer: int, M: int, plan_ids,
+                         plan_counts, elb_flags: int, I: int, group_size: int, wg_q, wg_s, wu_q,
+                         wu_s, wd_q, wd_s, workspace, slot_out, y, shared=None, shared_out=None,
+                         stream=None) -> None:
+    """The whole draft layer in one call: smoe_route_align_elb,
+    smoe_w4a16_expert_ffn and smoe_combine with the same arguments.
+    elb_counts [L][E] or None; shared: optional (wg, wu, wd) fp16 weights."""
+    T, H = x.shape
+    E = w_router.shape[0]
+    L = elb_counts.shape[0] if elb_counts is not None else 0
+    _route_sizes(T, H, E, k, w_router, logit_bias, topk_ids, topk_w, logits, shared_gate_w,
+                 shared_gate)
+    _align_sizes(T * k, E, expert_counts, expert_offsets, sorted_slots, active_experts, n_active)
+    _need(elb_counts, L * E, "elb_counts")
+    _need(plan_ids, L * M, "plan_ids")
+    _need(plan_counts, L * M, "plan_counts")
+    sI, sg, su, sd, so = _shared_args(shared, shared_out)
+    G = max(group_size, 1)
+    for name, t in (("wg_q", wg_q), ("wu_q", wu_q)):
+        _need(t, E * I * H // 8, name)
+    for name, t in (("wg_s", wg_s), ("wu_s", wu_s)):
+        _need(t, E * I * H // G, name)
+    _need(wd_q, E * H * I // 8, "wd_q")
+    _need(wd_s, E * H * I // G, "wd_s")
+    _ffn_sizes(T, k, E, H, sI, sorted_slots, expert_offsets, slot_out, shared, shared_out)
+    _need(y, T * H, "y")
+    _check("smoe_moe_layer_w4a16", _lib.smoe_moe_layer_w4a16(
+        _ptr(x, torch.float16, "x"), _ptr(w_router, torch.float32, "w_router"),
+        _ptr(logit_bias, torch.float32, "logit_bias"), T, H, E, k, flags,
+        _ptr(topk_ids, torch.int32, "topk_ids"), _ptr(topk_w, torch.float32, "topk_w"),
+        _ptr(logits, torch.float32, "logits"),
+        _ptr(shared_gate_w, torch.float32, "shared_gate_w"),
+        _ptr(shared_gate, torch.float32, "shared_gate"),
+        _ptr(expert_counts, torch.int32, "expert_counts"),
+        _ptr(expert_offsets, torch.int32, "expert_offsets"),
+        _ptr(sorted_slots, torch.int32, "sorted_slots"),
+        _ptr(active_experts, torch.int32, "active_experts"),
+        _ptr(n_active, torch.int32, "n_active"),
+        _ptr(elb_counts, torch.int32, "elb_counts"), L, layer, M,
+        _ptr(plan_ids, torch.int32, "plan_ids"), _ptr(plan_counts, torch.int32, "plan_counts"),
+        elb_flags, I, group_size,
+        _ptr(wg_q, torch.int32, "wg_q"), _ptr(wg_s, torch.float16, "wg_s"),
+        _ptr(wu_q, torch.int32, "wu_q"), _ptr(wu_s, torch.float16, "wu_s"),
+        _ptr(wd_q, torch.int32, "wd_q"), _ptr(wd_s, torch.float16, "wd_s"),
+        sI, sg, su, sd,
+        _ptr(workspace, torch.uint8, "workspace"), workspace.numel(),
+        _ptr(slot_out, torch.float32, "slot_out"), so, _ptr(y, torch.float16, "y"),
+        _stream(stream)))

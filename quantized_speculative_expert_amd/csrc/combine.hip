@@ -76,10 +76,9 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(
 
 using namespace smoe;
 
-extern "C" smoe_status smoe_combine(const float* slot_out, const float* topk_w, int T, int k,
-                                    int H, const float* shared_out, const float* shared_gate,
-                                    void* y, void* stream) {
-  clear_error();
+namespace smoe {
+smoe_status combine_check(const float* slot_out, const float* topk_w, int T, int k, int H,
+                          const float* shared_out, const float* shared_gate, const void* y) {
   SMOE_REQUIRE(T >= 0 && k > 0 && H > 0, SMOE_EINVAL,
                "combine: need T >= 0, k > 0, H > 0 (T=%d k=%d H=%d)", T, k, H);
   SMOE_REQUIRE(k <= kMaxK && H % 128 == 0, SMOE_EUNSUPPORTED,
@@ -90,6 +89,16 @@ extern "C" smoe_status smoe_combine(const float* slot_out, const float* topk_w, 
   SMOE_REQUIRE(slot_out && topk_w && y, SMOE_EINVAL, "combine: null pointer");
   SMOE_REQUIRE(aligned16(slot_out) && aligned16(y) && (!shared_out || aligned16(shared_out)),
                SMOE_EINVAL, "combine: slot_out, shared_out and y must be 16-byte aligned");
+  return SMOE_OK;
+}
+}  // namespace smoe
+
+extern "C" smoe_status smoe_combine(const float* slot_out, const float* topk_w, int T, int k,
+                                    int H, const float* shared_out, const float* shared_gate,
+                                    void* y, void* stream) {
+  clear_error();
+  const smoe_status st = combine_check(slot_out, topk_w, T, k, H, shared_out, shared_gate, y);
+  if (st != SMOE_OK || T == 0) return st;
   const long long threads = static_cast<long long>(T) * (H / 8);
   const int grid = static_cast<int>((threads + kCombineThreads - 1) / kCombineThreads);
   hipLaunchKernelGGL(combine_kernel, dim3(grid), dim3(kCombineThreads), 0, as_stream(stream),

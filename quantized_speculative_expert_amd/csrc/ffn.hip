@@ -91,7 +91,7 @@
 #include <atomic>
 #include <type_traits>
 
-#include "smoe_internal.hpp"
+#include "smoe_blocks.hpp"  // route_check (the layer call validates every step)
 
 namespace smoe {
 namespace {
@@ -1170,4 +1170,66 @@ extern "C" smoe_status smoe_fp16_expert_ffn(
   if (st != SMOE_OK) return st;
   hipStream_t s = as_stream(stream);
   return p.nc == 2 ? launch_ffn<kFp16, 128, 2>(p, s) : launch_ffn<kFp16, 128, 1>(p, s);
+}
+
+extern "C" smoe_status smoe_moe_layer_w4a16(
+    const void* x, const float* w_router, const float* logit_bias, int T, int H, int E, int k,
+    int flags, int32_t* topk_ids, float* topk_w, float* logits, const float* shared_gate_w,
+    float* shared_gate, int32_t* expert_counts, int32_t* expert_offsets, int32_t* sorted_slots,
+    int32_t* active_experts, int32_t* n_active, int32_t* elb_counts, int L, int layer, int M,
+    int32_t* plan_ids, int32_t* plan_counts, int elb_flags, int I, int group_size,
+    const uint32_t* wg_q, const void* wg_s, const uint32_t* wu_q, const void* wu_s,
+    const uint32_t* wd_q, const void* wd_s, int shared_I, const void* shared_wg,
+    const void* shared_wu, const void* shared_wd, void* workspace, size_t workspace_bytes_,
+    float* slot_out, float* shared_out, void* y, void* stream) {
+  clear_error();
+  const char* who = "moe_layer_w4a16";
+  // every step's checks before anything is enqueued
+  RouteArgs ra;
+  smoe_status st = route_check(x, w_router, logit_bias, T, H, E, k, flags, topk_ids, topk_w,
+                               logits, shared_gate_w, shared_gate, ra);
+  if (st != SMOE_OK) return st;
+  st = align_check(topk_ids, T, k, E, expert_counts, expert_offsets, sorted_slots,
+                   active_experts, n_active);
+  if (st != SMOE_OK) return st;
+  if (elb_counts != nullptr) {
+    st = elb_check(elb_counts, L, E, topk_ids, layer, 1, T, k, M, plan_ids, elb_flags);
+    if (st != SMOE_OK) return st;
+  }
+  SMOE_REQUIRE(group_size == 32 || group_size == 64 || group_size == 128, SMOE_EUNSUPPORTED,
+               "%s: group size must be 32, 64 or 128 (got %d)", who, group_size);
+  st = check_common(who, x, T, k, E, H, I, sorted_slots, expert_offsets, shared_I, shared_wg,
+                    shared_wu, shared_wd, workspace, workspace_bytes_, slot_out, shared_out);
+  if (st != SMOE_OK) return st;
+  const float* s_out = shared_I > 0 ? shared_out : nullptr;
+  st = combine_check(slot_out, topk_w, T, k, H, s_out, shared_gate, y);
+  if (st != SMOE_OK) return st;
+  if (T == 0) return SMOE_OK;
+  SMOE_REQUIRE(wg_q && wg_s && wu_q && wu_s && wd_q && wd_s, SMOE_EINVAL,
+               "%s: null weight pointer", who);
+  SMOE_REQUIRE(aligned16(wg_q) && aligned16(wu_q) && aligned16(wd_q), SMOE_EINVAL,
+               "%s: packed weights must be 16-byte aligned", who);
+  SMOE_REQUIRE(((reinterpret_cast<uintptr_t>(wg_s) | reinterpret_cast<uintptr_t>(wu_s) |
+                 reinterpret_cast<uintptr_t>(wd_s)) & 7u) == 0,
+               SMOE_EINVAL, "%s: scales must be 8-byte aligned", who);
+  GroupWeights r{};
+  r.fmt = kInt4;
+  r.wg = wg_q; r.wu = wu_q; r.wd = wd_q;
+  r.sg = wg_s; r.su = wu_s; r.sd = wd_s;
+  r.E = E; r.I = I; r.G = group_size;
+  StagePlans p;
+  st = build_plans(who, p, x, T, k, H, sorted_slots, expert_offsets, workspace, r, shared_I,
+                   shared_wg, shared_wu, shared_wd, slot_out, shared_out);
+  if (st != SMOE_OK) return st;
+  // (the steps' own checks pass again; they enqueue the launches)
+  st = smoe_route_align_elb(x, w_router, logit_bias, T, H, E, k, flags, topk_ids, topk_w,
+                            logits, shared_gate_w, shared_gate, expert_counts, expert_offsets,
+                            sorted_slots, active_experts, n_active, elb_counts, L, layer, M,
+                            plan_ids, plan_counts, elb_flags, stream);
+  if (st != SMOE_OK) return st;
+  st = smoe_w4a16_expert_ffn(x, T, k, E, H, I, group_size, wg_q, wg_s, wu_q, wu_s, wd_q, wd_s,
+                             sorted_slots, expert_offsets, shared_I, shared_wg, shared_wu,
+                             shared_wd, workspace, workspace_bytes_, slot_out, shared_out, stream);
+  if (st != SMOE_OK) return st;
+  return smoe_combine(slot_out, topk_w, T, k, H, s_out, shared_gate, y, stream);
 }

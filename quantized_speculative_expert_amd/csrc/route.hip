@@ -32,17 +32,6 @@ constexpr int kMaxTokTile = 4;              // tokens per logits workgroup
 constexpr int kSlice = 32;                  // row chunks of 64 held in registers (2048 h)
 constexpr int kTopkWaves = 4;               // tokens per top-k workgroup
 
-struct RouteArgs {
-  const _Float16* x;
-  const float* w;
-  const float* bias;
-  const float* gate_w;
-  int32_t* ids;
-  float* wout;
-  float* logits;
-  float* gate;                              // raw gate dot, then its sigmoid
-  int T, H, E, k, flags, tok_tile;
-};
 
 // Staged x of a token tile, transposed so that lane l finds its terms
 // h = 64c + l at consecutive c: xs[(t * 64 + l) * ncp + c], with the row
@@ -158,74 +147,12 @@ __global__ __launch_bounds__(kTopkWaves * kWave) void topk_kernel(RouteArgs a) {
     a.gate[t] = 1.0f / (1.0f + expf(-a.gate[t]));
 }
 
-// Top-k, alignment and the ELB update of one layer in one workgroup, for
-// windows of at most kFusedMaxSlots slots: wave w takes the top-k of tokens
-// w, w + 16, ... (the IDs also go to LDS), then align_block sorts the
-// slots from LDS, then elb_block updates the layer's counter row and ranks
-// every layer. The results equal those of the three separate kernels.
-constexpr int kFusedMaxSlots = 512;
-constexpr int kFusedMaxLogits = 4096;  // logits staged in LDS up to this many
-
-struct FusedArgs {
-  RouteArgs r;
-  int32_t* counts;
-  int32_t* offsets;
-  int32_t* sorted_slots;
-  int32_t* active;
-  int32_t* n_active;
-  int32_t* elb_counts;  // [L][E] or null (no ELB update)
-  int32_t* plan_ids;
-  int32_t* plan_counts;
-  int L, layer, M, elb_clear;
-};
-
+// Top-k, alignment and the ELB update of one layer in one workgroup of
+// kAlignThreads (smoe_blocks.hpp), for windows of at most kFusedMaxSlots
+// slots. The results equal those of the three separate kernels.
 __global__ __launch_bounds__(kAlignThreads) void topk_align_elb_kernel(FusedArgs f) {
-  __shared__ AlignSmem sm;
-  __shared__ int ids_lds[kFusedMaxSlots];
-  __shared__ int hist[kMaxE];
-  __shared__ int row[kMaxE];
-  __shared__ float lg_lds[kFusedMaxLogits];
-  const RouteArgs& a = f.r;
-  const int wave = threadIdx.x / kWave;
-  const int lane = threadIdx.x % kWave;
-  // the top-k's per-wave LDS words live in the alignment's scratch, which is
-  // not in use yet
-  static_assert(sizeof(sm.wave_cnt) + sizeof(sm.wave_base) >= kAlignWaves * kMaxE * 8,
-                "per-wave top-k keys fit the alignment scratch");
-  static_assert(sizeof(sm.exp_off) >= kAlignWaves * kMaxK * 4, "per-wave picks fit");
-  uint64_t* keys = reinterpret_cast<uint64_t*>(&sm.wave_cnt[0][0]) + wave * kMaxE;
-  int* sel = &sm.exp_off[0] + wave * kMaxK;
-  // all logits in one round trip when they fit, then the top-k from LDS
-  const int n_lg = a.T * a.E;
-  const bool lg_in_lds = n_lg <= kFusedMaxLogits;
-  if (lg_in_lds) {
-    for (int i = threadIdx.x; i < n_lg; i += kAlignThreads) lg_lds[i] = a.logits[i];
-    __syncthreads();
-  }
-  for (int t = wave; t < a.T; t += kAlignWaves) {
-    int id;
-    float w;
-    const float* lrow = (lg_in_lds ? lg_lds : a.logits) + static_cast<size_t>(t) * a.E;
-    wave_topk(lrow, a.E, a.k, a.flags, keys, sel, &id, &w);
-    if (lane < a.k) {
-      a.ids[static_cast<size_t>(t) * a.k + lane] = id;
-      a.wout[static_cast<size_t>(t) * a.k + lane] = w;
-      ids_lds[t * a.k + lane] = id;
-    }
-    if (a.gate != nullptr && a.gate_w != nullptr && lane == 0)
-      a.gate[t] = 1.0f / (1.0f + expf(-a.gate[t]));
-  }
-  __syncthreads();
-  const int S = a.T * a.k;
-  align_block(ids_lds, S, a.E, f.counts, f.offsets, f.sorted_slots, f.active, f.n_active, sm);
-  if (f.elb_counts == nullptr) return;
-  for (int l = 0; l < f.L; ++l) {
-    __syncthreads();
-    elb_block(f.elb_counts + static_cast<size_t>(l) * a.E, a.E, l == f.layer ? ids_lds : nullptr,
-              S, f.M, f.plan_ids + static_cast<size_t>(l) * f.M,
-              f.plan_counts != nullptr ? f.plan_counts + static_cast<size_t>(l) * f.M : nullptr,
-              f.elb_clear, hist, row);
-  }
+  __shared__ RouteBlockSmem<kAlignThreads> sm;
+  route_align_elb_block<kAlignThreads>(f, sm);
 }
 
 }  // namespace
@@ -234,7 +161,6 @@ __global__ __launch_bounds__(kAlignThreads) void topk_align_elb_kernel(FusedArgs
 using namespace smoe;
 
 namespace smoe {
-namespace {
 
 smoe_status route_check(const void* x, const float* w_router, const float* logit_bias, int T,
                         int H, int E, int k, int flags, int32_t* topk_ids, float* topk_w,
@@ -283,7 +209,6 @@ smoe_status launch_logits(const RouteArgs& a, hipStream_t st) {
   return check_launch("route_topk logits");
 }
 
-}  // namespace
 }  // namespace smoe
 
 extern "C" smoe_status smoe_route_topk(const void* x, const float* w_router,

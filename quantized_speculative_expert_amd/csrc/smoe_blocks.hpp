@@ -2,7 +2,8 @@
 // top-k of the router, the counting sort of slots by expert and the ELB
 // counter update with its top-M ranking. Each exists as a kernel of its own
 // (route.hip, align.hip, elb.hip) and, for short windows, all three run
-// back to back in one workgroup (route_align.hip).
+// back to back in one workgroup (route.hip); that block is written for any
+// workgroup size.
 #pragma once
 
 #include "smoe_internal.hpp"
@@ -98,14 +99,17 @@ __device__ __forceinline__ void wave_topk(const float* l, int E, int k, int flag
 constexpr int kAlignThreads = 1024;
 constexpr int kAlignWaves = kAlignThreads / kWave;
 
-struct alignas(16) AlignSmem {
-  int wave_cnt[kAlignWaves][kMaxE];   // pass 1 counts, then running counters
-  int wave_base[kAlignWaves][kMaxE];  // slots of expert e in earlier waves
+// LDS of align_block for a workgroup of NT threads.
+template <int NT>
+struct alignas(16) AlignSmemT {
+  int wave_cnt[NT / kWave][kMaxE];   // pass 1 counts, then running counters
+  int wave_base[NT / kWave][kMaxE];  // slots of expert e in earlier waves
   int exp_off[kMaxE + 1];
   int act_pos[kMaxE];
 };
+using AlignSmem = AlignSmemT<kAlignThreads>;
 
-// One workgroup of kAlignThreads: stable counting sort of the S slots by
+// One workgroup of NT threads: stable counting sort of the S slots by
 // expert. Each wave owns a contiguous run of slots and walks it 64 slots at
 // a time. Within a 64-slot chunk, the lanes holding the same expert are
 // found with eight ballots (one per bit of the expert ID), and a lane's
@@ -116,19 +120,22 @@ struct alignas(16) AlignSmem {
 //           offsets[e] + base[wave][e] + running[wave][e] + rank, which is
 //           its position in (expert, slot) order.
 // `ids` may point to global or LDS memory.
-__device__ __forceinline__ void align_block(const int32_t* ids, int S, int E, int32_t* counts,
-                                            int32_t* offsets, int32_t* sorted_slots,
-                                            int32_t* active, int32_t* n_active, AlignSmem& sm) {
+template <int NT>
+__device__ __forceinline__ void align_block_t(const int32_t* ids, int S, int E, int32_t* counts,
+                                              int32_t* offsets, int32_t* sorted_slots,
+                                              int32_t* active, int32_t* n_active,
+                                              AlignSmemT<NT>& sm) {
+  constexpr int kWaves = NT / kWave;
   const int wave = threadIdx.x / kWave;
   const int lane = threadIdx.x % kWave;
 
-  for (int i = threadIdx.x; i < kAlignWaves * kMaxE; i += kAlignThreads)
+  for (int i = threadIdx.x; i < kWaves * kMaxE; i += NT)
     (&sm.wave_cnt[0][0])[i] = 0;
   __syncthreads();
 
   // contiguous run of whole 64-slot chunks per wave
   const int nchunks = (S + kWave - 1) / kWave;
-  const int per_wave = (nchunks + kAlignWaves - 1) / kAlignWaves;
+  const int per_wave = (nchunks + kWaves - 1) / kWaves;
   const int c_begin = wave * per_wave;
   const int c_end = min(nchunks, c_begin + per_wave);
 
@@ -154,8 +161,8 @@ __device__ __forceinline__ void align_block(const int32_t* ids, int S, int E, in
   __syncthreads();
 
   // per expert: total, per-wave bases (only waves that own slots count)
-  const int busy_waves = per_wave > 0 ? min(kAlignWaves, (nchunks + per_wave - 1) / per_wave) : 0;
-  for (int e = threadIdx.x; e < E; e += kAlignThreads) {
+  const int busy_waves = per_wave > 0 ? min(kWaves, (nchunks + per_wave - 1) / per_wave) : 0;
+  for (int e = threadIdx.x; e < E; e += NT) {
     int run = 0;
     for (int w = 0; w < busy_waves; ++w) {
       sm.wave_base[w][e] = run;
@@ -202,14 +209,14 @@ __device__ __forceinline__ void align_block(const int32_t* ids, int S, int E, in
   }
   __syncthreads();
 
-  for (int e = threadIdx.x; e < E; e += kAlignThreads) {
+  for (int e = threadIdx.x; e < E; e += NT) {
     offsets[e] = sm.exp_off[e];
     active[e] = -1;
   }
   __syncthreads();
-  for (int e = threadIdx.x; e < E; e += kAlignThreads)
+  for (int e = threadIdx.x; e < E; e += NT)
     if (sm.act_pos[e] >= 0) active[sm.act_pos[e]] = e;
-  for (int p = sm.exp_off[E] + threadIdx.x; p < S; p += kAlignThreads) sorted_slots[p] = -1;
+  for (int p = sm.exp_off[E] + threadIdx.x; p < S; p += NT) sorted_slots[p] = -1;
 
   // pass 2: stable placement; wave_cnt becomes the running count per wave
   for (int i = lane; i < E; i += kWave) sm.wave_cnt[wave][i] = 0;
@@ -239,6 +246,12 @@ __device__ __forceinline__ void align_block(const int32_t* ids, int S, int E, in
     const int s = c * kWave + lane;
     place(c, s < S ? ids[s] : -1);
   }
+}
+
+__device__ __forceinline__ void align_block(const int32_t* ids, int S, int E, int32_t* counts,
+                                            int32_t* offsets, int32_t* sorted_slots,
+                                            int32_t* active, int32_t* n_active, AlignSmem& sm) {
+  align_block_t<kAlignThreads>(ids, S, E, counts, offsets, sorted_slots, active, n_active, sm);
 }
 
 // ------------------------------------------------------------------ ELB
@@ -291,6 +304,108 @@ __device__ __forceinline__ void elb_block(int32_t* crow, int E, const int32_t* l
   }
   if (clear) {
     for (int e = threadIdx.x; e < E; e += nt) crow[e] = 0;
+  }
+}
+
+
+// ------------------------------------------------------------------ routing
+
+struct RouteArgs {
+  const _Float16* x;
+  const float* w;
+  const float* bias;
+  const float* gate_w;
+  int32_t* ids;
+  float* wout;
+  float* logits;
+  float* gate;                              // raw gate dot, then its sigmoid
+  int T, H, E, k, flags, tok_tile;
+};
+
+// Top-k, alignment and the ELB update of one layer in one workgroup, for
+// windows of at most kFusedMaxSlots slots.
+constexpr int kFusedMaxSlots = 512;
+constexpr int kFusedMaxLogits = 4096;  // logits staged in LDS up to this many
+
+struct FusedArgs {
+  RouteArgs r;
+  int32_t* counts;
+  int32_t* offsets;
+  int32_t* sorted_slots;
+  int32_t* active;
+  int32_t* n_active;
+  int32_t* elb_counts;  // [L][E] or null (no ELB update)
+  int32_t* plan_ids;
+  int32_t* plan_counts;
+  int L, layer, M, elb_clear;
+};
+
+// Argument checks of smoe_route_topk (filling `a`), and the router-logits
+// launch (route.hip); the one-call layer (ffn.hip) checks with the former.
+smoe_status route_check(const void* x, const float* w_router, const float* logit_bias, int T,
+                        int H, int E, int k, int flags, int32_t* topk_ids, float* topk_w,
+                        float* logits, const float* shared_gate_w, float* shared_gate,
+                        RouteArgs& a);
+smoe_status launch_logits(const RouteArgs& a, hipStream_t st);
+
+template <int NT>
+struct alignas(16) RouteBlockSmem {
+  AlignSmemT<NT> al;
+  int ids[kFusedMaxSlots];
+  int hist[kMaxE];
+  int row[kMaxE];
+  float lg[kFusedMaxLogits];
+};
+
+// One workgroup of NT threads, after the router logits: wave w takes the
+// top-k of tokens w, w + NT/64, ... (the IDs also go to LDS), then
+// align_block_t sorts the slots from LDS, then elb_block updates the
+// layer's counter row and ranks every layer. The results equal those of the
+// three separate kernels.
+template <int NT>
+__device__ __forceinline__ void route_align_elb_block(const FusedArgs& f, RouteBlockSmem<NT>& sm) {
+  constexpr int kWaves = NT / kWave;
+  const RouteArgs& a = f.r;
+  const int wave = threadIdx.x / kWave;
+  const int lane = threadIdx.x % kWave;
+  // the top-k's per-wave LDS words live in the alignment's scratch, which is
+  // not in use yet
+  static_assert(sizeof(sm.al.wave_cnt) + sizeof(sm.al.wave_base) >= kWaves * kMaxE * 8,
+                "per-wave top-k keys fit the alignment scratch");
+  static_assert(sizeof(sm.al.exp_off) >= kWaves * kMaxK * 4, "per-wave picks fit");
+  uint64_t* keys = reinterpret_cast<uint64_t*>(&sm.al.wave_cnt[0][0]) + wave * kMaxE;
+  int* sel = &sm.al.exp_off[0] + wave * kMaxK;
+  // all logits in one round trip when they fit, then the top-k from LDS
+  const int n_lg = a.T * a.E;
+  const bool lg_in_lds = n_lg <= kFusedMaxLogits;
+  if (lg_in_lds) {
+    for (int i = threadIdx.x; i < n_lg; i += NT) sm.lg[i] = a.logits[i];
+    __syncthreads();
+  }
+  for (int t = wave; t < a.T; t += kWaves) {
+    int id;
+    float w;
+    const float* lrow = (lg_in_lds ? sm.lg : a.logits) + static_cast<size_t>(t) * a.E;
+    wave_topk(lrow, a.E, a.k, a.flags, keys, sel, &id, &w);
+    if (lane < a.k) {
+      a.ids[static_cast<size_t>(t) * a.k + lane] = id;
+      a.wout[static_cast<size_t>(t) * a.k + lane] = w;
+      sm.ids[t * a.k + lane] = id;
+    }
+    if (a.gate != nullptr && a.gate_w != nullptr && lane == 0)
+      a.gate[t] = 1.0f / (1.0f + expf(-a.gate[t]));
+  }
+  __syncthreads();
+  const int S = a.T * a.k;
+  align_block_t<NT>(sm.ids, S, a.E, f.counts, f.offsets, f.sorted_slots, f.active, f.n_active,
+                    sm.al);
+  if (f.elb_counts == nullptr) return;
+  for (int l = 0; l < f.L; ++l) {
+    __syncthreads();
+    elb_block(f.elb_counts + static_cast<size_t>(l) * a.E, a.E, l == f.layer ? sm.ids : nullptr,
+              S, f.M, f.plan_ids + static_cast<size_t>(l) * f.M,
+              f.plan_counts != nullptr ? f.plan_counts + static_cast<size_t>(l) * f.M : nullptr,
+              f.elb_clear, sm.hist, sm.row);
   }
 }
 

@@ -26,6 +26,8 @@ smoe_status check_launch(const char* what);
 smoe_status align_check(const int32_t* topk_ids, int T, int k, int E, const int32_t* expert_counts,
                         const int32_t* expert_offsets, const int32_t* sorted_slots,
                         const int32_t* active_experts, const int32_t* n_active);
+smoe_status combine_check(const float* slot_out, const float* topk_w, int T, int k, int H,
+                          const float* shared_out, const float* shared_gate, const void* y);
 smoe_status elb_check(const int32_t* elb_counts, int L, int E, const int32_t* topk_ids,
                       int layer_begin, int n_layers, int T, int k, int M, const int32_t* plan_ids,
                       int flags);

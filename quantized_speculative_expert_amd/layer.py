@@ -175,10 +175,32 @@ class DeviceLayer:
         _lib.smoe_combine(self.slot_out, self.topk_w, self.shared_out, self.shared_gate,
                           self.y, stream=stream)
 
+    def layer_call(self, elb: bool = True, layer: int = 0, stream=None) -> None:
+        """The whole draft layer as one library call (smoe_moe_layer_w4a16),
+        which checks every step's arguments before it enqueues anything."""
+        c = self.cfg
+        M = c.elb_M if elb else 0
+        shared = shared_out = None
+        if self.shared_out is not None:
+            shared = (self.sg16, self.su16, self.sd16)
+            shared_out = self.shared_out
+        _lib.smoe_moe_layer_w4a16(
+            self.x, self.w_router, self.router_bias, c.k, 0, self.topk_ids, self.topk_w,
+            self.logits, self.shared_gate_w, self.shared_gate, self.counts, self.offsets,
+            self.sorted_slots, self.active, self.n_active,
+            self.elb_counts if elb else None, layer, M,
+            self.plan_ids if M > 0 else None, self.plan_counts if M > 0 else None, 0,
+            c.I, c.G, self.wg_q, self.wg_s, self.wu_q, self.wu_s, self.wd_q, self.wd_s,
+            self.workspace, self.slot_out, self.y, shared=shared, shared_out=shared_out,
+            stream=stream)
+
     # ---------------------------------------------------------------- whole layer
     def run(self, target: bool = False, elb: bool = True, fuse_shared: bool = True,
-            fuse_routing: bool = True, side_stream=None) -> None:
+            fuse_routing: bool = True, side_stream=None, one_call: bool = False) -> None:
         """Enqueue the whole layer on the current stream.
+
+        one_call runs the draft layer as the single library call
+        smoe_moe_layer_w4a16 (shared experts fused, no side stream).
 
         fuse_routing makes routing, alignment and the ELB update one call
         (smoe_route_align_elb); otherwise they are three. fuse_shared runs
@@ -192,6 +214,11 @@ class DeviceLayer:
         """
         separate = not fuse_shared and self.shared_out is not None
         use_elb = elb and self.cfg.elb_M > 0 and not target
+        if one_call:
+            if target or separate or side_stream is not None:
+                raise ValueError("one_call covers the draft layer with fused shared experts")
+            self.layer_call(elb=use_elb)
+            return
         main = torch.cuda.current_stream(self.device)
         side = side_stream
 

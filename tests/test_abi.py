@@ -51,7 +51,7 @@ def test_binding_signatures_cover_header():
 
 
 def test_status_strings(lib):
-    assert lib.smoe_abi_version() == 2
+    assert lib.smoe_abi_version() == 3
     assert lib.smoe_status_string(0) == b"SMOE_OK"
     assert b"EINVAL" in lib.smoe_status_string(EINVAL)
     assert b"EUNSUPPORTED" in lib.smoe_status_string(EUNSUPPORTED)

@@ -627,15 +627,18 @@ def test_empty_window_is_a_noop(smoe):
 
 @pytest.mark.parametrize("name", ["tiny", "dsv2", "qwen", "dsv2_t1"])
 @pytest.mark.parametrize("mode", ["fused", "fused-side", "separate", "separate-side",
-                                  "three-routing-calls"])
+                                  "three-routing-calls", "one-call"])
 def test_layer_draft_matches_oracle(smoe, name, mode):
     from quantized_speculative_expert_amd.layer import DeviceLayer
     L = layer(name)
     ref = oracle.moe_layer(L, "draft")
     d = DeviceLayer(L)
-    d.run(fuse_shared=not mode.startswith("separate"),
-          fuse_routing=mode != "three-routing-calls",
-          side_stream=torch.cuda.Stream() if mode.endswith("side") else None)
+    if mode == "one-call":
+        d.run(one_call=True)
+    else:
+        d.run(fuse_shared=not mode.startswith("separate"),
+              fuse_routing=mode != "three-routing-calls",
+              side_stream=torch.cuda.Stream() if mode.endswith("side") else None)
     assert np.array_equal(host(d.topk_ids), ref["ids"])
     assert np.array_equal(host(d.sorted_slots), ref["sorted_slots"])
     assert int(host(d.n_active)[0]) == int(ref["n_active"])
@@ -694,12 +697,13 @@ def test_batch_layer_full_size_sampled(smoe):
     assert np.array_equal(host(d.plan_ids), pid) and np.array_equal(host(d.plan_counts), pc)
 
 
-@pytest.mark.parametrize("fused", [True, False])
+@pytest.mark.parametrize("fused", [True, False, "one-call"])
 def test_layer_graph_replay_matches_eager(smoe, fused):
     from quantized_speculative_expert_amd.layer import DeviceLayer
     L = layer("dsv2")
     d = DeviceLayer(L)
-    d.run(elb=False, fuse_shared=fused)
+    one = fused == "one-call"
+    d.run(elb=False, fuse_shared=bool(fused), one_call=one)
     eager = host(d.y).copy()
     side = torch.cuda.Stream()
     g = torch.cuda.CUDAGraph()
@@ -707,8 +711,10 @@ def test_layer_graph_replay_matches_eager(smoe, fused):
     s.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(s):
         with torch.cuda.graph(g, stream=s):
-            # the ELB update runs on the side branch of the graph
-            d.run(elb=True, fuse_shared=fused, side_stream=side)
+            # the ELB update runs on the side branch of the graph (or in line,
+            # in one call)
+            d.run(elb=True, fuse_shared=bool(fused), side_stream=None if one else side,
+                  one_call=one)
     torch.cuda.current_stream().wait_stream(s)
     ids_eager = host(d.topk_ids).copy()
     once = np.bincount(ids_eager.ravel(), minlength=L.cfg.E)
@@ -724,3 +730,72 @@ def test_layer_graph_replay_matches_eager(smoe, fused):
         # split-K tiles add fp32 partial sums with device atomics, so the
         # float output may differ from the eager run in the last bits
         assert row_rel_err(host(d.y), eager) <= 1e-3
+
+
+def _layer_outputs(d):
+    return dict(ids=host(d.topk_ids).copy(), w=host(d.topk_w).copy(), lg=host(d.logits).copy(),
+                counts=host(d.counts).copy(), offsets=host(d.offsets).copy(),
+                slots=host(d.sorted_slots).copy(), active=host(d.active).copy(),
+                n_active=host(d.n_active).copy(), elb=host(d.elb_counts).copy(),
+                plan=host(d.plan_ids).copy(), plan_c=host(d.plan_counts).copy(),
+                y=host(d.y).astype(np.float64))
+
+
+@pytest.mark.parametrize("name", ["tiny", "dsv2", "qwen", "phi", "dsv2_t1"])
+def test_layer_one_call_equals_separate_calls(smoe, name):
+    # the one-call layer against the separate calls on the device: integer
+    # results bit for bit, y up to the order of the split-K float atomics
+    from quantized_speculative_expert_amd.layer import DeviceLayer
+    L = layer(name)
+    d = DeviceLayer(L)
+    d.run()
+    sep = _layer_outputs(d)
+    d.elb_counts.zero_()
+    for t in (d.topk_ids, d.counts, d.offsets, d.sorted_slots, d.active, d.n_active,
+              d.plan_ids, d.plan_counts):
+        t.fill_(-3)
+    d.y.zero_()
+    d.run(one_call=True)
+    one = _layer_outputs(d)
+    keys = ["ids", "lg", "counts", "offsets", "slots", "active", "n_active"]
+    if L.cfg.elb_M > 0:  # (no ELB plan without M)
+        keys += ["elb", "plan", "plan_c"]
+    for key in keys:
+        assert np.array_equal(one[key], sep[key]), key
+    assert np.array_equal(one["w"], sep["w"])
+    assert row_rel_err(one["y"], sep["y"]) <= 1e-3
+
+
+def test_layer_one_call_interleaved_with_other_calls(smoe):
+    # one-call layers mixed with separate-call layers on one FFN workspace
+    # (whose call counter every FFN call advances) all match the oracle
+    from quantized_speculative_expert_amd.layer import DeviceLayer
+    L = layer("dsv2")
+    ref = oracle.moe_layer(L, "draft")
+    d = DeviceLayer(L)
+    for one in (True, False, True, True, False, False, True):
+        d.topk_ids.fill_(-1)
+        d.sorted_slots.fill_(-1)
+        d.y.zero_()
+        d.run(elb=False, one_call=one)
+        assert np.array_equal(host(d.topk_ids), ref["ids"]), one
+        assert np.array_equal(host(d.sorted_slots), ref["sorted_slots"]), one
+        assert row_rel_err(host(d.y), ref["y64"]) <= ROW_TOL, one
+
+
+def test_layer_one_call_batch_window(smoe):
+    # 544 tokens x top-6 = 3264 slots, above the one-workgroup routing
+    # limit (the routing takes its three separate launches inside the call)
+    from quantized_speculative_expert_amd.layer import DeviceLayer
+    L = layer("batch", layer_idx=1)
+    d = DeviceLayer(L, elb_layers=L.cfg.layers)
+    d.run()
+    sep = _layer_outputs(d)
+    d.elb_counts.zero_()
+    d.topk_ids.fill_(-1)
+    d.sorted_slots.fill_(-1)
+    d.run(one_call=True)
+    one = _layer_outputs(d)
+    for key in ("ids", "slots", "offsets", "elb", "plan"):
+        assert np.array_equal(one[key], sep[key]), key
+    assert row_rel_err(one["y"], sep["y"]) <= 1e-3
