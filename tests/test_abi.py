@@ -208,3 +208,43 @@ def test_binding_refuses_short_tensors(lib):
     with pytest.raises(ValueError, match="y holds"):
         smoe.smoe_combine(torch.zeros(T * k * H, **f32), torch.zeros((T, k), **f32), None, None,
                           torch.zeros((T - 1, H), **f16))
+
+
+def test_layer_call_argument_checks(lib):
+    # every step's checks run before anything is enqueued, with the errors
+    # the separate calls give
+    f = lib.smoe_moe_layer_w4a16
+    f.argtypes = ([ctypes.c_void_p] * 3 + [ctypes.c_int] * 5 + [ctypes.c_void_p] * 11 +
+                  [ctypes.c_int] * 3 + [ctypes.c_void_p] * 2 + [ctypes.c_int] * 3 +
+                  [ctypes.c_void_p] * 6 + [ctypes.c_int] + [ctypes.c_void_p] * 4 +
+                  [ctypes.c_size_t] + [ctypes.c_void_p] * 4)
+    r = [16, 16, N]                      # x, w_router, bias
+    o = [16, 16, 16, N, N]               # ids, weights, logits, gate_w, gate
+    al = [16, 16, 16, 16, 16]            # counts, offsets, sorted, active, n_active
+    elb = [N, 0, 0, 0, N, N, 0]          # no activation counter
+    w = [16] * 6                         # routed codes and scales
+    ns = [0, N, N, N]                    # no shared expert
+    ws = 1 << 30
+
+    def call(T=17, H=2048, E=64, k=6, I=1408, G=128, x=16, route=None, align=None, elb_=None,
+             weights=None, shared=None, wsp=256, wsb=ws, slot_out=16, shared_out=N, y=16):
+        return f(x, *r[1:], T, H, E, k, 0, *(route or o), *(align or al), *(elb_ or elb), I, G,
+                 *(weights or w), *(shared or ns), wsp, wsb, slot_out, shared_out, y, N)
+
+    assert call(E=300) == EUNSUPPORTED                                  # routing limits
+    assert b"route_topk" in lib.smoe_last_error()
+    assert call(align=[16, N, 16, 16, 16]) == EINVAL                    # align outputs
+    assert b"align_by_expert" in lib.smoe_last_error()
+    assert call(elb_=[16, 1, 1, 0, N, N, 0]) == EINVAL                  # layer >= L
+    assert b"elb_accumulate_topm" in lib.smoe_last_error()
+    assert call(G=96) == EUNSUPPORTED                                   # group size
+    assert call(I=1400) == EUNSUPPORTED                                 # FFN limits
+    assert call(wsb=10) == EINVAL                                       # workspace size
+    assert b"workspace" in lib.smoe_last_error()
+    assert call(shared=[2816, 16, 16, 16]) == EINVAL                    # no shared_out
+    assert call(route=[16, 16, 16, 16, 16]) == EINVAL                   # gate without shared
+    assert b"combine" in lib.smoe_last_error()
+    assert call(y=N) == EINVAL                                          # combine output
+    assert call(weights=[16, 16, N, 16, 16, 16]) == EINVAL              # null weight
+    assert b"weight" in lib.smoe_last_error()
+    assert call(T=0, x=N) == 0                                          # empty window
