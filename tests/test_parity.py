@@ -160,6 +160,24 @@ def test_route_single_token_and_large_E(smoe):
     assert np.array_equal(ids, oracle.topk_experts(ref_lg, 8))
 
 
+@pytest.mark.parametrize("T", [1, 17, 29, 57, 64, 85, 100, 113, 150])
+def test_route_token_tiles(smoe, T):
+    # the logits kernel's token tile follows the window (one token per
+    # workgroup at short windows, up to four at long ones): T = 57..113 at
+    # 64 experts and a gate row gives tiles of 2 and 3 with ragged last
+    # tiles; the logits stay bit-identical to the oracle's fixed order
+    rng = np.random.default_rng(100 + T)
+    x = rng.standard_normal((T, 2048)).astype(np.float16)
+    w = (rng.standard_normal((64, 2048)) * 0.02).astype(np.float32)
+    gw = (rng.standard_normal(2048) * 0.02).astype(np.float32)
+    ids, wt, lg, gate = run_route(smoe, x, w, None, 6, gate_w=gw)
+    ref_lg = oracle.router_logits_f32(x, w)
+    assert np.array_equal(lg.view(np.uint32), ref_lg.view(np.uint32))
+    assert np.array_equal(ids, oracle.topk_experts(ref_lg, 6))
+    ref_gate = oracle.shared_gate(x, gw)
+    assert np.allclose(gate, ref_gate, rtol=1e-5, atol=1e-7)
+
+
 # ------------------------------------------------------------------ fused routing call
 
 def _routing_buffers(T, k, E, gated, L, M):
