@@ -210,6 +210,8 @@ smoe_status route_check(const void* x, const float* w_router, const float* logit
   return SMOE_OK;
 }
 
+namespace {
+
 smoe_status launch_logits(const RouteArgs& a, hipStream_t st) {
   const int nrows = a.E + (a.gate_w != nullptr ? 1 : 0);
   const dim3 grid((nrows + kRowsPerWg - 1) / kRowsPerWg, (a.T + a.tok_tile - 1) / a.tok_tile);
@@ -218,6 +220,7 @@ smoe_status launch_logits(const RouteArgs& a, hipStream_t st) {
   return check_launch("route_topk logits");
 }
 
+}  // namespace
 }  // namespace smoe
 
 extern "C" smoe_status smoe_route_topk(const void* x, const float* w_router,

@@ -340,13 +340,12 @@ struct FusedArgs {
   int L, layer, M, elb_clear;
 };
 
-// Argument checks of smoe_route_topk (filling `a`), and the router-logits
-// launch (route.hip); the one-call layer (ffn.hip) checks with the former.
+// Argument checks of smoe_route_topk, filling `a` (route.hip); the one-call
+// layer (ffn.hip) runs them before it enqueues anything.
 smoe_status route_check(const void* x, const float* w_router, const float* logit_bias, int T,
                         int H, int E, int k, int flags, int32_t* topk_ids, float* topk_w,
                         float* logits, const float* shared_gate_w, float* shared_gate,
                         RouteArgs& a);
-smoe_status launch_logits(const RouteArgs& a, hipStream_t st);
 
 template <int NT>
 struct alignas(16) RouteBlockSmem {
