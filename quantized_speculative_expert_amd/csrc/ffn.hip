@@ -131,6 +131,10 @@ constexpr int phase_k(int stage) { return stage_d(stage) * 128; }
 #define SMOE_FFN_MAX_WG 512
 #endif
 constexpr int kMaxWg = SMOE_FFN_MAX_WG;    // persistent grid cap
+#ifndef SMOE_FFN_EXACT_SMALL
+#define SMOE_FFN_EXACT_SMALL 1
+#endif
+constexpr bool kExactSmall = SMOE_FFN_EXACT_SMALL != 0;
 
 // A set of experts that share a weight format and shapes: the routed
 // experts (group 0) or the shared expert (group 1, FP16).
@@ -317,10 +321,25 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
   // together.
   const int nwg = gridDim.x;
   int q0 = static_cast<int>(static_cast<long long>(n_items) * kStaticPermille / 1000 / nwg);
-  if (q0 < 2) q0 = 0;
-  const int s0 = b * q0;
-  const int dyn_base = nwg * q0;
+  int s0, dyn_base;
+  if (q0 >= 2) {
+    s0 = b * q0;
+    dyn_base = nwg * q0;
+  } else if (kExactSmall) {
+    // A short list (under about two items per workgroup, as for a single
+    // token): every item static, consecutive runs of n / nwg or one more, so
+    // that no workgroup waits on a ticket before its first weight loads.
+    const int base_q = n_items / nwg, extra = n_items - base_q * nwg;
+    q0 = base_q + (b < extra ? 1 : 0);
+    s0 = b * base_q + min(b, extra);
+    dyn_base = n_items;
+  } else {
+    q0 = 0;
+    s0 = 0;
+    dyn_base = 0;
+  }
   const int n_units = (n_items - dyn_base + kUnit - 1) / kUnit;
+  const bool tickets = n_units > 0;
   const int pool = b & (kPools - 1);
   int* ctr = a.hdr + (STAGE == 1 ? kHdrCtr1 : kHdrCtr2) + pool;
   // first item of the unit of ticket t (-1: no such unit)
@@ -333,7 +352,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
   int cur, nxt;
   if (q0 > 0) {
     cur = s0;
-    nxt = s0 + 1;
+    nxt = q0 > 1 ? s0 + 1 : -1;
+  } else if (!tickets) {  // no items at all
+    cur = nxt = -1;
   } else {  // no static run: tickets for positions 0 and 1 now
     if (tid == 0)
       s_tk[0] = __hip_atomic_fetch_add(ctr, kUnit > 1 ? 1 : 2, __ATOMIC_RELAXED,
@@ -770,7 +791,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
 
     // position pos + 2 starts a unit: take its ticket now
     const int r = pos + 2 - q0;
-    const bool grab = r >= 0 && r % kUnit == 0 && nxt >= 0;
+    const bool grab = tickets && r >= 0 && r % kUnit == 0 && nxt >= 0;
     int tk_new = 0;
     if (grab && tid == 0) {
       // the address goes through a VGPR so the compiler issues the plain
@@ -829,9 +850,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
     if (r < 0)
       nn = s0 + pos + 2;
     else if (r % kUnit != 0)
-      nn = next_in_unit(nxt);
+      nn = tickets ? next_in_unit(nxt) : -1;
     else
-      nn = uniform(unit_item(s_tk[(r / kUnit) & 1]));
+      nn = tickets ? uniform(unit_item(s_tk[(r / kUnit) & 1])) : -1;
     prev = cur;
     cur = nxt;
     nxt = nn;
