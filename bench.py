@@ -306,8 +306,8 @@ def main() -> int:
     args = parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print("bench.py measures one GPU only: the layer runs on a single MI355X and this "
-              f"build has no multi-GPU path (asked for --gpus {args.gpus}, WORLD_SIZE {world})",
+        print("bench.py measures one GPU only: the layer runs on a single MI355X and libsmoe "
+              f"has no multi-GPU path (asked for --gpus {args.gpus}, WORLD_SIZE {world})",
               file=sys.stderr)
         return 2
 

@@ -26,7 +26,7 @@ HIPCC_FLAGS = [
     "-std=c++17",
     "-fPIC",
     "-fno-gpu-rdc",
-    # packed fp32 VALU ops stay off (never emitted by this build)
+    # packed fp32 VALU ops stay off (these flags never emit them)
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     f"-I{INCLUDE}",
     f"-I{CSRC}",
