@@ -62,6 +62,9 @@ def parse_args():
     p.add_argument("--layer", choices=("one-call", "calls"), default="calls",
                    help="the layer step as one library call (smoe_moe_layer_w4a16) or as "
                         "the separate calls")
+    p.add_argument("--layout", choices=("tiled", "rows"), default="tiled",
+                   help="expert weights in the tiled layout of smoe_tile_weights, tiled once "
+                        "before timing (default), or row-major")
     p.add_argument("--side-stream", action="store_true",
                    help="run the ELB update (and a separate shared-expert call) on a side "
                         "stream branch of the step graph instead of in line")
@@ -137,11 +140,12 @@ def source_digest() -> str:
     return h.hexdigest()[:16]
 
 
-def recorded_traffic(config: str, shared_mode: str):
+def recorded_traffic(config: str, shared_mode: str, layout: str):
     """HBM bytes per FFN call from the committed rocprofv3 counter summary.
 
-    Returns None when no summary exists for this workload and shared-expert
-    mode, or when the kernel sources changed since the counters were taken.
+    Returns None when no summary exists for this workload, shared-expert mode
+    and weight layout, or when the kernel sources changed since the counters
+    were taken.
     """
     path = os.path.join(PROFILES, f"w4a16_expert_ffn_{config}_traffic.md")
     if not os.path.exists(path):
@@ -150,7 +154,8 @@ def recorded_traffic(config: str, shared_mode: str):
     if not m:
         return None
     rec = json.loads(m.group(1))
-    if rec.get("source_digest") != source_digest() or rec.get("shared") != shared_mode:
+    if (rec.get("source_digest") != source_digest() or rec.get("shared") != shared_mode
+            or rec.get("layout", "rows") != layout):
         return None
     return rec.get("bytes_per_call")
 
@@ -248,9 +253,9 @@ def compare_ffn(base, layers, fused: bool, stream, batched_us: float) -> dict:
     def per_expert(d):
         for e, o in zip(act, offs):
             sl = slice(e, e + 1)
-            _lib.smoe_w4a16_expert_ffn(d.x, c.k, 1, c.I, c.G, d.wg_q[sl], d.wg_s[sl],
-                                       d.wu_q[sl], d.wu_s[sl], d.wd_q[sl], d.wd_s[sl],
-                                       d.sorted_slots, o, ws, d.slot_out)
+            d._call("smoe_w4a16_expert_ffn")(d.x, c.k, 1, c.I, c.G, d.wg_q[sl], d.wg_s[sl],
+                                             d.wu_q[sl], d.wu_s[sl], d.wd_q[sl], d.wd_s[sl],
+                                             d.sorted_slots, o, ws, d.slot_out)
         if fused:
             d.shared_ffn()
 
@@ -328,7 +333,8 @@ def main() -> int:
     inp = make_layer(cfg, seed=0, layer=0, want_fp16=args.compare)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    base = DeviceLayer(inp, device=dev, with_target=args.compare, elb_layers=cfg.layers)
+    base = DeviceLayer(inp, device=dev, with_target=args.compare, elb_layers=cfg.layers,
+                       tiled=args.layout == "tiled")
     del inp
     # rotation sized on the draft path's weights (the FP16 routed copies that
     # --compare adds are read only by the comparison)
@@ -417,7 +423,7 @@ def main() -> int:
     ffn_stats = percentiles(ffn_us)
     fb = ffn_bytes(base, n_active, fused)
     achieved = fb / (ffn_stats["mean"] * 1e3)  # bytes/ns = GB/s
-    traffic = recorded_traffic(cfg.name, args.shared)
+    traffic = recorded_traffic(cfg.name, args.shared, args.layout)
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBPS,
                 "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBPS, 4),
                 "traffic": traffic,
@@ -475,6 +481,7 @@ def main() -> int:
             "shared_experts": args.shared,
             "side_stream": side is not None,
             "layer_call": args.layer,
+            "weight_layout": args.layout,
         },
         "hbm_gbps": round(layer_gbps, 1),
         "hbm_frac": round(layer_gbps / PEAK_HBM_GBPS, 4),

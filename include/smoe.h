@@ -317,6 +317,84 @@ smoe_status smoe_moe_layer_w4a16(const void* x, const float* w_router, const flo
                                  const void* shared_wd, void* workspace, size_t workspace_bytes,
                                  float* slot_out, float* shared_out, void* y, void* stream);
 
+/*
+ * Tiled weight layout.  [P] fused multi-expert draft kernel paragraph (INT4
+ * weight tiles streamed per expert); [D] "Streamlined Execution Engine"
+ * (W4A16 dequantisation of weight tiles). The pages fix no memory layout;
+ * this one is the expert FFN's own: the same bytes as the row-major
+ * layout, ordered so that every load of the FFN reads one contiguous
+ * kilobyte (and the scales of a row slice and block of k one contiguous
+ * run). Weights are tiled once, when loaded; the *_tiled calls below then
+ * stream them.
+ *
+ * For one [E][N][K] weight tensor (row n of expert e holds the K
+ * reduction values of output n):
+ *   group_size 0:   w fp16 [E][N][K], scales ignored (NULL);
+ *   group_size G:   w uint32 [E][N][K/8] INT4 codes (the packed format of
+ *                   smoe_w4a16_expert_ffn), scales fp16 [E][N][K/G].
+ * Output, for each expert e, row slice sl = n / 16 (slices in order) and
+ * block b of 64 bytes of a row (blocks in order within a slice): 1 KB
+ * where bytes 16 (16 g + r) .. +15 hold four 32-bit words of row
+ * 16 sl + r, block b: words 4 g + q (q = 0..3) for FP16 and G = 128;
+ * words (q / (G/32)) (G/8) + g (G/32) + q % (G/32) for G = 64 and 32.
+ * Scales, for each (e, sl, b): 16 runs (r = 0..15) of 128 / G values, the
+ * scales of row 16 sl + r in block b, in k order.
+ *
+ *   N a multiple of 16, K of 128; w_tiled (and scales_tiled) the sizes of
+ *   w (and scales), caller-owned device memory, 16-byte aligned, not
+ *   overlapping the inputs.
+ * SMOE_EINVAL for null, misaligned or overlapping buffers,
+ * SMOE_EUNSUPPORTED for other shapes or group sizes. Asynchronous on
+ * `stream`; E = 0 or N = 0 enqueues nothing.
+ */
+smoe_status smoe_tile_weights(const void* w, const void* scales, int E, int N, int K,
+                              int group_size, void* w_tiled, void* scales_tiled, void* stream);
+
+/*
+ * smoe_w4a16_expert_ffn, smoe_fp16_expert_ffn and smoe_moe_layer_w4a16
+ * with every weight tensor passed (routed codes and scales, and the shared
+ * FP16 weights) in the tiled layout of smoe_tile_weights, each tiled as
+ * the [E][N][K] tensor its row-major form is. Arguments, results, checks
+ * and errors are otherwise those of the row-major calls.
+ */
+smoe_status smoe_w4a16_expert_ffn_tiled(const void* x, int T, int k, int E, int H, int I,
+                                        int group_size,
+                                        const uint32_t* wg_q, const void* wg_s,
+                                        const uint32_t* wu_q, const void* wu_s,
+                                        const uint32_t* wd_q, const void* wd_s,
+                                        const int32_t* sorted_slots,
+                                        const int32_t* expert_offsets,
+                                        int shared_I, const void* shared_wg,
+                                        const void* shared_wu, const void* shared_wd,
+                                        void* workspace, size_t workspace_bytes,
+                                        float* slot_out, float* shared_out, void* stream);
+smoe_status smoe_fp16_expert_ffn_tiled(const void* x, int T, int k, int E, int H, int I,
+                                       const void* wg, const void* wu, const void* wd,
+                                       const int32_t* sorted_slots,
+                                       const int32_t* expert_offsets,
+                                       int shared_I, const void* shared_wg,
+                                       const void* shared_wu, const void* shared_wd,
+                                       void* workspace, size_t workspace_bytes,
+                                       float* slot_out, float* shared_out, void* stream);
+smoe_status smoe_moe_layer_w4a16_tiled(const void* x, const float* w_router,
+                                       const float* logit_bias, int T, int H, int E, int k,
+                                       int flags, int32_t* topk_ids, float* topk_w,
+                                       float* logits, const float* shared_gate_w,
+                                       float* shared_gate, int32_t* expert_counts,
+                                       int32_t* expert_offsets, int32_t* sorted_slots,
+                                       int32_t* active_experts, int32_t* n_active,
+                                       int32_t* elb_counts, int L, int layer, int M,
+                                       int32_t* plan_ids, int32_t* plan_counts, int elb_flags,
+                                       int I, int group_size,
+                                       const uint32_t* wg_q, const void* wg_s,
+                                       const uint32_t* wu_q, const void* wu_s,
+                                       const uint32_t* wd_q, const void* wd_s,
+                                       int shared_I, const void* shared_wg,
+                                       const void* shared_wu, const void* shared_wd,
+                                       void* workspace, size_t workspace_bytes,
+                                       float* slot_out, float* shared_out, void* y,
+                                       void* stream);
+
 #ifdef __cplusplus
 }
 #endif

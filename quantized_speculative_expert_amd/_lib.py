@@ -51,7 +51,11 @@ _SIGNATURES = {
                                   _i, _i, _p, _p, _p, _p, _p, _p,      # I, G, routed weights
                                   _i, _p, _p, _p,                      # shared_I, shared weights
                                   _p, _sz, _p, _p, _p, _p]),           # workspace .. stream
+    "smoe_tile_weights": (_i, [_p, _p, _i, _i, _i, _i, _p, _p, _p]),
 }
+# the tiled-layout calls take the same arguments as their row-major forms
+for _name in ("smoe_w4a16_expert_ffn", "smoe_fp16_expert_ffn", "smoe_moe_layer_w4a16"):
+    _SIGNATURES[_name + "_tiled"] = _SIGNATURES[_name]
 
 for _name, (_res, _args) in _SIGNATURES.items():
     _fn = getattr(_lib, _name)
@@ -241,8 +245,9 @@ def _ffn_sizes(T, k, E, H, sI, sorted_slots, expert_offsets, slot_out, shared, s
 
 def smoe_w4a16_expert_ffn(x, k: int, E: int, I: int, group_size: int, wg_q, wg_s, wu_q, wu_s,
                           wd_q, wd_s, sorted_slots, expert_offsets, workspace, slot_out,
-                          shared=None, shared_out=None, stream=None) -> None:
+                          shared=None, shared_out=None, stream=None, *, _fn="") -> None:
     """shared: optional (wg, wu, wd) fp16 weights of the always-on shared expert."""
+    fname = _fn or "smoe_w4a16_expert_ffn"
     T, H = x.shape
     sI, sg, su, sd, so = _shared_args(shared, shared_out)
     G = max(group_size, 1)
@@ -253,7 +258,7 @@ def smoe_w4a16_expert_ffn(x, k: int, E: int, I: int, group_size: int, wg_q, wg_s
     _need(wd_q, E * H * I // 8, "wd_q")
     _need(wd_s, E * H * I // G, "wd_s")
     _ffn_sizes(T, k, E, H, sI, sorted_slots, expert_offsets, slot_out, shared, shared_out)
-    _check("smoe_w4a16_expert_ffn", _lib.smoe_w4a16_expert_ffn(
+    _check(fname, getattr(_lib, fname)(
         _ptr(x, torch.float16, "x"), T, k, E, H, I, group_size,
         _ptr(wg_q, torch.int32, "wg_q"), _ptr(wg_s, torch.float16, "wg_s"),
         _ptr(wu_q, torch.int32, "wu_q"), _ptr(wu_s, torch.float16, "wu_s"),
@@ -265,14 +270,16 @@ def smoe_w4a16_expert_ffn(x, k: int, E: int, I: int, group_size: int, wg_q, wg_s
 
 
 def smoe_fp16_expert_ffn(x, k: int, E: int, I: int, wg, wu, wd, sorted_slots, expert_offsets,
-                         workspace, slot_out, shared=None, shared_out=None, stream=None) -> None:
+                         workspace, slot_out, shared=None, shared_out=None, stream=None, *,
+                         _fn="") -> None:
     """shared: optional (wg, wu, wd) fp16 weights of the always-on shared expert."""
+    fname = _fn or "smoe_fp16_expert_ffn"
     T, H = x.shape
     sI, sg, su, sd, so = _shared_args(shared, shared_out)
     for name, t in (("wg", wg), ("wu", wu), ("wd", wd)):
         _need(t, E * I * H, name)
     _ffn_sizes(T, k, E, H, sI, sorted_slots, expert_offsets, slot_out, shared, shared_out)
-    _check("smoe_fp16_expert_ffn", _lib.smoe_fp16_expert_ffn(
+    _check(fname, getattr(_lib, fname)(
         _ptr(x, torch.float16, "x"), T, k, E, H, I,
         _ptr(wg, torch.float16, "wg"), _ptr(wu, torch.float16, "wu"),
         _ptr(wd, torch.float16, "wd"),
@@ -306,10 +313,11 @@ def smoe_moe_layer_w4a16(x, w_router, logit_bias, k: int, flags: int, topk_ids, 
                          active_experts, n_active, elb_counts, layer: int, M: int, plan_ids,
                          plan_counts, elb_flags: int, I: int, group_size: int, wg_q, wg_s, wu_q,
                          wu_s, wd_q, wd_s, workspace, slot_out, y, shared=None, shared_out=None,
-                         stream=None) -> None:
+                         stream=None, *, _fn="") -> None:
     """The whole draft layer in one call: smoe_route_align_elb,
     smoe_w4a16_expert_ffn and smoe_combine with the same arguments.
     elb_counts [L][E] or None; shared: optional (wg, wu, wd) fp16 weights."""
+    fname = _fn or "smoe_moe_layer_w4a16"
     T, H = x.shape
     E = w_router.shape[0]
     L = elb_counts.shape[0] if elb_counts is not None else 0
@@ -329,7 +337,7 @@ def smoe_moe_layer_w4a16(x, w_router, logit_bias, k: int, flags: int, topk_ids, 
     _need(wd_s, E * H * I // G, "wd_s")
     _ffn_sizes(T, k, E, H, sI, sorted_slots, expert_offsets, slot_out, shared, shared_out)
     _need(y, T * H, "y")
-    _check("smoe_moe_layer_w4a16", _lib.smoe_moe_layer_w4a16(
+    _check(fname, getattr(_lib, fname)(
         _ptr(x, torch.float16, "x"), _ptr(w_router, torch.float32, "w_router"),
         _ptr(logit_bias, torch.float32, "logit_bias"), T, H, E, k, flags,
         _ptr(topk_ids, torch.int32, "topk_ids"), _ptr(topk_w, torch.float32, "topk_w"),
@@ -350,4 +358,40 @@ def smoe_moe_layer_w4a16(x, w_router, logit_bias, k: int, flags: int, topk_ids, 
         sI, sg, su, sd,
         _ptr(workspace, torch.uint8, "workspace"), workspace.numel(),
         _ptr(slot_out, torch.float32, "slot_out"), so, _ptr(y, torch.float16, "y"),
+        _stream(stream)))
+
+
+def smoe_w4a16_expert_ffn_tiled(*args, **kw) -> None:
+    """smoe_w4a16_expert_ffn with every weight in the tiled layout."""
+    smoe_w4a16_expert_ffn(*args, **kw, _fn="smoe_w4a16_expert_ffn_tiled")
+
+
+def smoe_fp16_expert_ffn_tiled(*args, **kw) -> None:
+    """smoe_fp16_expert_ffn with every weight in the tiled layout."""
+    smoe_fp16_expert_ffn(*args, **kw, _fn="smoe_fp16_expert_ffn_tiled")
+
+
+def smoe_moe_layer_w4a16_tiled(*args, **kw) -> None:
+    """smoe_moe_layer_w4a16 with every weight in the tiled layout."""
+    smoe_moe_layer_w4a16(*args, **kw, _fn="smoe_moe_layer_w4a16_tiled")
+
+
+def smoe_tile_weights(w, scales, E: int, N: int, K: int, group_size: int, w_tiled,
+                      scales_tiled=None, stream=None) -> None:
+    """Tiled copy of one [E][N][K] weight tensor: group_size 0 for fp16 values
+    (w, w_tiled float16, scales None), else INT4 codes (int32 [E][N][K/8]) and
+    fp16 scales [E][N][K/G]."""
+    if group_size:
+        wdt, n_w, n_s = torch.int32, E * N * K // 8, E * N * K // group_size
+    else:
+        wdt, n_w, n_s = torch.float16, E * N * K, 0
+    _need(w, n_w, "w")
+    _need(w_tiled, n_w, "w_tiled")
+    if group_size:
+        _need(scales, n_s, "scales")
+        _need(scales_tiled, n_s, "scales_tiled")
+    _check("smoe_tile_weights", _lib.smoe_tile_weights(
+        _ptr(w, wdt, "w"), _ptr(scales, torch.float16, "scales") if group_size else None,
+        E, N, K, group_size, _ptr(w_tiled, wdt, "w_tiled"),
+        _ptr(scales_tiled, torch.float16, "scales_tiled") if group_size else None,
         _stream(stream)))

@@ -86,6 +86,8 @@
 //   G = 128: word 4g + q  (one 16-byte load of words 4g .. 4g+3);
 //   G =  64: word 8(q/2) + 2g + q%2 (two 8-byte loads);
 //   G =  32: word 4q + g  (four 4-byte loads).
+// In the tiled layout (smoe_tile_weights) each lane's four words already
+// sit in step order in 16 consecutive bytes, one load for every G.
 // FP16 block: one MFMA step, lane group g takes k = 8g .. 8g+7 of the block.
 #include <algorithm>
 #include <atomic>
@@ -150,6 +152,7 @@ struct Group {
   int w_rstride;                // bytes per weight row
   int s_rstride;                // scale elements per row
   int fmt;                      // kInt4 or kFp16
+  int tiled;                    // weights and scales in the 16-row tiled layout
   int N, K;                     // output rows and reduction length of this stage
   int nblk;                     // blocks per weight row
   int tiles, parts;             // row tiles and K parts per chunk
@@ -210,13 +213,6 @@ __device__ __forceinline__ u32x4 permute_k8(u32x4 d) {
   e[2] = (d[1] & 0xFFFFu) | (d[3] << 16);
   e[3] = (d[1] >> 16) | (d[3] & 0xFFFF0000u);
   return e;
-}
-
-// Word index (within an INT4 block) that MFMA step q of lane group g uses.
-template <int G>
-__device__ __forceinline__ int int4_word(int g, int q) {
-  constexpr int per = G / 32;  // MFMA steps per quantisation group
-  return (q / per) * (G / 8) + g * per + (q % per);
 }
 
 // One item: part `part` of row tile `tile` of chunk `chunk` of group `grp`
@@ -432,29 +428,48 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
   const uint8_t* wp[2];
   const uint16_t* sp[2];
   int l_blk0 = 0, l_nblk = 1, l_fmt = kFp16;
+  // Tiled layout: the 16 rows of a wave's row slice and one block of k form
+  // 1 KB in lane order (lane 16 g + r holds the 16 bytes that MFMA lane
+  // group g of row r takes), so each load instruction reads 1 KB in one
+  // piece; their scales form 16 NQ consecutive values. Row-major layout:
+  // each lane reads within its own row.
+  bool l_tiled = false;
+  int l_bstride = kBlockBytes, l_sbstride = NQ;  // per block of k: bytes, scale elements
   auto set_load_item = [&](const Item& it) {
     const Group& gr = a.grp[it.grp];
     l_fmt = WK == kInt4 ? gr.fmt : kFp16;
     l_blk0 = it.part * D;
     l_nblk = gr.nblk;
+    l_tiled = gr.tiled != 0;
+    l_bstride = l_tiled ? 16 * kBlockBytes : kBlockBytes;
+    l_sbstride = l_tiled ? 16 * NQ : NQ;
     const int lane_kb = (l_fmt == kInt4 && G == 64) ? 8 * g : (l_fmt == kInt4 && G == 32) ? 4 * g
                                                                                           : 16 * g;
 #pragma unroll
     for (int m = 0; m < 2; ++m) {
-      const int row = min(row_of(it.tile, m), gr.N - 1);  // rows past N: loaded, never stored
       const uint8_t* wm = (STAGE == 1 && m == 1) ? gr.w1 : gr.w0;
-      wp[m] = wm + it.e * gr.w_estride + static_cast<long long>(row) * gr.w_rstride + lane_kb;
-      if (WK == kInt4) {  // (FP16 groups: null + 0)
-        const uint16_t* sm = (STAGE == 1 && m == 1) ? gr.s1 : gr.s0;
-        sp[m] = sm + it.e * gr.s_estride + static_cast<long long>(row) * gr.s_rstride;
+      const uint16_t* sm = (STAGE == 1 && m == 1) ? gr.s1 : gr.s0;
+      if (l_tiled) {
+        // N is a multiple of 16: a slice past N is wholly past it, and
+        // reads the last slice instead (loaded, never stored)
+        const int sl = min(row_of(it.tile, m) >> 4, gr.N / 16 - 1);
+        const long long t0 = static_cast<long long>(sl) * gr.nblk;
+        wp[m] = wm + it.e * gr.w_estride + t0 * (16 * kBlockBytes) + 16 * lane;
+        if (WK == kInt4) sp[m] = l_fmt == kInt4 ? sm + it.e * gr.s_estride + (t0 * 16 + r16) * NQ
+                                                : sm;
+      } else {
+        const int row = min(row_of(it.tile, m), gr.N - 1);  // rows past N: loaded, never stored
+        wp[m] = wm + it.e * gr.w_estride + static_cast<long long>(row) * gr.w_rstride + lane_kb;
+        if (WK == kInt4)  // (FP16 groups: null + 0)
+          sp[m] = sm + it.e * gr.s_estride + static_cast<long long>(row) * gr.s_rstride;
       }
     }
   };
   auto load = [&](u32x4 (&r)[2], int blk) {
 #pragma unroll
     for (int m = 0; m < 2; ++m) {
-      const uint8_t* base = wp[m] + blk * kBlockBytes;
-      if (WK == kInt4 && G != 128 && l_fmt == kInt4) {
+      const uint8_t* base = wp[m] + blk * l_bstride;
+      if (WK == kInt4 && G != 128 && l_fmt == kInt4 && !l_tiled) {
         if (G == 64) {
           const u32x2 lo = *reinterpret_cast<const u32x2*>(base);
           const u32x2 hi = *reinterpret_cast<const u32x2*>(base + 32);
@@ -479,7 +494,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
   auto load_scales = [&](int blk0) {
 #pragma unroll
     for (int m = 0; m < 2; ++m) {
-      const uint16_t* sptr = sp[m] + min(blk0 + g, l_nblk - 1) * NQ;
+      const uint16_t* sptr = sp[m] + min(blk0 + g, l_nblk - 1) * l_sbstride;
       if (NQ == 1) {
         sring[m][0] = *sptr;
       } else if (NQ == 2) {
@@ -514,7 +529,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
     if (NCE == 1) {
 #pragma unroll
       for (int qq = 0; qq < 4; ++qq)
-        A[qq] = *reinterpret_cast<const f16x8*>(xs + arow[0] + 2 * (kk + 8 * int4_word<G>(g, qq)));
+        A[qq] = *reinterpret_cast<const f16x8*>(xs + arow[0] + 2 * (kk + 8 * int4_word(G, g, qq)));
     }
 #pragma unroll
     for (int m = 0; m < 2; ++m) {
@@ -536,7 +551,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
             const int q = grp * per + qq;
             const f16x8 Aq = NCE == 1 ? A[q]
                                       : *reinterpret_cast<const f16x8*>(
-                                            xs + arow[cg] + 2 * (kk + 8 * int4_word<G>(g, q)));
+                                            xs + arow[cg] + 2 * (kk + 8 * int4_word(G, g, q)));
             t = __builtin_amdgcn_mfma_f32_16x16x32_f16(Aq, B[q], t, 0, 0, 0);
           }
           acc[m][cg] += sc * t;
@@ -908,6 +923,7 @@ size_t workspace_bytes(long long T, long long k, long long I, long long Is) {
 // Weights of one group as the entry points hand them over.
 struct GroupWeights {
   int fmt;                       // kInt4 or kFp16
+  int tiled;                     // 16-row tiled layout (else row-major)
   const void *wg, *wu, *wd;      // codes (INT4) or values (FP16)
   const void *sg, *su, *sd;      // INT4 scales, else null
   int E, I, G;                   // experts, intermediate size, INT4 group size
@@ -920,6 +936,7 @@ struct GroupWeights {
 void set_matrix(Group& g, const GroupWeights& w, int N, int K, const void* wq, const void* ws,
                 int D) {
   g.fmt = w.fmt;
+  g.tiled = w.tiled;
   g.N = N;
   g.K = K;
   g.w_rstride = w.fmt == kInt4 ? K / 2 : K * 2;
@@ -1085,6 +1102,7 @@ smoe_status build_plans(const char* who, StagePlans& p, const void* x, int T, in
                         const int32_t* sorted_slots, const int32_t* offsets, void* workspace,
                         GroupWeights routed, int shared_I, const void* swg, const void* swu,
                         const void* swd, float* slot_out, float* shared_out) {
+  // (both groups share one layout; H, I and shared_I are multiples of 128)
   GroupWeights gw[2];
   routed.csz = chunk_slots(T, k, routed.E);
   routed.rows = T * k;
@@ -1096,6 +1114,7 @@ smoe_status build_plans(const char* who, StagePlans& p, const void* x, int T, in
     GroupWeights& s = gw[1];
     s = GroupWeights{};
     s.fmt = kFp16;
+    s.tiled = routed.tiled;
     s.wg = swg; s.wu = swu; s.wd = swd;
     s.E = 1; s.I = shared_I; s.G = 0;
     s.csz = std::min(T, kMaxChunk);
@@ -1113,24 +1132,13 @@ smoe_status build_plans(const char* who, StagePlans& p, const void* x, int T, in
   return SMOE_OK;
 }
 
-}  // namespace
-}  // namespace smoe
-
-using namespace smoe;
-
-extern "C" size_t smoe_ffn_workspace_bytes(int T, int k, int E, int H, int I, int shared_I) {
-  if (T <= 0 || k <= 0 || E <= 0 || H <= 0 || I <= 0 || shared_I < 0) return 0;
-  return workspace_bytes(T, k, I, shared_I);
-}
-
-extern "C" smoe_status smoe_w4a16_expert_ffn(
+smoe_status w4a16_ffn(int tiled,
     const void* x, int T, int k, int E, int H, int I, int group_size, const uint32_t* wg_q,
     const void* wg_s, const uint32_t* wu_q, const void* wu_s, const uint32_t* wd_q,
     const void* wd_s, const int32_t* sorted_slots, const int32_t* expert_offsets, int shared_I,
     const void* shared_wg, const void* shared_wu, const void* shared_wd, void* workspace,
     size_t workspace_bytes_, float* slot_out, float* shared_out, void* stream) {
-  clear_error();
-  const char* who = "w4a16_expert_ffn";
+  const char* who = tiled ? "w4a16_expert_ffn_tiled" : "w4a16_expert_ffn";
   SMOE_REQUIRE(group_size == 32 || group_size == 64 || group_size == 128, SMOE_EUNSUPPORTED,
                "%s: group size must be 32, 64 or 128 (got %d)", who, group_size);
   smoe_status st = check_common(who, x, T, k, E, H, I, sorted_slots, expert_offsets, shared_I,
@@ -1148,6 +1156,7 @@ extern "C" smoe_status smoe_w4a16_expert_ffn(
 
   GroupWeights r{};
   r.fmt = kInt4;
+  r.tiled = tiled;
   r.wg = wg_q; r.wu = wu_q; r.wd = wd_q;
   r.sg = wg_s; r.su = wu_s; r.sd = wd_s;
   r.E = E; r.I = I; r.G = group_size;
@@ -1166,13 +1175,12 @@ extern "C" smoe_status smoe_w4a16_expert_ffn(
 #undef SMOE_FFN_NC
 }
 
-extern "C" smoe_status smoe_fp16_expert_ffn(
+smoe_status fp16_ffn(int tiled,
     const void* x, int T, int k, int E, int H, int I, const void* wg, const void* wu,
     const void* wd, const int32_t* sorted_slots, const int32_t* expert_offsets, int shared_I,
     const void* shared_wg, const void* shared_wu, const void* shared_wd, void* workspace,
     size_t workspace_bytes_, float* slot_out, float* shared_out, void* stream) {
-  clear_error();
-  const char* who = "fp16_expert_ffn";
+  const char* who = tiled ? "fp16_expert_ffn_tiled" : "fp16_expert_ffn";
   smoe_status st = check_common(who, x, T, k, E, H, I, sorted_slots, expert_offsets, shared_I,
                                 shared_wg, shared_wu, shared_wd, workspace, workspace_bytes_,
                                 slot_out, shared_out);
@@ -1183,6 +1191,7 @@ extern "C" smoe_status smoe_fp16_expert_ffn(
                "%s: weights must be 16-byte aligned", who);
   GroupWeights r{};
   r.fmt = kFp16;
+  r.tiled = tiled;
   r.wg = wg; r.wu = wu; r.wd = wd;
   r.E = E; r.I = I; r.G = 0;
   StagePlans p;
@@ -1193,7 +1202,7 @@ extern "C" smoe_status smoe_fp16_expert_ffn(
   return p.nc == 2 ? launch_ffn<kFp16, 128, 2>(p, s) : launch_ffn<kFp16, 128, 1>(p, s);
 }
 
-extern "C" smoe_status smoe_moe_layer_w4a16(
+smoe_status moe_layer(int tiled,
     const void* x, const float* w_router, const float* logit_bias, int T, int H, int E, int k,
     int flags, int32_t* topk_ids, float* topk_w, float* logits, const float* shared_gate_w,
     float* shared_gate, int32_t* expert_counts, int32_t* expert_offsets, int32_t* sorted_slots,
@@ -1203,8 +1212,7 @@ extern "C" smoe_status smoe_moe_layer_w4a16(
     const uint32_t* wd_q, const void* wd_s, int shared_I, const void* shared_wg,
     const void* shared_wu, const void* shared_wd, void* workspace, size_t workspace_bytes_,
     float* slot_out, float* shared_out, void* y, void* stream) {
-  clear_error();
-  const char* who = "moe_layer_w4a16";
+  const char* who = tiled ? "moe_layer_w4a16_tiled" : "moe_layer_w4a16";
   // every step's checks before anything is enqueued
   RouteArgs ra;
   smoe_status st = route_check(x, w_router, logit_bias, T, H, E, k, flags, topk_ids, topk_w,
@@ -1235,6 +1243,7 @@ extern "C" smoe_status smoe_moe_layer_w4a16(
                SMOE_EINVAL, "%s: scales must be 8-byte aligned", who);
   GroupWeights r{};
   r.fmt = kInt4;
+  r.tiled = tiled;
   r.wg = wg_q; r.wu = wu_q; r.wd = wd_q;
   r.sg = wg_s; r.su = wu_s; r.sd = wd_s;
   r.E = E; r.I = I; r.G = group_size;
@@ -1248,9 +1257,101 @@ extern "C" smoe_status smoe_moe_layer_w4a16(
                             sorted_slots, active_experts, n_active, elb_counts, L, layer, M,
                             plan_ids, plan_counts, elb_flags, stream);
   if (st != SMOE_OK) return st;
-  st = smoe_w4a16_expert_ffn(x, T, k, E, H, I, group_size, wg_q, wg_s, wu_q, wu_s, wd_q, wd_s,
+  st = w4a16_ffn(tiled, x, T, k, E, H, I, group_size, wg_q, wg_s, wu_q, wu_s, wd_q, wd_s,
                              sorted_slots, expert_offsets, shared_I, shared_wg, shared_wu,
                              shared_wd, workspace, workspace_bytes_, slot_out, shared_out, stream);
   if (st != SMOE_OK) return st;
   return smoe_combine(slot_out, topk_w, T, k, H, s_out, shared_gate, y, stream);
+}
+
+}  // namespace
+}  // namespace smoe
+
+using namespace smoe;
+
+extern "C" size_t smoe_ffn_workspace_bytes(int T, int k, int E, int H, int I, int shared_I) {
+  if (T <= 0 || k <= 0 || E <= 0 || H <= 0 || I <= 0 || shared_I < 0) return 0;
+  return workspace_bytes(T, k, I, shared_I);
+}
+
+extern "C" smoe_status smoe_w4a16_expert_ffn(
+    const void* x, int T, int k, int E, int H, int I, int group_size, const uint32_t* wg_q,
+    const void* wg_s, const uint32_t* wu_q, const void* wu_s, const uint32_t* wd_q,
+    const void* wd_s, const int32_t* sorted_slots, const int32_t* expert_offsets, int shared_I,
+    const void* shared_wg, const void* shared_wu, const void* shared_wd, void* workspace,
+    size_t workspace_bytes_, float* slot_out, float* shared_out, void* stream) {
+  clear_error();
+  return w4a16_ffn(0, x, T, k, E, H, I, group_size, wg_q, wg_s, wu_q, wu_s, wd_q, wd_s, sorted_slots,
+                   expert_offsets, shared_I, shared_wg, shared_wu, shared_wd, workspace,
+                   workspace_bytes_, slot_out, shared_out, stream);
+}
+
+extern "C" smoe_status smoe_w4a16_expert_ffn_tiled(
+    const void* x, int T, int k, int E, int H, int I, int group_size, const uint32_t* wg_q,
+    const void* wg_s, const uint32_t* wu_q, const void* wu_s, const uint32_t* wd_q,
+    const void* wd_s, const int32_t* sorted_slots, const int32_t* expert_offsets, int shared_I,
+    const void* shared_wg, const void* shared_wu, const void* shared_wd, void* workspace,
+    size_t workspace_bytes_, float* slot_out, float* shared_out, void* stream) {
+  clear_error();
+  return w4a16_ffn(1, x, T, k, E, H, I, group_size, wg_q, wg_s, wu_q, wu_s, wd_q, wd_s, sorted_slots,
+                   expert_offsets, shared_I, shared_wg, shared_wu, shared_wd, workspace,
+                   workspace_bytes_, slot_out, shared_out, stream);
+}
+
+extern "C" smoe_status smoe_fp16_expert_ffn(
+    const void* x, int T, int k, int E, int H, int I, const void* wg, const void* wu,
+    const void* wd, const int32_t* sorted_slots, const int32_t* expert_offsets, int shared_I,
+    const void* shared_wg, const void* shared_wu, const void* shared_wd, void* workspace,
+    size_t workspace_bytes_, float* slot_out, float* shared_out, void* stream) {
+  clear_error();
+  return fp16_ffn(0, x, T, k, E, H, I, wg, wu, wd, sorted_slots, expert_offsets, shared_I, shared_wg,
+                  shared_wu, shared_wd, workspace, workspace_bytes_, slot_out, shared_out, stream);
+}
+
+extern "C" smoe_status smoe_fp16_expert_ffn_tiled(
+    const void* x, int T, int k, int E, int H, int I, const void* wg, const void* wu,
+    const void* wd, const int32_t* sorted_slots, const int32_t* expert_offsets, int shared_I,
+    const void* shared_wg, const void* shared_wu, const void* shared_wd, void* workspace,
+    size_t workspace_bytes_, float* slot_out, float* shared_out, void* stream) {
+  clear_error();
+  return fp16_ffn(1, x, T, k, E, H, I, wg, wu, wd, sorted_slots, expert_offsets, shared_I, shared_wg,
+                  shared_wu, shared_wd, workspace, workspace_bytes_, slot_out, shared_out, stream);
+}
+
+extern "C" smoe_status smoe_moe_layer_w4a16(
+    const void* x, const float* w_router, const float* logit_bias, int T, int H, int E, int k,
+    int flags, int32_t* topk_ids, float* topk_w, float* logits, const float* shared_gate_w,
+    float* shared_gate, int32_t* expert_counts, int32_t* expert_offsets, int32_t* sorted_slots,
+    int32_t* active_experts, int32_t* n_active, int32_t* elb_counts, int L, int layer, int M,
+    int32_t* plan_ids, int32_t* plan_counts, int elb_flags, int I, int group_size,
+    const uint32_t* wg_q, const void* wg_s, const uint32_t* wu_q, const void* wu_s,
+    const uint32_t* wd_q, const void* wd_s, int shared_I, const void* shared_wg,
+    const void* shared_wu, const void* shared_wd, void* workspace, size_t workspace_bytes_,
+    float* slot_out, float* shared_out, void* y, void* stream) {
+  clear_error();
+  return moe_layer(0, x, w_router, logit_bias, T, H, E, k, flags, topk_ids, topk_w, logits,
+                   shared_gate_w, shared_gate, expert_counts, expert_offsets, sorted_slots,
+                   active_experts, n_active, elb_counts, L, layer, M, plan_ids, plan_counts,
+                   elb_flags, I, group_size, wg_q, wg_s, wu_q, wu_s, wd_q, wd_s, shared_I,
+                   shared_wg, shared_wu, shared_wd, workspace, workspace_bytes_, slot_out,
+                   shared_out, y, stream);
+}
+
+extern "C" smoe_status smoe_moe_layer_w4a16_tiled(
+    const void* x, const float* w_router, const float* logit_bias, int T, int H, int E, int k,
+    int flags, int32_t* topk_ids, float* topk_w, float* logits, const float* shared_gate_w,
+    float* shared_gate, int32_t* expert_counts, int32_t* expert_offsets, int32_t* sorted_slots,
+    int32_t* active_experts, int32_t* n_active, int32_t* elb_counts, int L, int layer, int M,
+    int32_t* plan_ids, int32_t* plan_counts, int elb_flags, int I, int group_size,
+    const uint32_t* wg_q, const void* wg_s, const uint32_t* wu_q, const void* wu_s,
+    const uint32_t* wd_q, const void* wd_s, int shared_I, const void* shared_wg,
+    const void* shared_wu, const void* shared_wd, void* workspace, size_t workspace_bytes_,
+    float* slot_out, float* shared_out, void* y, void* stream) {
+  clear_error();
+  return moe_layer(1, x, w_router, logit_bias, T, H, E, k, flags, topk_ids, topk_w, logits,
+                   shared_gate_w, shared_gate, expert_counts, expert_offsets, sorted_slots,
+                   active_experts, n_active, elb_counts, L, layer, M, plan_ids, plan_counts,
+                   elb_flags, I, group_size, wg_q, wg_s, wu_q, wu_s, wd_q, wd_s, shared_I,
+                   shared_wg, shared_wu, shared_wd, workspace, workspace_bytes_, slot_out,
+                   shared_out, y, stream);
 }

@@ -44,6 +44,14 @@ inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 
 
 // ------------------------------------------------------------------ device
 
+// Word (of the 16 in a 64-byte INT4 block of one weight row) that the
+// expert FFN's MFMA step q (0..3) of lane group g (0..3) takes, for
+// quantisation groups of G = 32, 64 or 128 codes: each step's 32 codes then
+// lie in one group.
+__host__ __device__ constexpr int int4_word(int G, int g, int q) {
+  return (q / (G / 32)) * (G / 8) + g * (G / 32) + (q % (G / 32));
+}
+
 // Lane index within the wave.
 __device__ __forceinline__ int lane_id() { return threadIdx.x & (kWave - 1); }
 

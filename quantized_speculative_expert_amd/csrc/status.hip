@@ -30,7 +30,7 @@ smoe_status check_launch(const char* what) {
 
 extern "C" {
 
-int smoe_abi_version(void) { return 3; }
+int smoe_abi_version(void) { return 4; }
 
 const char* smoe_status_string(smoe_status status) {
   switch (status) {

@@ -37,7 +37,11 @@ def _dev(a: Optional[np.ndarray], device) -> Optional[torch.Tensor]:
 
 
 class DeviceLayer:
-    def __init__(self, inp, device="cuda", elb_layers: int = 1, with_target: Optional[bool] = None):
+    def __init__(self, inp, device="cuda", elb_layers: int = 1, with_target: Optional[bool] = None,
+                 tiled: bool = False):
+        """tiled: hold every expert weight (routed INT4, FP16 target, FP16
+        shared) in the tiled layout of smoe_tile_weights, tiled once here on
+        the device, and run the *_tiled library calls."""
         cfg = inp.cfg
         self.cfg = cfg
         self.device = torch.device(device)
@@ -60,6 +64,21 @@ class DeviceLayer:
                                           _dev(inp.sd16, d))
         Is = self.sg16.shape[0] if self.sg16 is not None else 0
         self.shared_I = Is
+        self.tiled = bool(tiled)
+        if self.tiled:
+            G = cfg.G
+            self.wg_q, self.wg_s = self._tile(self.wg_q, self.wg_s, E, I, H, G)
+            self.wu_q, self.wu_s = self._tile(self.wu_q, self.wu_s, E, I, H, G)
+            self.wd_q, self.wd_s = self._tile(self.wd_q, self.wd_s, E, H, I, G)
+            if self.wg16 is not None:
+                self.wg16 = self._tile(self.wg16, None, E, I, H, 0)[0]
+                self.wu16 = self._tile(self.wu16, None, E, I, H, 0)[0]
+                self.wd16 = self._tile(self.wd16, None, E, H, I, 0)[0]
+            if Is:
+                self.sg16 = self._tile(self.sg16, None, 1, Is, H, 0)[0]
+                self.su16 = self._tile(self.su16, None, 1, Is, H, 0)[0]
+                self.sd16 = self._tile(self.sd16, None, 1, H, Is, 0)[0]
+            torch.cuda.synchronize(d)
 
         i32 = dict(dtype=torch.int32, device=d)
         f32 = dict(dtype=torch.float32, device=d)
@@ -90,6 +109,17 @@ class DeviceLayer:
         M = max(cfg.elb_M, 0)
         self.plan_ids = torch.empty((elb_layers, max(M, 1)), **i32)
         self.plan_counts = torch.empty((elb_layers, max(M, 1)), **i32)
+
+    @staticmethod
+    def _tile(w, s, E, N, K, G):
+        wt = torch.empty_like(w)
+        st = torch.empty_like(s) if s is not None else None
+        _lib.smoe_tile_weights(w, s, E, N, K, G, wt, st)
+        return wt, st
+
+    def _call(self, name: str):
+        """The library call `name`, or its tiled-layout form."""
+        return getattr(_lib, name + "_tiled" if self.tiled else name)
 
     _WEIGHTS = ("w_router", "router_bias", "shared_gate_w", "wg_q", "wg_s", "wu_q", "wu_s",
                 "wd_q", "wd_s", "wg16", "wu16", "wd16", "sg16", "su16", "sd16")
@@ -151,12 +181,12 @@ class DeviceLayer:
             shared = (self.sg16, self.su16, self.sd16)
             shared_out = self.shared_out
         if target:
-            _lib.smoe_fp16_expert_ffn(self.x, c.k, c.E, c.I, self.wg16, self.wu16, self.wd16,
+            self._call("smoe_fp16_expert_ffn")(self.x, c.k, c.E, c.I, self.wg16, self.wu16, self.wd16,
                                       self.sorted_slots, self.offsets, self.workspace,
                                       self.slot_out, shared=shared, shared_out=shared_out,
                                       stream=stream)
         else:
-            _lib.smoe_w4a16_expert_ffn(self.x, c.k, c.E, c.I, c.G, self.wg_q, self.wg_s,
+            self._call("smoe_w4a16_expert_ffn")(self.x, c.k, c.E, c.I, c.G, self.wg_q, self.wg_s,
                                        self.wu_q, self.wu_s, self.wd_q, self.wd_s,
                                        self.sorted_slots, self.offsets, self.workspace,
                                        self.slot_out, shared=shared, shared_out=shared_out,
@@ -167,7 +197,7 @@ class DeviceLayer:
         every token uses once."""
         if self.shared_out is None:
             return
-        _lib.smoe_fp16_expert_ffn(self.x, 1, 1, self.shared_I, self.sg16, self.su16, self.sd16,
+        self._call("smoe_fp16_expert_ffn")(self.x, 1, 1, self.shared_I, self.sg16, self.su16, self.sd16,
                                   self.shared_slots, self.shared_offsets, self.shared_ws,
                                   self.shared_out, stream=stream)
 
@@ -184,7 +214,7 @@ class DeviceLayer:
         if self.shared_out is not None:
             shared = (self.sg16, self.su16, self.sd16)
             shared_out = self.shared_out
-        _lib.smoe_moe_layer_w4a16(
+        self._call("smoe_moe_layer_w4a16")(
             self.x, self.w_router, self.router_bias, c.k, 0, self.topk_ids, self.topk_w,
             self.logits, self.shared_gate_w, self.shared_gate, self.counts, self.offsets,
             self.sorted_slots, self.active, self.n_active,

@@ -51,7 +51,7 @@ def test_binding_signatures_cover_header():
 
 
 def test_status_strings(lib):
-    assert lib.smoe_abi_version() == 3
+    assert lib.smoe_abi_version() == 4
     assert lib.smoe_status_string(0) == b"SMOE_OK"
     assert b"EINVAL" in lib.smoe_status_string(EINVAL)
     assert b"EUNSUPPORTED" in lib.smoe_status_string(EUNSUPPORTED)
@@ -248,3 +248,42 @@ def test_layer_call_argument_checks(lib):
     assert call(weights=[16, 16, N, 16, 16, 16]) == EINVAL              # null weight
     assert b"weight" in lib.smoe_last_error()
     assert call(T=0, x=N) == 0                                          # empty window
+
+
+def test_tiled_calls_check_like_row_major(lib):
+    # the tiled-layout calls take the row-major calls' arguments and checks
+    f = lib.smoe_w4a16_expert_ffn_tiled
+    f.argtypes = ([ctypes.c_void_p] + [ctypes.c_int] * 6 + [ctypes.c_void_p] * 8 +
+                  [ctypes.c_int] + [ctypes.c_void_p] * 4 +
+                  [ctypes.c_size_t, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p])
+    w = [16] * 8
+    ns = [0, N, N, N]
+    ws = 1 << 30
+    assert f(16, 17, 6, 64, 2048, 1408, 96, *w, *ns, 256, ws, 16, N, N) == EUNSUPPORTED
+    assert b"w4a16_expert_ffn_tiled" in lib.smoe_last_error()
+    assert f(16, 17, 6, 64, 2048, 1408, 128, *w, *ns, 256, 10, 16, N, N) == EINVAL
+    assert f(N, 0, 6, 64, 2048, 1408, 128, *w, *ns, 256, ws, 16, N, N) == 0  # empty window
+    g = lib.smoe_fp16_expert_ffn_tiled
+    g.argtypes = ([ctypes.c_void_p] + [ctypes.c_int] * 5 + [ctypes.c_void_p] * 5 +
+                  [ctypes.c_int] + [ctypes.c_void_p] * 4 +
+                  [ctypes.c_size_t, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p])
+    assert g(N, 17, 6, 64, 2048, 1408, *[16] * 5, *ns, 256, ws, 16, N, N) == EINVAL
+    assert b"fp16_expert_ffn_tiled" in lib.smoe_last_error()
+
+
+def test_tile_weights_argument_checks(lib):
+    f = lib.smoe_tile_weights
+    f.argtypes = [ctypes.c_void_p] * 2 + [ctypes.c_int] * 4 + [ctypes.c_void_p] * 3
+    a, b = 1 << 20, 1 << 30          # two well-separated (never dereferenced) addresses
+    assert f(a, a, 2, 8, 256, 128, b, b, N) == EUNSUPPORTED       # N not a multiple of 16
+    assert f(a, a, 2, 16, 200, 128, b, b, N) == EUNSUPPORTED      # K not a multiple of 128
+    assert f(a, a, 2, 16, 256, 16, b, b, N) == EUNSUPPORTED       # group size
+    assert b"group size" in lib.smoe_last_error()
+    assert f(-1, a, 2, 16, 256, 128, b, b, N) == EINVAL            # negative E
+    assert f(N, a, 2, 16, 256, 128, b, b, N) == EINVAL             # null weights
+    assert f(a, N, 2, 16, 256, 128, b, b, N) == EINVAL             # INT4 without scales
+    assert f(a, a, 2, 16, 256, 128, a + 16, b, N) == EINVAL        # overlapping copy
+    assert b"overlap" in lib.smoe_last_error()
+    assert f(a + 8, a, 2, 16, 256, 128, b, b, N) == EINVAL         # misaligned
+    assert f(a, a, 0, 16, 256, 128, b, b, N) == 0                  # nothing to tile
+

@@ -354,44 +354,135 @@ def oracle_slots_int4(L, ids, slots=None):
     return oracle.routed_ffn_expertwise(L.x, ids, load)
 
 
-def _shared_dev(shared, T, H):
+def tile_dev(smoe, w, s, E, N, K, G):
+    """Device copies of a row-major [E][N][K] weight (and its INT4 scales)
+    in the tiled layout, made by smoe_tile_weights."""
+    w = dev(w) if isinstance(w, np.ndarray) else w
+    s = dev(s) if isinstance(s, np.ndarray) else s
+    wt = torch.empty_like(w)
+    st = torch.empty_like(s) if s is not None else None
+    smoe.smoe_tile_weights(w, s, E, N, K, G, wt, st)
+    return wt, st
+
+
+def tiled_layout_np(w, s, G):
+    """The tiled layout written out from its definition with numpy index
+    arithmetic: w uint32 words [E][N][nb * 16] (K = 128 nb INT4 codes, or
+    32 nb FP16 values as words), s [E][N][nb * 128 / G] or None."""
+    E, N, words = w.shape
+    nb = words // 16
+    Gw = 128 if G == 0 else G
+    per = Gw // 32
+    wt = np.empty(E * N * words, np.uint32)
+    o = 0
+    for e in range(E):
+        for sl in range(N // 16):
+            for b in range(nb):
+                for g in range(4):
+                    for r in range(16):
+                        for q in range(4):
+                            word = (q // per) * (Gw // 8) + g * per + q % per
+                            wt[o] = w[e, 16 * sl + r, 16 * b + word]
+                            o += 1
+    if s is None:
+        return wt, None
+    nq = 128 // G
+    st = np.empty(s.size, s.dtype)
+    o = 0
+    for e in range(E):
+        for sl in range(N // 16):
+            for b in range(nb):
+                for r in range(16):
+                    st[o:o + nq] = s[e, 16 * sl + r, nq * b:nq * (b + 1)]
+                    o += nq
+    return wt, st
+
+
+@pytest.mark.parametrize("G", [0, 32, 64, 128])
+def test_tile_weights_layout(smoe, G):
+    """smoe_tile_weights matches the layout's definition bit for bit
+    (two experts, 48 rows, K = 256: three row slices, several blocks)."""
+    E, N, K = 2, 48, 256
+    rng = np.random.default_rng(G + 1)
+    if G:
+        w = rng.integers(0, 2**32, (E, N, K // 8), dtype=np.uint64).astype(np.uint32)
+        s = rng.standard_normal((E, N, K // G)).astype(np.float16)
+    else:
+        w = rng.standard_normal((E, N, K)).astype(np.float16)
+        s = None
+    wt, st = tile_dev(smoe, w, s, E, N, K, G)
+    w_words = w if G else w.view(np.uint32)
+    ref_w, ref_s = tiled_layout_np(w_words.reshape(E, N, -1), s, G)
+    got_w = host(wt).reshape(-1).view(np.uint32)
+    assert np.array_equal(got_w, ref_w)
+    if G:
+        assert np.array_equal(host(st).reshape(-1).view(np.uint16), ref_s.view(np.uint16))
+
+
+def test_tile_weights_argument_checks(smoe):
+    w = torch.zeros(2 * 16 * 32, dtype=torch.int32, device="cuda")
+    s = torch.zeros(2 * 16 * 2, dtype=torch.float16, device="cuda")
+    out, so = torch.empty_like(w), torch.empty_like(s)
+    with pytest.raises(smoe.SmoeError, match="multiple"):
+        smoe.smoe_tile_weights(w, s, 2, 8, 256, 128, out, so)      # N not a multiple of 16
+    with pytest.raises(smoe.SmoeError, match="group size"):
+        smoe.smoe_tile_weights(w, s, 2, 16, 256, 256, out, so)
+    with pytest.raises(smoe.SmoeError, match="overlap"):
+        smoe.smoe_tile_weights(w, s, 2, 16, 256, 128, w, so)
+    smoe.smoe_tile_weights(w, s, 0, 16, 256, 128, out, so)         # nothing to do
+
+
+def _shared_dev(shared, T, H, smoe=None, tiled=False):
     if shared is None:
         return None, None, 0
     sg, su, sd = shared
     out = torch.full((T, H), float("nan"), dtype=torch.float32, device="cuda")
-    return (dev(sg), dev(su), dev(sd)), out, sg.shape[0]
+    Is = sg.shape[0]
+    if tiled:
+        return (tile_dev(smoe, sg, None, 1, Is, H, 0)[0], tile_dev(smoe, su, None, 1, Is, H, 0)[0],
+                tile_dev(smoe, sd, None, 1, H, Is, 0)[0]), out, Is
+    return (dev(sg), dev(su), dev(sd)), out, Is
 
 
-def run_w4a16(smoe, x, ids, E, I, G, wg_q, wg_s, wu_q, wu_s, wd_q, wd_s, shared=None, calls=1):
+def run_w4a16(smoe, x, ids, E, I, G, wg_q, wg_s, wu_q, wu_s, wd_q, wd_s, shared=None, calls=1,
+              tiled=False):
     """slot_out (and shared_out when shared = (sg, su, sd) fp16 is given);
     with calls > 1 the same workspace serves that many calls in a row and
-    the last call's outputs are returned."""
+    the last call's outputs are returned. tiled: every weight tiled by
+    smoe_tile_weights and the tiled-layout call used."""
     T, k = ids.shape
     H = x.shape[1]
     al = oracle.align_by_expert(ids, E)
-    sh, sh_out, Is = _shared_dev(shared, T, H)
+    sh, sh_out, Is = _shared_dev(shared, T, H, smoe, tiled)
     ws = torch.zeros(smoe.smoe_ffn_workspace_bytes(T, k, E, H, I, Is), dtype=torch.uint8,
                      device="cuda")
     args = [dev(a) for a in (x, wg_q, wg_s, wu_q, wu_s, wd_q, wd_s, al["sorted_slots"],
                              al["offsets"])]
+    fn = smoe.smoe_w4a16_expert_ffn
+    if tiled:
+        args[1:3] = tile_dev(smoe, args[1], args[2], E, I, H, G)
+        args[3:5] = tile_dev(smoe, args[3], args[4], E, I, H, G)
+        args[5:7] = tile_dev(smoe, args[5], args[6], E, H, I, G)
+        fn = smoe.smoe_w4a16_expert_ffn_tiled
     for _ in range(calls):
         out = torch.full((T * k, H), float("nan"), dtype=torch.float32, device="cuda")
         if sh_out is not None:
             sh_out.fill_(float("nan"))
-        smoe.smoe_w4a16_expert_ffn(args[0], k, E, I, G, *args[1:7], args[7], args[8], ws, out,
-                                   shared=sh, shared_out=sh_out)
+        fn(args[0], k, E, I, G, *args[1:7], args[7], args[8], ws, out,
+           shared=sh, shared_out=sh_out)
     if shared is None:
         return host(out)
     return host(out), host(sh_out)
 
 
+@pytest.mark.parametrize("tiled", [False, True], ids=["rows", "tiled"])
 @pytest.mark.parametrize("name", ["tiny", "dsv2", "qwen"])
-def test_w4a16_ffn_matches_oracle(smoe, name):
+def test_w4a16_ffn_matches_oracle(smoe, name, tiled):
     L = layer(name)
     cfg = L.cfg
     ids = oracle.topk_experts(oracle.router_logits_f32(L.x, L.w_router, L.router_bias), cfg.k)
     got = run_w4a16(smoe, L.x, ids, cfg.E, cfg.I, cfg.G, L.wg_q, L.wg_s, L.wu_q, L.wu_s,
-                    L.wd_q, L.wd_s)
+                    L.wd_q, L.wd_s, tiled=tiled)
     ref = oracle_slots_int4(L, ids)
     assert np.isfinite(got).all()
     err = row_rel_err(got, ref)
@@ -447,13 +538,14 @@ def _synthetic_int4(E, H, I, G, seed):
     (256, 8, 33, 128, 128, 32),      # the limits: 256 experts, top-8, g32
     (8, 2, 17, 256, 512, 64),        # x resident in LDS for the gate/up stage, g64
 ])
-def test_w4a16_ffn_shapes(smoe, E, k, T, H, I, G):
+@pytest.mark.parametrize("tiled", [False, True], ids=["rows", "tiled"])
+def test_w4a16_ffn_shapes(smoe, E, k, T, H, I, G, tiled):
     rng = np.random.default_rng(T * 7 + E)
     x = rng.standard_normal((T, H)).astype(np.float16)
     q = _synthetic_int4(E, H, I, G, seed=E + H)
     ids = np.stack([rng.permutation(E)[:k] for _ in range(T)]).astype(np.int32)
     got = run_w4a16(smoe, x, ids, E, I, G, q["wg_q"], q["wg_s"], q["wu_q"], q["wu_s"],
-                    q["wd_q"], q["wd_s"])
+                    q["wd_q"], q["wd_s"], tiled=tiled)
 
     def load(e):
         return tuple(oracle.dequant_int4(q[n + "_q"][e], q[n + "_s"][e], G) for n in ("wg", "wu", "wd"))
@@ -477,20 +569,26 @@ def test_w4a16_ffn_one_hot_expert(smoe):
     assert row_rel_err(got, oracle.routed_ffn_expertwise(x, ids, load)) <= ROW_TOL
 
 
-def run_fp16(smoe, x, ids, E, I, wg, wu, wd, shared=None, calls=1):
+def run_fp16(smoe, x, ids, E, I, wg, wu, wd, shared=None, calls=1, tiled=False):
     T, k = ids.shape
     H = x.shape[1]
     al = oracle.align_by_expert(ids, E)
-    sh, sh_out, Is = _shared_dev(shared, T, H)
+    sh, sh_out, Is = _shared_dev(shared, T, H, smoe, tiled)
     ws = torch.zeros(smoe.smoe_ffn_workspace_bytes(T, k, E, H, I, Is), dtype=torch.uint8,
                      device="cuda")
     args = [dev(a) for a in (x, wg, wu, wd, al["sorted_slots"], al["offsets"])]
+    fn = smoe.smoe_fp16_expert_ffn
+    if tiled:
+        args[1] = tile_dev(smoe, args[1], None, E, I, H, 0)[0]
+        args[2] = tile_dev(smoe, args[2], None, E, I, H, 0)[0]
+        args[3] = tile_dev(smoe, args[3], None, E, H, I, 0)[0]
+        fn = smoe.smoe_fp16_expert_ffn_tiled
     for _ in range(calls):
         out = torch.full((T * k, H), float("nan"), dtype=torch.float32, device="cuda")
         if sh_out is not None:
             sh_out.fill_(float("nan"))
-        smoe.smoe_fp16_expert_ffn(args[0], k, E, I, *args[1:4], args[4], args[5], ws, out,
-                                  shared=sh, shared_out=sh_out)
+        fn(args[0], k, E, I, *args[1:4], args[4], args[5], ws, out,
+           shared=sh, shared_out=sh_out)
     if shared is None:
         return host(out)
     return host(out), host(sh_out)
@@ -506,14 +604,16 @@ def test_fp16_ffn_shared_expert_dsv2(smoe):
 
 
 @pytest.mark.parametrize("name", ["dsv2", "qwen"])
-def test_w4a16_ffn_with_shared_expert(smoe, name):
+@pytest.mark.parametrize("tiled", [False, True], ids=["rows", "tiled"])
+def test_w4a16_ffn_with_shared_expert(smoe, name, tiled):
     # routed INT4 experts and the FP16 shared expert(s) in the same launches,
     # three calls in a row on one workspace
     L = layer(name)
     cfg = L.cfg
     ids = oracle.topk_experts(oracle.router_logits_f32(L.x, L.w_router, L.router_bias), cfg.k)
     got, got_sh = run_w4a16(smoe, L.x, ids, cfg.E, cfg.I, cfg.G, L.wg_q, L.wg_s, L.wu_q,
-                            L.wu_s, L.wd_q, L.wd_s, shared=(L.sg16, L.su16, L.sd16), calls=3)
+                            L.wu_s, L.wd_q, L.wd_s, shared=(L.sg16, L.su16, L.sd16), calls=3,
+                            tiled=tiled)
     assert np.isfinite(got).all() and np.isfinite(got_sh).all()
     assert row_rel_err(got, oracle_slots_int4(L, ids)) <= ROW_TOL
     assert row_rel_err(got_sh, oracle.shared_ffn(L.x, L.sg16, L.su16, L.sd16)) <= ROW_TOL
@@ -530,7 +630,8 @@ def test_w4a16_ffn_with_shared_expert(smoe, name):
     (64, 6, 19, 2048, 256, 128, 256),  # the widest window that keeps x resident at H = 2048
     (64, 6, 20, 2048, 256, 128, 256),  # one token more: x staged per chunk again
 ])
-def test_w4a16_ffn_with_shared_shapes(smoe, E, k, T, H, I, G, Is):
+@pytest.mark.parametrize("tiled", [False, True], ids=["rows", "tiled"])
+def test_w4a16_ffn_with_shared_shapes(smoe, E, k, T, H, I, G, Is, tiled):
     rng = np.random.default_rng(T + Is)
     x = rng.standard_normal((T, H)).astype(np.float16)
     q = _synthetic_int4(E, H, I, G, seed=E + Is)
@@ -539,7 +640,7 @@ def test_w4a16_ffn_with_shared_shapes(smoe, E, k, T, H, I, G, Is):
     sd = (rng.standard_normal((H, Is)) * 0.02).astype(np.float16)
     ids = np.stack([rng.permutation(E)[:k] for _ in range(T)]).astype(np.int32)
     got, got_sh = run_w4a16(smoe, x, ids, E, I, G, q["wg_q"], q["wg_s"], q["wu_q"], q["wu_s"],
-                            q["wd_q"], q["wd_s"], shared=(sg, su, sd), calls=2)
+                            q["wd_q"], q["wd_s"], shared=(sg, su, sd), calls=2, tiled=tiled)
 
     def load(e):
         return tuple(oracle.dequant_int4(q[n + "_q"][e], q[n + "_s"][e], G) for n in ("wg", "wu", "wd"))
@@ -547,7 +648,8 @@ def test_w4a16_ffn_with_shared_shapes(smoe, E, k, T, H, I, G, Is):
     assert row_rel_err(got_sh, oracle.shared_ffn(x, sg, su, sd)) <= ROW_TOL
 
 
-def test_fp16_ffn_with_shared_expert(smoe):
+@pytest.mark.parametrize("tiled", [False, True], ids=["rows", "tiled"])
+def test_fp16_ffn_with_shared_expert(smoe, tiled):
     E, k, T, H, I, Is = 8, 2, 17, 256, 512, 768
     rng = np.random.default_rng(5)
     x = rng.standard_normal((T, H)).astype(np.float16)
@@ -556,7 +658,8 @@ def test_fp16_ffn_with_shared_expert(smoe):
     sg, su = [(rng.standard_normal((Is, H)) * 0.02).astype(np.float16) for _ in range(2)]
     sd = (rng.standard_normal((H, Is)) * 0.02).astype(np.float16)
     ids = np.stack([rng.permutation(E)[:k] for _ in range(T)]).astype(np.int32)
-    got, got_sh = run_fp16(smoe, x, ids, E, I, wg, wu, wd, shared=(sg, su, sd), calls=2)
+    got, got_sh = run_fp16(smoe, x, ids, E, I, wg, wu, wd, shared=(sg, su, sd), calls=2,
+                           tiled=tiled)
     ref = oracle.routed_ffn_expertwise(x, ids, lambda e: (wg[e], wu[e], wd[e]))
     assert row_rel_err(got, ref) <= ROW_TOL
     assert row_rel_err(got_sh, oracle.shared_ffn(x, sg, su, sd)) <= ROW_TOL
@@ -564,19 +667,21 @@ def test_fp16_ffn_with_shared_expert(smoe):
 
 @pytest.mark.parametrize("E,k,T,H,I", [(8, 2, 17, 256, 512), (4, 2, 150, 256, 256),
                                        (16, 1, 1, 384, 256), (3, 3, 300, 256, 384)])
-def test_fp16_ffn_shapes(smoe, E, k, T, H, I):
+@pytest.mark.parametrize("tiled", [False, True], ids=["rows", "tiled"])
+def test_fp16_ffn_shapes(smoe, E, k, T, H, I, tiled):
     rng = np.random.default_rng(E * T)
     x = rng.standard_normal((T, H)).astype(np.float16)
     wg = (rng.standard_normal((E, I, H)) * 0.02).astype(np.float16)
     wu = (rng.standard_normal((E, I, H)) * 0.02).astype(np.float16)
     wd = (rng.standard_normal((E, H, I)) * 0.02).astype(np.float16)
     ids = np.stack([rng.permutation(E)[:k] for _ in range(T)]).astype(np.int32)
-    got = run_fp16(smoe, x, ids, E, I, wg, wu, wd)
+    got = run_fp16(smoe, x, ids, E, I, wg, wu, wd, tiled=tiled)
     ref = oracle.routed_ffn_expertwise(x, ids, lambda e: (wg[e], wu[e], wd[e]))
     assert row_rel_err(got, ref) <= ROW_TOL
 
 
-def test_phi_draft_and_target(smoe):
+@pytest.mark.parametrize("tiled", [False, True], ids=["rows", "tiled"])
+def test_phi_draft_and_target(smoe, tiled):
     L = layer("phi")
     cfg = L.cfg
     ids = oracle.topk_experts(oracle.router_logits_f32(L.x, L.w_router), cfg.k)
@@ -585,8 +690,8 @@ def test_phi_draft_and_target(smoe):
     experts = sorted(set(flat.tolist()))[:3]
     sel = np.flatnonzero(np.isin(flat, experts))
     draft = run_w4a16(smoe, L.x, ids, cfg.E, cfg.I, cfg.G, L.wg_q, L.wg_s, L.wu_q, L.wu_s,
-                      L.wd_q, L.wd_s)
-    target = run_fp16(smoe, L.x, ids, cfg.E, cfg.I, L.wg16, L.wu16, L.wd16)
+                      L.wd_q, L.wd_s, tiled=tiled)
+    target = run_fp16(smoe, L.x, ids, cfg.E, cfg.I, L.wg16, L.wu16, L.wd16, tiled=tiled)
     assert np.isfinite(draft).all() and np.isfinite(target).all()
     for e in experts:
         s = np.flatnonzero(flat == e)
@@ -645,12 +750,15 @@ def test_empty_window_is_a_noop(smoe):
 
 @pytest.mark.parametrize("name", ["tiny", "dsv2", "qwen", "dsv2_t1"])
 @pytest.mark.parametrize("mode", ["fused", "fused-side", "separate", "separate-side",
-                                  "three-routing-calls", "one-call"])
+                                  "three-routing-calls", "one-call", "fused-tiled",
+                                  "separate-tiled", "one-call-tiled"])
 def test_layer_draft_matches_oracle(smoe, name, mode):
     from quantized_speculative_expert_amd.layer import DeviceLayer
     L = layer(name)
     ref = oracle.moe_layer(L, "draft")
-    d = DeviceLayer(L)
+    tiled = mode.endswith("-tiled")
+    mode = mode[:-len("-tiled")] if tiled else mode
+    d = DeviceLayer(L, tiled=tiled)
     if mode == "one-call":
         d.run(one_call=True)
     else:
