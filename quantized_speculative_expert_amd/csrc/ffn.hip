@@ -115,7 +115,10 @@ constexpr int kTkOff = kCpOff + kMaxE + 1;     // work-ticket slots (2 words)
 constexpr int kTabInts = kTkOff + 2;
 constexpr int kPools = 8;                  // work-ticket counters per stage
 constexpr int kUnit = 2;                   // consecutive items per ticket
-constexpr int kStaticPermille = 900;       // share of the even split taken up front
+#ifndef SMOE_FFN_STATIC_PERMILLE
+#define SMOE_FFN_STATIC_PERMILLE 900
+#endif
+constexpr int kStaticPermille = SMOE_FFN_STATIC_PERMILLE;  // share of the even split taken up front
 constexpr int kHdrCtr1 = 8;                // header words of the stage-1 counters
 constexpr int kHdrCtr2 = kHdrCtr1 + kPools;
 constexpr int kTabBytes = (kTabInts * 4 + 15) / 16 * 16;  // offsets, chunk prefix
@@ -124,8 +127,14 @@ constexpr int kMaxSlotsLds = 1024;         // sorted slots kept whole in LDS up 
 constexpr int kLdsPerCu = 160 * 1024;      // gfx950
 constexpr int kLdsBudget = kLdsPerCu / 2;  // per workgroup: two workgroups per CU
 constexpr int kRowPad = 16;                // bytes of padding per staged row
-constexpr int kD1 = 4;                     // blocks per item, stage 1 (8 KB per wave)
-constexpr int kD2 = 3;                     // blocks per item, stage 2 (finer: fewer items per WG)
+#ifndef SMOE_FFN_D1
+#define SMOE_FFN_D1 4
+#endif
+#ifndef SMOE_FFN_D2
+#define SMOE_FFN_D2 3
+#endif
+constexpr int kD1 = SMOE_FFN_D1;           // blocks per item, stage 1 (8 KB per wave)
+constexpr int kD2 = SMOE_FFN_D2;           // blocks per item, stage 2 (finer: fewer items per WG)
 constexpr int stage_d(int stage) { return stage == 1 ? kD1 : kD2; }
 // staged phases are whole INT4 items of the stage
 constexpr int phase_k(int stage) { return stage_d(stage) * 128; }

@@ -823,12 +823,12 @@ def test_batch_layer_full_size_sampled(smoe):
     assert np.array_equal(host(d.plan_ids), pid) and np.array_equal(host(d.plan_counts), pc)
 
 
-@pytest.mark.parametrize("fused", [True, False, "one-call"])
+@pytest.mark.parametrize("fused", [True, False, "one-call", "one-call-tiled"])
 def test_layer_graph_replay_matches_eager(smoe, fused):
     from quantized_speculative_expert_amd.layer import DeviceLayer
     L = layer("dsv2")
-    d = DeviceLayer(L)
-    one = fused == "one-call"
+    d = DeviceLayer(L, tiled=fused == "one-call-tiled")
+    one = fused in ("one-call", "one-call-tiled")
     d.run(elb=False, fuse_shared=bool(fused), one_call=one)
     eager = host(d.y).copy()
     side = torch.cuda.Stream()
@@ -856,6 +856,23 @@ def test_layer_graph_replay_matches_eager(smoe, fused):
         # split-K tiles add fp32 partial sums with device atomics, so the
         # float output may differ from the eager run in the last bits
         assert row_rel_err(host(d.y), eager) <= 1e-3
+
+
+@pytest.mark.parametrize("name", ["tiny", "dsv2", "phi", "dsv2_t1"])
+def test_tiled_layer_equals_row_major(smoe, name):
+    """Tiling moves bytes, not values: the same layer over tiled weights
+    gives the row-major layer's IDs and alignment, and its outputs up to the
+    order in which split-K tiles add their partial sums."""
+    from quantized_speculative_expert_amd.layer import DeviceLayer
+    L = layer(name)
+    rows, tiled = DeviceLayer(L), DeviceLayer(L, tiled=True)
+    for d in (rows, tiled):
+        d.run()
+    torch.cuda.synchronize()
+    assert np.array_equal(host(rows.topk_ids), host(tiled.topk_ids))
+    assert np.array_equal(host(rows.sorted_slots), host(tiled.sorted_slots))
+    assert row_rel_err(host(tiled.slot_out), host(rows.slot_out)) <= 1e-3
+    assert row_rel_err(host(tiled.y), host(rows.y)) <= 1e-3
 
 
 def _layer_outputs(d):
