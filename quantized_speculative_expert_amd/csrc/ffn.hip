@@ -77,9 +77,10 @@
 //
 // INT4 dequantisation without lookup tables: a packed word w holds 8 codes;
 // (w >> 4i) & 0x000F000F | 0x64006400 read as two fp16 values is
-// (1024 + c_i, 1024 + c_{i+4}); subtracting 1032 gives c - 8 exactly. The
-// eight values come out in k order 0,4,1,5,2,6,3,7, and the activations are
-// staged with the same permutation within each group of 8.
+// (1024 + c_i, 1024 + c_{i+4}); subtracting 1032 gives c - 8 exactly (the
+// odd i are read in place, see dequant_word). The eight values come out in
+// k order 0,4,1,5,2,6,3,7, and the activations are staged with the same
+// permutation within each group of 8.
 //
 // INT4 word layout per block so that each MFMA's 32 k lie in one
 // quantisation group (lane group g, MFMA step q):
@@ -200,14 +201,21 @@ __device__ __forceinline__ T bitcast(U u) {
 __device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
 
 // Eight INT4 codes of one word -> (c - 8) as fp16, in k order 0,4,1,5,2,6,3,7.
-// lo = 0x000F000F and magic = 0x64006400 are passed in registers so that
-// each (w >> 4i) & lo | magic is a single v_and_or_b32.
-__device__ __forceinline__ f16x8 dequant_word(uint32_t w, uint32_t lo, uint32_t magic) {
+// lo = 0x000F000F, hi = 0x00F000F0 and magic = 0x64006400 are passed in
+// registers so that each mask-and-or is a single v_and_or_b32. A code in
+// bits 4..7 of a half reads as 1024 + 16 c, and (1024 + 16 c) / 16 - 72 =
+// c - 8 is exact in one fp16 fma, so one shift (by 8) serves all four
+// pairs.
+__device__ __forceinline__ f16x8 dequant_word(uint32_t w, uint32_t lo, uint32_t hi,
+                                              uint32_t magic) {
   const f16x2 bias = {static_cast<_Float16>(1032.0f), static_cast<_Float16>(1032.0f)};
+  const f16x2 sixteenth = {static_cast<_Float16>(0.0625f), static_cast<_Float16>(0.0625f)};
+  const f16x2 bias16 = {static_cast<_Float16>(-72.0f), static_cast<_Float16>(-72.0f)};
+  const uint32_t w8 = w >> 8;
   const f16x2 v0 = bitcast<f16x2>((w & lo) | magic) - bias;
-  const f16x2 v1 = bitcast<f16x2>(((w >> 4) & lo) | magic) - bias;
-  const f16x2 v2 = bitcast<f16x2>(((w >> 8) & lo) | magic) - bias;
-  const f16x2 v3 = bitcast<f16x2>(((w >> 12) & lo) | magic) - bias;
+  const f16x2 v1 = __builtin_elementwise_fma(bitcast<f16x2>((w & hi) | magic), sixteenth, bias16);
+  const f16x2 v2 = bitcast<f16x2>((w8 & lo) | magic) - bias;
+  const f16x2 v3 = __builtin_elementwise_fma(bitcast<f16x2>((w8 & hi) | magic), sixteenth, bias16);
   f16x8 r;
   r[0] = v0[0]; r[1] = v0[1]; r[2] = v1[0]; r[3] = v1[1];
   r[4] = v2[0]; r[5] = v2[1]; r[6] = v3[0]; r[7] = v3[1];
@@ -517,8 +525,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
   };
 
   f32x4 acc[2][NC];
-  uint32_t dq_lo = 0x000F000Fu, dq_magic = 0x64006400u;
-  asm volatile("" : "+v"(dq_lo), "+v"(dq_magic));  // keep the masks in VGPRs
+  uint32_t dq_lo = 0x000F000Fu, dq_hi = 0x00F000F0u, dq_magic = 0x64006400u;
+  asm volatile("" : "+v"(dq_lo), "+v"(dq_hi), "+v"(dq_magic));  // keep the masks in VGPRs
 
   // Slot r of routed chunk `it` (from the full copy in LDS, or the chunk's copy).
   auto chunk_slot = [&](const Item& it, int r) {
@@ -544,7 +552,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
     for (int m = 0; m < 2; ++m) {
       f16x8 B[4];
 #pragma unroll
-      for (int qq = 0; qq < 4; ++qq) B[qq] = dequant_word(r[m][qq], dq_lo, dq_magic);
+      for (int qq = 0; qq < 4; ++qq) B[qq] = dequant_word(r[m][qq], dq_lo, dq_hi, dq_magic);
 #pragma unroll
       for (int grp = 0; grp < NQ; ++grp) {
         const int src = d * 16 + r16;
