@@ -777,14 +777,15 @@ def test_layer_draft_matches_oracle(smoe, name, mode):
         assert np.array_equal(host(d.plan_ids), pid) and np.array_equal(host(d.plan_counts), pc)
 
 
-def test_batch_layer_full_size_sampled(smoe):
+@pytest.mark.parametrize("tiled", [False, True], ids=["rows", "tiled"])
+def test_batch_layer_full_size_sampled(smoe, tiled):
     # the batched window (544 tokens, Zipf-skewed router, 32-slot chunks) at
     # full size through the whole layer; the oracle checks every slot of
     # three experts and the outputs of two tokens, computed one by one
     from quantized_speculative_expert_amd.layer import DeviceLayer
     L = layer("batch", layer_idx=3)
     cfg = L.cfg
-    d = DeviceLayer(L, elb_layers=cfg.layers)
+    d = DeviceLayer(L, elb_layers=cfg.layers, tiled=tiled)
     d.run()
     lg = oracle.router_logits_f32(L.x, L.w_router, L.router_bias)
     ids = oracle.topk_experts(lg, cfg.k)
