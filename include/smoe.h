@@ -262,8 +262,8 @@ smoe_status smoe_fp16_expert_ffn(const void* x, int T, int k, int E, int H, int 
 
 /*
  * Weighted combine back to token order.               [P] expert-wise
- * verification paragraph (scatter the routing-weighted outputs and
- * accumulate them into their original sequence positions); [D] "Streamlined
+ * verification paragraph (per-slot expert outputs go back to their own
+ * token, weighted by the router, and add up there); [D] "Streamlined
  * Execution Engine" (kernels reduce expert outputs).
  *
  *   y[t] = fp16( sum_{j=0..k-1} topk_w[t][j] * slot_out[t*k + j]

@@ -32,8 +32,19 @@ something other than itself):
   combine                pinned (k=1, w=1 identity; linearity)
   elb_accumulate/topm    pinned (bincount; sum of counts; split-call
                          additivity; brute-force ranking)
-  layer outputs vs the pages: parity unpinned -- the pages print no worked
-                         numeric example of a layer output.
+  shared_ffn             pinned (hand-worked layer: gate and up rows give
+                         different results when swapped)
+  moe_layer              pinned (a whole layer worked by hand, both passes,
+                         tests/golden/layer_handworked.json; token-by-token
+                         composition of the pinned pieces with bias, gated
+                         shared experts and both passes; planted wiring
+                         mistakes -- swapped shared gate/up, dropped gate,
+                         renormalised weights, INT4 weights in the target
+                         pass, dropped bias, dropped shared term -- each
+                         fail these pins)
+  layer outputs vs the pages: the pages print no worked numeric example of
+                         a layer, so the pins above are hand-worked and
+                         structural rather than the pages' own numbers.
 """
 
 from .moe import (  # noqa: F401

@@ -277,8 +277,9 @@ def shared_ffn(x16: np.ndarray, sg16: np.ndarray, su16: np.ndarray, sd16: np.nda
 
 
 # --------------------------------------------------------------------------
-# Combine (Specter paper: scatter the routing-weighted outputs and
-# accumulate them back into their original sequence positions)
+# Combine (Specter paper, expert-wise verification paragraph: each expert's
+# per-slot outputs return to the token they came from, weighted by the
+# router, and are summed there)
 # --------------------------------------------------------------------------
 
 def combine(slot_out: np.ndarray, w: np.ndarray,

@@ -1,9 +1,9 @@
 // smoe_combine: routing-weighted sum of the per-slot expert outputs back in
 // token order, plus the (optionally gated) shared-expert output.
 //
-// Specter paper, expert-wise verification paragraph: after all expert
-// sub-batches finish, the routing-weighted outputs are scattered and
-// accumulated back into their original sequence positions. Design notes,
+// Specter paper, expert-wise verification paragraph: once every expert's
+// sub-batch is done, each slot's output goes back to its own token, scaled
+// by the router weight, and the slots of a token add up. Design notes,
 // "Streamlined Execution Engine" (kernels reduce expert outputs).
 //
 // Streaming kernel: each thread owns 8 consecutive hidden units of one

@@ -1,13 +1,12 @@
 // smoe_elb_accumulate_topm: ELB activation counter and top-M prefetch plan.
 //
-// Specter paper, Incremental Routing Pattern Analyzer paragraphs: the ELB
-// is a GPU-resident, layer-indexed set of activation counters
-// ELB_cnt[j, e] = number of draft tokens whose top-k route set in layer j
-// contains e; at each prefetch checkpoint the experts of every layer are
-// ranked by count and the top M (the layer's cache slots) form a compact
-// plan; the ELB is cleared at the end of the draft stage. Design notes,
-// "Predictive I/O Orchestrator" (pattern_analyzer accumulates routing
-// counts on the GPU and ranks experts at chunk boundaries).
+// Specter paper, Incremental Routing Pattern Analyzer paragraphs: per layer
+// j and expert e, the counter ELB_cnt[j, e] holds how many draft tokens so
+// far had e among their top-k experts in layer j; it lives on the GPU. At a
+// prefetch checkpoint each layer's experts are ordered by that count, the
+// first M (as many as the layer has cache slots) make up the plan, and the
+// counters go back to zero when drafting ends. Design notes, "Predictive I/O
+// Orchestrator" (the pattern analyzer).
 //
 // One workgroup per layer. Accumulation: an LDS histogram of the layer's
 // T*k IDs (integer adds, order-free) added to the counter row, which only
