@@ -91,6 +91,12 @@ extern "C" smoe_status smoe_tile_weights(const void* w, const void* scales, int 
   const char* db = static_cast<const char*>(w_tiled);
   SMOE_REQUIRE(db + bytes <= wb || wb + bytes <= db, SMOE_EINVAL,
                "%s: w_tiled must not overlap w", who);
+  const long long n_runs = rows * nblk;
+  const long long sbytes = int4 ? rows * (K / group_size) * 2 : 0;
+  const char* sb = static_cast<const char*>(scales);
+  const char* tb = static_cast<const char*>(scales_tiled);
+  SMOE_REQUIRE(!int4 || tb + sbytes <= sb || sb + sbytes <= tb, SMOE_EINVAL,
+               "%s: scales_tiled must not overlap scales", who);
   hipStream_t st = as_stream(stream);
   const long long n_chunks = bytes / 16;
   const uint32_t* src = static_cast<const uint32_t*>(w);
@@ -110,12 +116,6 @@ extern "C" smoe_status smoe_tile_weights(const void* w, const void* scales, int 
   }
   smoe_status s = check_launch(who);
   if (s != SMOE_OK || !int4) return s;
-  const long long n_runs = rows * nblk;
-  const long long sbytes = rows * (K / group_size) * 2;
-  const char* sb = static_cast<const char*>(scales);
-  const char* tb = static_cast<const char*>(scales_tiled);
-  SMOE_REQUIRE(tb + sbytes <= sb || sb + sbytes <= tb, SMOE_EINVAL,
-               "%s: scales_tiled must not overlap scales", who);
   const uint16_t* ss = static_cast<const uint16_t*>(scales);
   uint16_t* sd = static_cast<uint16_t*>(scales_tiled);
   switch (group_size) {

@@ -150,9 +150,11 @@ class DeviceLayer:
                              self.topk_ids, self.topk_w, self.logits,
                              self.shared_gate_w, self.shared_gate, stream=stream)
 
-    def route_align_elb(self, elb: bool = True, layer: int = 0, stream=None) -> None:
-        """route, align and (with elb) the ELB update of `layer` in one call."""
-        M = self.cfg.elb_M if elb else 0
+    def route_align_elb(self, elb: bool = True, layer: int = 0, rank: bool = True,
+                        stream=None) -> None:
+        """route, align and (with elb) the ELB update of `layer` in one call;
+        with rank, also the top-M plan of every layer of the counter."""
+        M = self.cfg.elb_M if elb and rank else 0
         _lib.smoe_route_align_elb(self.x, self.w_router, self.router_bias, self.cfg.k, 0,
                                   self.topk_ids, self.topk_w, self.logits,
                                   self.shared_gate_w, self.shared_gate, self.counts,
@@ -166,9 +168,13 @@ class DeviceLayer:
         _lib.smoe_align_by_expert(self.topk_ids, self.cfg.E, self.counts, self.offsets,
                                   self.sorted_slots, self.active, self.n_active, stream=stream)
 
-    def elb(self, layer: int = 0, M: Optional[int] = None, flags: int = 0, stream=None) -> None:
+    def elb(self, layer: int = 0, M: Optional[int] = None, flags: int = 0, stream=None,
+            accumulate: bool = True) -> None:
+        """Add this window's IDs to row `layer` of the counter (unless not
+        accumulate) and rank every layer's top-M (M = 0: no ranking)."""
         M = self.cfg.elb_M if M is None else M
-        _lib.smoe_elb_accumulate_topm(self.elb_counts, self.topk_ids[None], layer, M,
+        _lib.smoe_elb_accumulate_topm(self.elb_counts, self.topk_ids[None] if accumulate else None,
+                                      layer, M,
                                       self.plan_ids if M > 0 else None,
                                       self.plan_counts if M > 0 else None, flags, stream=stream)
 
@@ -205,11 +211,12 @@ class DeviceLayer:
         _lib.smoe_combine(self.slot_out, self.topk_w, self.shared_out, self.shared_gate,
                           self.y, stream=stream)
 
-    def layer_call(self, elb: bool = True, layer: int = 0, stream=None) -> None:
+    def layer_call(self, elb: bool = True, layer: int = 0, rank: bool = True,
+                   stream=None) -> None:
         """The whole draft layer as one library call (smoe_moe_layer_w4a16),
         which checks every step's arguments before it enqueues anything."""
         c = self.cfg
-        M = c.elb_M if elb else 0
+        M = c.elb_M if elb and rank else 0
         shared = shared_out = None
         if self.shared_out is not None:
             shared = (self.sg16, self.su16, self.sd16)
@@ -226,8 +233,13 @@ class DeviceLayer:
 
     # ---------------------------------------------------------------- whole layer
     def run(self, target: bool = False, elb: bool = True, fuse_shared: bool = True,
-            fuse_routing: bool = True, side_stream=None, one_call: bool = False) -> None:
+            fuse_routing: bool = True, side_stream=None, one_call: bool = False,
+            layer: int = 0, rank: bool = True) -> None:
         """Enqueue the whole layer on the current stream.
+
+        The ELB update adds this window's IDs to row `layer` of the counter;
+        with rank it also writes every layer's top-M plan (a stack of layers
+        can accumulate with rank=False and rank once at the end).
 
         one_call runs the draft layer as the single library call
         smoe_moe_layer_w4a16 (shared experts fused, no side stream).
@@ -247,7 +259,7 @@ class DeviceLayer:
         if one_call:
             if target or separate or side_stream is not None:
                 raise ValueError("one_call covers the draft layer with fused shared experts")
-            self.layer_call(elb=use_elb)
+            self.layer_call(elb=use_elb, layer=layer, rank=rank)
             return
         main = torch.cuda.current_stream(self.device)
         side = side_stream
@@ -274,16 +286,17 @@ class DeviceLayer:
             shared_done.record(side)
         side_elb = False
         if fuse_routing:
-            self.route_align_elb(elb=use_elb)
+            self.route_align_elb(elb=use_elb, layer=layer, rank=rank)
         else:
             self.route()
             if use_elb:
+                M = None if rank else 0
                 if side is not None:
                     fork()
-                    self.elb(stream=side)
+                    self.elb(layer=layer, M=M, stream=side)
                     side_elb = True
                 else:
-                    self.elb()
+                    self.elb(layer=layer, M=M)
             self.align()
         self.routed_ffn(target=target, with_shared=not separate)
         if shared_done is not None:

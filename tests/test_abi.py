@@ -287,3 +287,17 @@ def test_tile_weights_argument_checks(lib):
     assert f(a + 8, a, 2, 16, 256, 128, b, b, N) == EINVAL         # misaligned
     assert f(a, a, 0, 16, 256, 128, b, b, N) == 0                  # nothing to tile
 
+
+@pytest.mark.skipif(os.environ.get("HIP_VISIBLE_DEVICES", "") != "" or
+                    os.path.exists("/dev/kfd"),
+                    reason="passes host-side addresses; run only where no GPU can be reached")
+def test_tile_weights_checks_scales_before_any_launch(lib):
+    # codes that do not overlap but scales that do: the call must refuse
+    # before it enqueues the code-tiling kernel (a launch here, without a
+    # GPU, would report SMOE_EHIP instead)
+    f = lib.smoe_tile_weights
+    f.argtypes = [ctypes.c_void_p] * 2 + [ctypes.c_int] * 4 + [ctypes.c_void_p] * 3
+    a, b, c = 1 << 20, 1 << 30, 1 << 34
+    assert f(a, c, 2, 16, 256, 128, b, c + 16, N) == EINVAL
+    assert b"scales_tiled must not overlap" in lib.smoe_last_error()
+

@@ -8,8 +8,9 @@ import pytest
 import torch
 
 import oracle
-from workload import get_config, make_layer, quantize_rtn_int4
+from workload import get_config, make_activations, make_layer, make_router, quantize_rtn_int4
 from workload.configs import MoEConfig
+from workload.gen import zipf_bias
 
 pytestmark = pytest.mark.gpu
 
@@ -50,6 +51,7 @@ def row_rel_err(got, ref):
 
 
 _LAYERS = {}
+_REFS = {}
 
 
 def layer(name, seed=0, layer_idx=0):
@@ -57,6 +59,14 @@ def layer(name, seed=0, layer_idx=0):
     if key not in _LAYERS:
         _LAYERS[key] = make_layer(get_config(name), seed=seed, layer=layer_idx)
     return _LAYERS[key]
+
+
+def ref_layer(name, pass_="draft", seed=0, layer_idx=0):
+    """oracle.moe_layer of a generated layer, computed once per session."""
+    key = (name, pass_, seed, layer_idx)
+    if key not in _REFS:
+        _REFS[key] = oracle.moe_layer(layer(name, seed, layer_idx), pass_)
+    return _REFS[key]
 
 
 def run_route(smoe, x, w, bias, k, flags=0, gate_w=None):
@@ -682,27 +692,23 @@ def test_fp16_ffn_shapes(smoe, E, k, T, H, I, tiled):
 
 @pytest.mark.parametrize("tiled", [False, True], ids=["rows", "tiled"])
 def test_phi_draft_and_target(smoe, tiled):
+    # both expert FFN calls of the Phi-shaped window against the oracle, on
+    # every slot of every active expert (34 slots over the 15 experts the
+    # window routes to)
     L = layer("phi")
     cfg = L.cfg
-    ids = oracle.topk_experts(oracle.router_logits_f32(L.x, L.w_router), cfg.k)
-    flat = ids.ravel()
-    # sample: the slots of three experts (the oracle computes them one by one)
-    experts = sorted(set(flat.tolist()))[:3]
-    sel = np.flatnonzero(np.isin(flat, experts))
+    ref_d, ref_t = ref_layer("phi", "draft"), ref_layer("phi", "target")
+    ids = ref_d["ids"]
+    assert np.array_equal(ref_t["ids"], ids)
     draft = run_w4a16(smoe, L.x, ids, cfg.E, cfg.I, cfg.G, L.wg_q, L.wg_s, L.wu_q, L.wu_s,
                       L.wd_q, L.wd_s, tiled=tiled)
     target = run_fp16(smoe, L.x, ids, cfg.E, cfg.I, L.wg16, L.wu16, L.wd16, tiled=tiled)
     assert np.isfinite(draft).all() and np.isfinite(target).all()
-    for e in experts:
-        s = np.flatnonzero(flat == e)
-        xt = L.x[s // cfg.k].astype(np.float64)
-        ref_d = oracle.swiglu(xt, oracle.dequant_int4(L.wg_q[e], L.wg_s[e], cfg.G),
-                              oracle.dequant_int4(L.wu_q[e], L.wu_s[e], cfg.G),
-                              oracle.dequant_int4(L.wd_q[e], L.wd_s[e], cfg.G))
-        ref_t = oracle.swiglu(xt, L.wg16[e], L.wu16[e], L.wd16[e])
-        assert row_rel_err(draft[s], ref_d) <= ROW_TOL
-        assert row_rel_err(target[s], ref_t) <= ROW_TOL
-    assert len(sel) > 0
+    assert draft.shape == ref_d["slot_out"].shape == (cfg.T * cfg.k, cfg.H)
+    assert row_rel_err(draft, ref_d["slot_out"]) <= ROW_TOL
+    assert row_rel_err(target, ref_t["slot_out"]) <= ROW_TOL
+    # the two passes really differ (INT4 against FP16 weights)
+    assert row_rel_err(draft, target) > 1e-3
 
 
 # ------------------------------------------------------------------ combine
@@ -748,17 +754,22 @@ def test_empty_window_is_a_noop(smoe):
 
 # ------------------------------------------------------------------ whole layer
 
-@pytest.mark.parametrize("name", ["tiny", "dsv2", "qwen", "dsv2_t1"])
-@pytest.mark.parametrize("mode", ["fused", "fused-side", "separate", "separate-side",
-                                  "three-routing-calls", "one-call", "fused-tiled",
-                                  "separate-tiled", "one-call-tiled"])
+_LAYER_MODES = ["fused", "fused-side", "separate", "separate-side", "three-routing-calls",
+                "one-call", "fused-tiled", "separate-tiled", "one-call-tiled"]
+# (the Phi-shaped layer has no shared expert, so its separate modes equal fused)
+_LAYER_CASES = ([(n, m) for n in ("tiny", "dsv2", "qwen", "dsv2_t1") for m in _LAYER_MODES] +
+                [("phi", m) for m in ("fused", "three-routing-calls", "one-call", "fused-tiled",
+                                      "one-call-tiled")])
+
+
+@pytest.mark.parametrize("name,mode", _LAYER_CASES)
 def test_layer_draft_matches_oracle(smoe, name, mode):
     from quantized_speculative_expert_amd.layer import DeviceLayer
     L = layer(name)
-    ref = oracle.moe_layer(L, "draft")
+    ref = ref_layer(name, "draft")
     tiled = mode.endswith("-tiled")
     mode = mode[:-len("-tiled")] if tiled else mode
-    d = DeviceLayer(L, tiled=tiled)
+    d = DeviceLayer(L, tiled=tiled, with_target=False)
     if mode == "one-call":
         d.run(one_call=True)
     else:
@@ -770,11 +781,81 @@ def test_layer_draft_matches_oracle(smoe, name, mode):
     assert int(host(d.n_active)[0]) == int(ref["n_active"])
     err = row_rel_err(host(d.y), ref["y64"])
     assert err <= ROW_TOL, err
+    assert row_rel_err(host(d.slot_out), ref["slot_out"]) <= ROW_TOL
     if L.cfg.elb_M:
         ref_cnt = oracle.elb_accumulate(np.zeros((1, L.cfg.E), np.int32), ref["ids"][None], 0)
         pid, pc = oracle.elb_topm(ref_cnt, L.cfg.elb_M)
         assert np.array_equal(host(d.elb_counts), ref_cnt)
         assert np.array_equal(host(d.plan_ids), pid) and np.array_equal(host(d.plan_counts), pc)
+
+
+@pytest.mark.parametrize("tiled", [False, True], ids=["rows", "tiled"])
+def test_phi_target_layer_matches_oracle(smoe, tiled):
+    # the FP16 target verification pass of the Phi-shaped layer through the
+    # whole layer (route, align, FP16 expert FFN, combine): every slot and
+    # all 17 rows of y against oracle.moe_layer(..., "target")
+    from quantized_speculative_expert_amd.layer import DeviceLayer
+    L = layer("phi")
+    ref = ref_layer("phi", "target")
+    d = DeviceLayer(L, tiled=tiled)
+    d.run(target=True)
+    assert np.array_equal(host(d.topk_ids), ref["ids"])
+    assert np.array_equal(host(d.sorted_slots), ref["sorted_slots"])
+    assert row_rel_err(host(d.slot_out), ref["slot_out"]) <= ROW_TOL
+    y = host(d.y)
+    assert y.shape == (17, 4096) and np.isfinite(y).all()
+    assert row_rel_err(y, ref["y64"]) <= ROW_TOL
+    # the draft pass over the same tokens on the same runner picks the same
+    # experts (one shared router) and matches the oracle's draft layer,
+    # which is not the target output
+    d.run(target=False)
+    assert np.array_equal(host(d.topk_ids), ref["ids"])
+    ref_d = ref_layer("phi", "draft")
+    assert row_rel_err(host(d.y), ref_d["y64"]) <= ROW_TOL
+    assert row_rel_err(ref_d["y64"], ref["y64"]) > 1e-3
+
+
+def test_batch_stack_26_layers(smoe):
+    # The batched stack: 26 layers of 544 tokens, each with its own
+    # activations, router and Zipf(1.1) router skew, each run as the whole
+    # draft layer (routing, alignment, ELB update of its own counter row,
+    # W4A16 FFN with the shared experts, combine). The ELB accumulates over
+    # the 26 layers and is ranked top-32 once at the end. Expert weights: the
+    # generated weights of layer 0 serve every layer (the counter and plan
+    # depend only on the routing inputs, which are per layer).
+    from quantized_speculative_expert_amd.layer import DeviceLayer
+    cfg = get_config("batch")
+    L0 = layer("batch", layer_idx=0)
+    d = DeviceLayer(L0, elb_layers=cfg.layers)
+    ids_all = np.empty((cfg.layers, cfg.T, cfg.k), np.int32)
+    y0 = None
+    for l in range(cfg.layers):
+        x = make_activations(cfg, 0, l)
+        wr = make_router(cfg, 0, l)
+        b = zipf_bias(cfg.E, cfg.zipf_s, 0, l)
+        d.x.copy_(torch.from_numpy(x))
+        d.w_router.copy_(torch.from_numpy(wr))
+        d.router_bias.copy_(torch.from_numpy(b))
+        d.run(layer=l, rank=False)
+        ids = host(d.topk_ids)
+        ref_ids = oracle.topk_experts(oracle.router_logits_f32(x, wr, b), cfg.k)
+        assert np.array_equal(ids, ref_ids), l
+        ids_all[l] = ids
+        if l == 0:
+            y0 = host(d.y).copy()
+            assert np.array_equal(host(d.sorted_slots),
+                                  oracle.align_by_expert(ref_ids, cfg.E)["sorted_slots"])
+    # one ranking over all 26 counter rows, then compare with the oracle
+    d.elb(layer=0, M=cfg.elb_M, accumulate=False)
+    ref_cnt = oracle.elb_accumulate(np.zeros((cfg.layers, cfg.E), np.int32), ids_all, 0)
+    pid, pc = oracle.elb_topm(ref_cnt, cfg.elb_M)
+    assert np.array_equal(host(d.elb_counts), ref_cnt)
+    assert np.array_equal(host(d.plan_ids), pid)
+    assert np.array_equal(host(d.plan_counts), pc)
+    assert ref_cnt.sum() == cfg.layers * cfg.T * cfg.k
+    # every token of layer 0 against the oracle layer
+    ref0 = ref_layer("batch", "draft", layer_idx=0)
+    assert row_rel_err(y0, ref0["y64"]) <= ROW_TOL
 
 
 @pytest.mark.parametrize("tiled", [False, True], ids=["rows", "tiled"])
