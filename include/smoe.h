@@ -238,6 +238,41 @@ smoe_status smoe_w4a16_expert_ffn(const void* x, int T, int k, int E, int H, int
                                   float* slot_out, float* shared_out, void* stream);
 
 /*
+ * smoe_w4a16_expert_ffn without a workspace argument, for callers that
+ * cannot allocate device memory: code under HIP graph capture, tight
+ * serving loops, harnesses that forbid allocation. The call allocates
+ * nothing; its workspace is a static device array of the library,
+ * SMOE_NOALLOC_SCRATCH_BYTES bytes on each device the library runs on, held
+ * until the process ends. Arguments, results, checks and errors are those
+ * of smoe_w4a16_expert_ffn (minus workspace and workspace_bytes); the
+ * caller still passes every input and output.
+ *
+ *   - A window whose workspace (smoe_ffn_workspace_bytes(T, k, E, H, I,
+ *     shared_I)) exceeds SMOE_NOALLOC_SCRATCH_BYTES is refused with
+ *     SMOE_EUNSUPPORTED before anything is enqueued (16 MiB covers windows
+ *     of a few hundred slots at I = 1408, e.g. T = 17, k = 6 needs 3 MB).
+ *   - Each call first clears the workspace bytes it uses (a fill kernel on
+ *     `stream`), so a call never depends on what an earlier call left there,
+ *     whatever its shapes.
+ *   - Every call on one device shares that device's array: calls that
+ *     overlap in time on one device (different streams without ordering
+ *     between them, or different host threads) race and give undefined
+ *     results. Calls ordered on one stream are safe.
+ *   - SMOE_EHIP if the array's device address cannot be obtained.
+ */
+#define SMOE_NOALLOC_SCRATCH_BYTES (16u << 20)
+smoe_status smoe_w4a16_expert_ffn_noalloc(const void* x, int T, int k, int E, int H, int I,
+                                          int group_size,
+                                          const uint32_t* wg_q, const void* wg_s,
+                                          const uint32_t* wu_q, const void* wu_s,
+                                          const uint32_t* wd_q, const void* wd_s,
+                                          const int32_t* sorted_slots,
+                                          const int32_t* expert_offsets,
+                                          int shared_I, const void* shared_wg,
+                                          const void* shared_wu, const void* shared_wd,
+                                          float* slot_out, float* shared_out, void* stream);
+
+/*
  * Expert FFN with FP16 weights (target verification pass and always-on
  * shared experts).                                    [P] expert-wise
  * verification paragraphs (target router decisions; tokens of each expert

@@ -52,6 +52,8 @@ _SIGNATURES = {
                                   _i, _p, _p, _p,                      # shared_I, shared weights
                                   _p, _sz, _p, _p, _p, _p]),           # workspace .. stream
     "smoe_tile_weights": (_i, [_p, _p, _i, _i, _i, _i, _p, _p, _p]),
+    "smoe_w4a16_expert_ffn_noalloc": (_i, [_p, _i, _i, _i, _i, _i, _i, _p, _p, _p, _p, _p, _p,
+                                           _p, _p, _i, _p, _p, _p, _p, _p, _p]),
 }
 # the tiled-layout calls take the same arguments as their row-major forms
 for _name in ("smoe_w4a16_expert_ffn", "smoe_fp16_expert_ffn", "smoe_moe_layer_w4a16"):
@@ -266,6 +268,34 @@ def smoe_w4a16_expert_ffn(x, k: int, E: int, I: int, group_size: int, wg_q, wg_s
         _ptr(sorted_slots, torch.int32, "sorted_slots"),
         _ptr(expert_offsets, torch.int32, "expert_offsets"), sI, sg, su, sd,
         _ptr(workspace, torch.uint8, "workspace"), workspace.numel(),
+        _ptr(slot_out, torch.float32, "slot_out"), so, _stream(stream)))
+
+
+SMOE_NOALLOC_SCRATCH_BYTES = 16 << 20
+
+
+def smoe_w4a16_expert_ffn_noalloc(x, k: int, E: int, I: int, group_size: int, wg_q, wg_s, wu_q,
+                                  wu_s, wd_q, wd_s, sorted_slots, expert_offsets, slot_out,
+                                  shared=None, shared_out=None, stream=None) -> None:
+    """smoe_w4a16_expert_ffn with the library's static workspace (no
+    workspace argument; the call allocates nothing)."""
+    T, H = x.shape
+    sI, sg, su, sd, so = _shared_args(shared, shared_out)
+    G = max(group_size, 1)
+    for name, t in (("wg_q", wg_q), ("wu_q", wu_q)):
+        _need(t, E * I * H // 8, name)
+    for name, t in (("wg_s", wg_s), ("wu_s", wu_s)):
+        _need(t, E * I * H // G, name)
+    _need(wd_q, E * H * I // 8, "wd_q")
+    _need(wd_s, E * H * I // G, "wd_s")
+    _ffn_sizes(T, k, E, H, sI, sorted_slots, expert_offsets, slot_out, shared, shared_out)
+    _check("smoe_w4a16_expert_ffn_noalloc", _lib.smoe_w4a16_expert_ffn_noalloc(
+        _ptr(x, torch.float16, "x"), T, k, E, H, I, group_size,
+        _ptr(wg_q, torch.int32, "wg_q"), _ptr(wg_s, torch.float16, "wg_s"),
+        _ptr(wu_q, torch.int32, "wu_q"), _ptr(wu_s, torch.float16, "wu_s"),
+        _ptr(wd_q, torch.int32, "wd_q"), _ptr(wd_s, torch.float16, "wd_s"),
+        _ptr(sorted_slots, torch.int32, "sorted_slots"),
+        _ptr(expert_offsets, torch.int32, "expert_offsets"), sI, sg, su, sd,
         _ptr(slot_out, torch.float32, "slot_out"), so, _stream(stream)))
 
 

@@ -92,6 +92,7 @@
 // FP16 block: one MFMA step, lane group g takes k = 8g .. 8g+7 of the block.
 #include <algorithm>
 #include <atomic>
+#include <mutex>
 #include <type_traits>
 
 #include "smoe_blocks.hpp"  // route_check (the layer call validates every step)
@@ -895,6 +896,53 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
   clear_share();
 }
 
+// Zero n16 16-byte words from p (the no-allocation entry point's workspace;
+// a kernel rather than a memset so that the call stays graph-capturable).
+__global__ __launch_bounds__(256) void zero_kernel(f32x4* __restrict__ p, long long n16) {
+  const long long stride = static_cast<long long>(gridDim.x) * blockDim.x;
+  for (long long i = static_cast<long long>(blockIdx.x) * blockDim.x + threadIdx.x; i < n16;
+       i += stride)
+    p[i] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+}
+
+}  // namespace
+}  // namespace smoe
+
+// Workspace of smoe_w4a16_expert_ffn_noalloc: one copy per device, held until
+// the process ends. Host code never passes this name to a kernel (in host
+// code it is only a stand-in for the symbol): the device address comes from
+// hipGetSymbolAddress, once per device, in noalloc_scratch().
+static __device__ __align__(256) uint8_t scratch[SMOE_NOALLOC_SCRATCH_BYTES];
+
+namespace smoe {
+namespace {
+
+// Device address of `scratch` on the current device (looked up once per
+// device with that device current), or null with the error text set.
+void* noalloc_scratch() {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static void* addr[kMaxDevices] = {};
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+    set_error("w4a16_expert_ffn_noalloc: no current device (or device index above %d)",
+              kMaxDevices - 1);
+    return nullptr;
+  }
+  std::lock_guard<std::mutex> lock(mu);
+  if (addr[dev] == nullptr) {
+    void* p = nullptr;
+    const hipError_t err = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (err != hipSuccess || p == nullptr) {
+      set_error("w4a16_expert_ffn_noalloc: hipGetSymbolAddress failed on device %d: %s", dev,
+                hipGetErrorString(err));
+      return nullptr;
+    }
+    addr[dev] = p;
+  }
+  return addr[dev];
+}
+
 // ------------------------------------------------------------------ host side
 
 int cu_count() {
@@ -1149,13 +1197,16 @@ smoe_status build_plans(const char* who, StagePlans& p, const void* x, int T, in
   return SMOE_OK;
 }
 
+// clear_ws: zero the workspace bytes this call uses before its launches
+// (the no-allocation entry point, whose workspace other calls share).
 smoe_status w4a16_ffn(int tiled,
     const void* x, int T, int k, int E, int H, int I, int group_size, const uint32_t* wg_q,
     const void* wg_s, const uint32_t* wu_q, const void* wu_s, const uint32_t* wd_q,
     const void* wd_s, const int32_t* sorted_slots, const int32_t* expert_offsets, int shared_I,
     const void* shared_wg, const void* shared_wu, const void* shared_wd, void* workspace,
-    size_t workspace_bytes_, float* slot_out, float* shared_out, void* stream) {
-  const char* who = tiled ? "w4a16_expert_ffn_tiled" : "w4a16_expert_ffn";
+    size_t workspace_bytes_, float* slot_out, float* shared_out, void* stream,
+    bool clear_ws = false, const char* who = nullptr) {
+  if (who == nullptr) who = tiled ? "w4a16_expert_ffn_tiled" : "w4a16_expert_ffn";
   SMOE_REQUIRE(group_size == 32 || group_size == 64 || group_size == 128, SMOE_EUNSUPPORTED,
                "%s: group size must be 32, 64 or 128 (got %d)", who, group_size);
   smoe_status st = check_common(who, x, T, k, E, H, I, sorted_slots, expert_offsets, shared_I,
@@ -1182,6 +1233,14 @@ smoe_status w4a16_ffn(int tiled,
                    shared_wg, shared_wu, shared_wd, slot_out, shared_out);
   if (st != SMOE_OK) return st;
   hipStream_t s = as_stream(stream);
+  if (clear_ws) {
+    const long long n16 = static_cast<long long>(workspace_bytes(T, k, I, shared_I) / 16);
+    const int grid = static_cast<int>(std::min<long long>((n16 + 255) / 256, 2048));
+    hipLaunchKernelGGL(zero_kernel, dim3(grid), dim3(256), 0, s,
+                       static_cast<f32x4*>(workspace), n16);
+    st = check_launch(who);
+    if (st != SMOE_OK) return st;
+  }
 #define SMOE_FFN_NC(G) \
   (p.nc == 2 ? launch_ffn<kInt4, G, 2>(p, s) : launch_ffn<kInt4, G, 1>(p, s))
   switch (group_size) {
@@ -1301,6 +1360,38 @@ extern "C" smoe_status smoe_w4a16_expert_ffn(
   return w4a16_ffn(0, x, T, k, E, H, I, group_size, wg_q, wg_s, wu_q, wu_s, wd_q, wd_s, sorted_slots,
                    expert_offsets, shared_I, shared_wg, shared_wu, shared_wd, workspace,
                    workspace_bytes_, slot_out, shared_out, stream);
+}
+
+extern "C" smoe_status smoe_w4a16_expert_ffn_noalloc(
+    const void* x, int T, int k, int E, int H, int I, int group_size, const uint32_t* wg_q,
+    const void* wg_s, const uint32_t* wu_q, const void* wu_s, const uint32_t* wd_q,
+    const void* wd_s, const int32_t* sorted_slots, const int32_t* expert_offsets, int shared_I,
+    const void* shared_wg, const void* shared_wu, const void* shared_wd, float* slot_out,
+    float* shared_out, void* stream) {
+  clear_error();
+  const char* who = "w4a16_expert_ffn_noalloc";
+  SMOE_REQUIRE(group_size == 32 || group_size == 64 || group_size == 128, SMOE_EUNSUPPORTED,
+               "%s: group size must be 32, 64 or 128 (got %d)", who, group_size);
+  // the size limit first: it needs no device
+  if (T > 0 && k > 0 && E > 0 && H > 0 && I > 0 && shared_I >= 0) {
+    const size_t need = workspace_bytes(T, k, I, shared_I);
+    SMOE_REQUIRE(need <= SMOE_NOALLOC_SCRATCH_BYTES, SMOE_EUNSUPPORTED,
+                 "%s: the window needs %zu bytes of workspace, above the %zu bytes of the "
+                 "library's static workspace (T=%d k=%d I=%d shared_I=%d); use "
+                 "smoe_w4a16_expert_ffn with a workspace of that size",
+                 who, need, static_cast<size_t>(SMOE_NOALLOC_SCRATCH_BYTES), T, k, I, shared_I);
+  }
+  // every other check on host values before the device is touched
+  smoe_status st = check_common(who, x, T, k, E, H, I, sorted_slots, expert_offsets, shared_I,
+                                shared_wg, shared_wu, shared_wd, reinterpret_cast<void*>(256),
+                                SMOE_NOALLOC_SCRATCH_BYTES, slot_out, shared_out);
+  if (st != SMOE_OK || T == 0) return st;
+  void* ws = noalloc_scratch();
+  if (ws == nullptr) return SMOE_EHIP;
+  return w4a16_ffn(0, x, T, k, E, H, I, group_size, wg_q, wg_s, wu_q, wu_s, wd_q, wd_s,
+                   sorted_slots, expert_offsets, shared_I, shared_wg, shared_wu, shared_wd, ws,
+                   SMOE_NOALLOC_SCRATCH_BYTES, slot_out, shared_out, stream, /*clear_ws=*/true,
+                   who);
 }
 
 extern "C" smoe_status smoe_w4a16_expert_ffn_tiled(

@@ -301,3 +301,16 @@ def test_tile_weights_checks_scales_before_any_launch(lib):
     assert f(a, c, 2, 16, 256, 128, b, c + 16, N) == EINVAL
     assert b"scales_tiled must not overlap" in lib.smoe_last_error()
 
+
+
+def test_noalloc_ffn_refuses_oversize_before_touching_a_device(lib):
+    # 544 tokens x top-6 need about 98 MB of workspace, above the library's
+    # static 16 MiB: refused from host values alone (no GPU here)
+    f = lib.smoe_w4a16_expert_ffn_noalloc
+    f.argtypes = ([ctypes.c_void_p] + [ctypes.c_int] * 6 + [ctypes.c_void_p] * 8 +
+                  [ctypes.c_int] + [ctypes.c_void_p] * 6)
+    w = [16] * 8
+    assert f(16, 544, 6, 64, 2048, 1408, 128, *w, 0, N, N, N, 16, N, N) == EUNSUPPORTED
+    assert b"static workspace" in lib.smoe_last_error()
+    assert f(16, 17, 6, 64, 2048, 1408, 96, *w, 0, N, N, N, 16, N, N) == EUNSUPPORTED  # G
+    assert f(N, 0, 6, 64, 2048, 1408, 128, *w, 0, N, N, N, 16, N, N) == 0  # empty window
