@@ -95,20 +95,13 @@
 #include <mutex>
 #include <type_traits>
 
+#include "ffn_device.hpp"
+#include "ffn_stream.hpp"
 #include "smoe_blocks.hpp"  // route_check (the layer call validates every step)
 
 namespace smoe {
 namespace {
 
-typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
-typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-typedef int i32x4 __attribute__((ext_vector_type(4)));
-
-enum { kInt4 = 0, kFp16 = 1 };
-constexpr int kBlockBytes = 64;            // bytes of one weight row per block
 constexpr int kWavesPerWg = 8;             // 4 waves per SIMD at two workgroups per CU
 constexpr int kThreads = kWavesPerWg * kWave;
 constexpr int kMaxChunk = 32;              // slots per chunk (two MFMA column groups)
@@ -190,48 +183,6 @@ struct FfnArgs {
   int xres;                     // stage 1: all T rows of x held in LDS for the whole launch
   Group grp[2];
 };
-
-template <typename T, typename U>
-__device__ __forceinline__ T bitcast(U u) {
-  static_assert(sizeof(T) == sizeof(U), "size");
-  T t;
-  __builtin_memcpy(&t, &u, sizeof(T));
-  return t;
-}
-
-__device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
-
-// Eight INT4 codes of one word -> (c - 8) as fp16, in k order 0,4,1,5,2,6,3,7.
-// lo = 0x000F000F, hi = 0x00F000F0 and magic = 0x64006400 are passed in
-// registers so that each mask-and-or is a single v_and_or_b32. A code in
-// bits 4..7 of a half reads as 1024 + 16 c, and (1024 + 16 c) / 16 - 72 =
-// c - 8 is exact in one fp16 fma, so one shift (by 8) serves all four
-// pairs.
-__device__ __forceinline__ f16x8 dequant_word(uint32_t w, uint32_t lo, uint32_t hi,
-                                              uint32_t magic) {
-  const f16x2 bias = {static_cast<_Float16>(1032.0f), static_cast<_Float16>(1032.0f)};
-  const f16x2 sixteenth = {static_cast<_Float16>(0.0625f), static_cast<_Float16>(0.0625f)};
-  const f16x2 bias16 = {static_cast<_Float16>(-72.0f), static_cast<_Float16>(-72.0f)};
-  const uint32_t w8 = w >> 8;
-  const f16x2 v0 = bitcast<f16x2>((w & lo) | magic) - bias;
-  const f16x2 v1 = __builtin_elementwise_fma(bitcast<f16x2>((w & hi) | magic), sixteenth, bias16);
-  const f16x2 v2 = bitcast<f16x2>((w8 & lo) | magic) - bias;
-  const f16x2 v3 = __builtin_elementwise_fma(bitcast<f16x2>((w8 & hi) | magic), sixteenth, bias16);
-  f16x8 r;
-  r[0] = v0[0]; r[1] = v0[1]; r[2] = v1[0]; r[3] = v1[1];
-  r[4] = v2[0]; r[5] = v2[1]; r[6] = v3[0]; r[7] = v3[1];
-  return r;
-}
-
-// Natural k order 0..7 -> 0,4,1,5,2,6,3,7 (matches dequant_word).
-__device__ __forceinline__ u32x4 permute_k8(u32x4 d) {
-  u32x4 e;
-  e[0] = (d[0] & 0xFFFFu) | (d[2] << 16);
-  e[1] = (d[0] >> 16) | (d[2] & 0xFFFF0000u);
-  e[2] = (d[1] & 0xFFFFu) | (d[3] << 16);
-  e[3] = (d[1] >> 16) | (d[3] & 0xFFFF0000u);
-  return e;
-}
 
 // One item: part `part` of row tile `tile` of chunk `chunk` of group `grp`
 // (expert e, positions [seg0, seg0 + m) of the group's slots).
@@ -580,9 +531,11 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
     }
   };
   // One FP16 block (32 k) at k offset kk of the staged rows.
-  // (resident x rows are k-permuted for the INT4 groups; the FP16 weights
-  // then take the same permutation)
-  constexpr bool bperm = WK == kInt4 && xres;
+  // (resident x rows are k-permuted for row-major INT4 groups; the FP16
+  // weights then take the same permutation. Tiled INT4 words dequantise in
+  // natural k order, so with tiled weights nothing is permuted.)
+  const bool xperm = WK == kInt4 && a.grp[0].tiled == 0;
+  const bool bperm = xres && xperm;
   auto compute_fp16 = [&](const u32x4 (&r)[2], int kk, auto nce_tag) {
     constexpr int NCE = decltype(nce_tag)::value;
     f16x8 B[2];
@@ -659,7 +612,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
       if (tid < it.m) s_slots[tid] = a.sorted_slots[it.seg0 + tid];
       __syncthreads();
     }
-    const bool perm = WK == kInt4 && gr.fmt == kInt4;
+    const bool perm = WK == kInt4 && gr.fmt == kInt4 && gr.tiled == 0;
     const int npr = (k1 - k0) / 8;  // 16-byte pieces per row
     const int tot = it.m * npr;
     for (int base = 0; base < tot; base += NB * kThreads) {
@@ -703,7 +656,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
 #pragma unroll
       for (int j = 0; j < NB; ++j)
         if (dst[j] >= 0)
-          *reinterpret_cast<u32x4*>(xs + dst[j]) = WK == kInt4 ? permute_k8(v[j]) : v[j];
+          *reinterpret_cast<u32x4*>(xs + dst[j]) = xperm ? permute_k8(v[j]) : v[j];
     }
     __syncthreads();
   };
@@ -976,13 +929,17 @@ int tiles_of(long long N, int rows_per_wave) {
 }
 
 // Workspace layout: call counter (2 words, padded to 256 bytes) | two g/u
-// buffers, each [2][S][I] fp32 (routed) followed by [2][T][Is] fp32 (shared).
+// buffers, each [2][S][I] fp32 (routed) followed by [2][T][Is] fp32 (shared)
+// | the streaming FFN's fp16 h ([S][I] routed, then [T][Is] shared).
 constexpr size_t kEpochBytes = 256;
 long long gu_floats(long long T, long long k, long long I, long long Is) {
   return 2 * T * k * I + 2 * T * Is;
 }
-size_t workspace_bytes(long long T, long long k, long long I, long long Is) {
+size_t gu_region_bytes(long long T, long long k, long long I, long long Is) {
   return kEpochBytes + static_cast<size_t>(2 * gu_floats(T, k, I, Is)) * sizeof(float);
+}
+size_t workspace_bytes(long long T, long long k, long long I, long long Is) {
+  return gu_region_bytes(T, k, I, Is) + stream_h_bytes(T, k, I, Is);
 }
 
 // Weights of one group as the entry points hand them over.
@@ -1197,6 +1154,35 @@ smoe_status build_plans(const char* who, StagePlans& p, const void* x, int T, in
   return SMOE_OK;
 }
 
+#ifndef SMOE_STREAM_FFN
+#define SMOE_STREAM_FFN 0
+#endif
+
+// Tiled weights and a short window: the streaming FFN (ffn_stream.hip), whose
+// fp16 h lives in the last region of the workspace. kStreamNotApplicable
+// (nothing enqueued) otherwise.
+smoe_status try_stream(const char* who, const GroupWeights& r, const void* x, int T, int k,
+                       int H, const int32_t* sorted_slots, const int32_t* offsets, int shared_I,
+                       const void* swg, const void* swu, const void* swd, void* workspace,
+                       float* slot_out, float* shared_out, hipStream_t s) {
+  if (!SMOE_STREAM_FFN || !r.tiled) return kStreamNotApplicable;
+  StreamCall c{};
+  c.fmt = r.fmt;
+  c.G = r.G;
+  c.x = x;
+  c.T = T; c.k = k; c.E = r.E; c.H = H; c.I = r.I;
+  c.wg = r.wg; c.wu = r.wu; c.wd = r.wd;
+  c.sg = r.sg; c.su = r.su; c.sd = r.sd;
+  c.Is = shared_I;
+  c.swg = swg; c.swu = swu; c.swd = swd;
+  c.sorted_slots = sorted_slots;
+  c.offsets = offsets;
+  c.h = static_cast<uint8_t*>(workspace) + gu_region_bytes(T, k, r.I, shared_I);
+  c.slot_out = slot_out;
+  c.shared_out = shared_I > 0 ? shared_out : nullptr;
+  return stream_ffn(c, s, who);
+}
+
 // clear_ws: zero the workspace bytes this call uses before its launches
 // (the no-allocation entry point, whose workspace other calls share).
 smoe_status w4a16_ffn(int tiled,
@@ -1233,8 +1219,11 @@ smoe_status w4a16_ffn(int tiled,
                    shared_wg, shared_wu, shared_wd, slot_out, shared_out);
   if (st != SMOE_OK) return st;
   hipStream_t s = as_stream(stream);
+  st = try_stream(who, r, x, T, k, H, sorted_slots, expert_offsets, shared_I, shared_wg,
+                  shared_wu, shared_wd, workspace, slot_out, shared_out, s);
+  if (st != kStreamNotApplicable) return st;
   if (clear_ws) {
-    const long long n16 = static_cast<long long>(workspace_bytes(T, k, I, shared_I) / 16);
+    const long long n16 = static_cast<long long>(gu_region_bytes(T, k, I, shared_I) / 16);
     const int grid = static_cast<int>(std::min<long long>((n16 + 255) / 256, 2048));
     hipLaunchKernelGGL(zero_kernel, dim3(grid), dim3(256), 0, s,
                        static_cast<f32x4*>(workspace), n16);
@@ -1275,6 +1264,9 @@ smoe_status fp16_ffn(int tiled,
                    shared_wg, shared_wu, shared_wd, slot_out, shared_out);
   if (st != SMOE_OK) return st;
   hipStream_t s = as_stream(stream);
+  st = try_stream(who, r, x, T, k, H, sorted_slots, expert_offsets, shared_I, shared_wg,
+                  shared_wu, shared_wd, workspace, slot_out, shared_out, s);
+  if (st != kStreamNotApplicable) return st;
   return p.nc == 2 ? launch_ffn<kFp16, 128, 2>(p, s) : launch_ffn<kFp16, 128, 1>(p, s);
 }
 

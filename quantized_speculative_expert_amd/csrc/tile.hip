@@ -8,7 +8,11 @@
 //   byte 16 * (16 g + r) + 4 q .. +3 = word W(g, q) of row 16 sl + r, block b
 // with W(g, q) = 4 g + q for FP16 and INT4 G = 128, and the FFN's step-order
 // word of lane group g for INT4 G = 64 and 32 (int4_word). Slices follow
-// each other in row order, blocks in k order within a slice. INT4 scales:
+// each other in row order, blocks in k order within a slice. Each INT4 word
+// has its nibbles unzipped: the codes of k = 8w + 2p sit in nibble positions
+// p = 0..3 and those of k = 8w + 2p + 1 in positions 4 + p, so that the
+// FFN's dequantisation, which pairs positions (0, 4), (1, 5), (2, 6), (3, 7),
+// yields the eight values in natural k order. INT4 scales:
 // for each (e, sl, b), 16 runs of NQ = 128 / G values, run r holding the
 // scales of row 16 sl + r that fall in block b.
 //
@@ -22,7 +26,19 @@ namespace {
 
 constexpr int kTileThreads = 256;
 
-template <int G>
+// Natural nibble order (k = 8w + j in nibble j) -> even k in nibbles 0..3,
+// odd k in nibbles 4..7.
+__device__ __forceinline__ uint32_t unzip_nibbles(uint32_t w) {
+  uint32_t r = 0;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const int pos = (j & 1) ? 4 + (j >> 1) : (j >> 1);
+    r |= ((w >> (4 * j)) & 0xFu) << (4 * pos);
+  }
+  return r;
+}
+
+template <int G, bool UNZIP>
 __global__ __launch_bounds__(kTileThreads) void tile_codes_kernel(
     const uint32_t* __restrict__ src, uint32_t* __restrict__ dst, long long n_chunks, int nblk) {
   const long long i = static_cast<long long>(blockIdx.x) * kTileThreads + threadIdx.x;
@@ -38,7 +54,10 @@ __global__ __launch_bounds__(kTileThreads) void tile_codes_kernel(
   const uint32_t* s = src + (row * nblk + b) * 16;
   uint32_t w[4];
 #pragma unroll
-  for (int q = 0; q < 4; ++q) w[q] = s[int4_word(G, g, q)];
+  for (int q = 0; q < 4; ++q) {
+    w[q] = s[int4_word(G, g, q)];
+    if (UNZIP) w[q] = unzip_nibbles(w[q]);
+  }
   reinterpret_cast<uint4*>(dst)[i] = uint4{w[0], w[1], w[2], w[3]};
 }
 
@@ -103,16 +122,20 @@ extern "C" smoe_status smoe_tile_weights(const void* w, const void* scales, int 
   uint32_t* dst = static_cast<uint32_t*>(w_tiled);
   switch (group_size) {
     case 32:
-      hipLaunchKernelGGL(tile_codes_kernel<32>, dim3(grid_of(n_chunks)), dim3(kTileThreads), 0,
-                         st, src, dst, n_chunks, nblk);
+      hipLaunchKernelGGL((tile_codes_kernel<32, true>), dim3(grid_of(n_chunks)),
+                         dim3(kTileThreads), 0, st, src, dst, n_chunks, nblk);
       break;
     case 64:
-      hipLaunchKernelGGL(tile_codes_kernel<64>, dim3(grid_of(n_chunks)), dim3(kTileThreads), 0,
-                         st, src, dst, n_chunks, nblk);
+      hipLaunchKernelGGL((tile_codes_kernel<64, true>), dim3(grid_of(n_chunks)),
+                         dim3(kTileThreads), 0, st, src, dst, n_chunks, nblk);
       break;
-    default:
-      hipLaunchKernelGGL(tile_codes_kernel<128>, dim3(grid_of(n_chunks)), dim3(kTileThreads), 0,
-                         st, src, dst, n_chunks, nblk);
+    case 128:
+      hipLaunchKernelGGL((tile_codes_kernel<128, true>), dim3(grid_of(n_chunks)),
+                         dim3(kTileThreads), 0, st, src, dst, n_chunks, nblk);
+      break;
+    default:  // FP16 values: words moved whole
+      hipLaunchKernelGGL((tile_codes_kernel<128, false>), dim3(grid_of(n_chunks)),
+                         dim3(kTileThreads), 0, st, src, dst, n_chunks, nblk);
   }
   smoe_status s = check_launch(who);
   if (s != SMOE_OK || !int4) return s;

@@ -378,7 +378,15 @@ def tile_dev(smoe, w, s, E, N, K, G):
 def tiled_layout_np(w, s, G):
     """The tiled layout written out from its definition with numpy index
     arithmetic: w uint32 words [E][N][nb * 16] (K = 128 nb INT4 codes, or
-    32 nb FP16 values as words), s [E][N][nb * 128 / G] or None."""
+    32 nb FP16 values as words), s [E][N][nb * 128 / G] or None. INT4 words
+    get their nibbles unzipped (k = 8w + 2p in position p, k = 8w + 2p + 1 in
+    position 4 + p)."""
+    if G != 0:
+        nib = [(w >> np.uint32(4 * j)) & np.uint32(0xF) for j in range(8)]
+        w = np.zeros_like(w)
+        for j in range(8):
+            pos = 4 + j // 2 if j % 2 else j // 2
+            w |= nib[j] << np.uint32(4 * pos)
     E, N, words = w.shape
     nb = words // 16
     Gw = 128 if G == 0 else G
