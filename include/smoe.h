@@ -176,14 +176,28 @@ smoe_status smoe_route_align_elb(const void* x, const float* w_router, const flo
  * the gate and up projections of every slot, and a small call counter.
  * Returns 0 for invalid sizes.
  *
- * Workspace contract: the caller fills the buffer with zeros before its
- * first use, and again before using it with a different (T, k, I,
- * shared_I). The FFN calls keep it consistent from one call to the next
- * (each call clears what the following call accumulates into), so it must
- * not be written between calls, and two calls that share a workspace must
- * not run concurrently.
+ * Workspace contract: the caller fills the buffer with zeros
+ * (smoe_ffn_workspace_clear, or any fill) before its first use, and again
+ * before using it with a different (T, k, I, shared_I). The FFN calls keep
+ * it consistent from one call to the next (each call clears what the
+ * following call accumulates into), so it must not be written between
+ * calls, and two calls that share a workspace must not run concurrently.
+ *
+ * Misuse is detected on the device: the first call after zeroing stamps
+ * the buffer with its (T, k, I, shared_I); a later call of another shape
+ * marks the buffer spoiled, and from then on every FFN call on it writes
+ * NaN to all of slot_out and shared_out instead of its results, until the
+ * buffer is zeroed again.
  */
 size_t smoe_ffn_workspace_bytes(int T, int k, int E, int H, int I, int shared_I);
+
+/*
+ * Zero a FFN workspace on `stream` with a fill kernel (no memset node, so
+ * the call can be captured into a HIP graph). workspace: device, 256-byte
+ * aligned; workspace_bytes: a multiple of 16 (smoe_ffn_workspace_bytes
+ * values are).
+ */
+smoe_status smoe_ffn_workspace_clear(void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * Fused multi-expert W4A16 expert FFN (draft pass).   [P] fused multi-expert
@@ -294,6 +308,46 @@ smoe_status smoe_fp16_expert_ffn(const void* x, int T, int k, int E, int H, int 
                                  const void* shared_wd,
                                  void* workspace, size_t workspace_bytes,
                                  float* slot_out, float* shared_out, void* stream);
+
+/*
+ * smoe_fp16_expert_ffn over weights addressed through a table: the FFN of
+ * the verification pass when the routed experts live in a pool of device
+ * slots (an expert cache) rather than at their own index.   [P] Verification
+ * Expert Cache Residency Manager paragraph (cache-hit experts go to the
+ * compute queue first, cache-miss experts join it as their copies land) and
+ * cache-aware execution schedule paragraph (compute the resident expert's
+ * sub-batch while the missing one is copied); [D] "Predictive I/O
+ * Orchestrator" (expert_cache: slot ownership, resident experts first).
+ *
+ * Same computation, alignment, shared-expert option and workspace contract
+ * as smoe_fp16_expert_ffn, except:
+ *   - the weights of routed expert e are matrix expert_matrix[e] of each of
+ *     wg, wu and wd (address base + expert_matrix[e] * the bytes of one
+ *     matrix), which must each hold n_matrices matrices;
+ *   - an expert whose entry is negative or >= n_matrices is left out of the
+ *     call: its slots are neither computed nor written. Only the rows of
+ *     slot_out of the call's experts are written; every other row keeps what
+ *     it held, so several calls over disjoint expert sets fill one slot_out
+ *     (the rows of slots the alignment dropped are not written either).
+ *
+ *   expert_matrix  int32 [E], HOST memory, read during the call (the table
+ *                  travels in the launch arguments, so a captured graph
+ *                  keeps the values it had at capture)
+ *   tiled          1: wg, wu, wd in the layout of smoe_tile_weights (each
+ *                  matrix tiled on its own), 0: row-major
+ * A pool that keeps an expert's three matrices together, [slots][3][matrix],
+ * is addressed with wg = pool, wu = pool + one matrix, wd = pool + two
+ * matrices, expert_matrix[e] = 3 * slot and n_matrices = 3 * slots - 2.
+ */
+smoe_status smoe_fp16_expert_ffn_mapped(const void* x, int T, int k, int E, int H, int I,
+                                        const void* wg, const void* wu, const void* wd,
+                                        int tiled, int n_matrices, const int32_t* expert_matrix,
+                                        const int32_t* sorted_slots,
+                                        const int32_t* expert_offsets, int shared_I,
+                                        const void* shared_wg, const void* shared_wu,
+                                        const void* shared_wd, void* workspace,
+                                        size_t workspace_bytes, float* slot_out,
+                                        float* shared_out, void* stream);
 
 /*
  * Weighted combine back to token order.               [P] expert-wise
@@ -429,6 +483,153 @@ smoe_status smoe_moe_layer_w4a16_tiled(const void* x, const float* w_router,
                                        void* workspace, size_t workspace_bytes,
                                        float* slot_out, float* shared_out, void* y,
                                        void* stream);
+
+/* ====================================================================
+ * Expert cache of the verification pass and the prefetch planner (host
+ * runtime).   [P] Layer-Aware Prefetch Planner paragraphs (Cold Start,
+ * Prefetch Overlap, Final Cleanup; top-M snapshot at each chunk boundary,
+ * the experts not yet cached form the next host-to-device batch, the next
+ * boundary chosen so the chunk's draft compute matches the batch's transfer
+ * time); Verification Expert Cache Residency Manager paragraph (hits
+ * computed first, misses copied and computed as they land, slots protected
+ * until their expert's tokens are done); cache-aware execution schedule
+ * paragraph; Overlap-Oriented Parallelism Optimizer paragraph (compute and
+ * I/O streams, events for readiness and slot reuse, pinned host memory,
+ * asynchronous copies); [D] "Predictive I/O Orchestrator" (expert_cache,
+ * prefetch_planner; residency is a per-layer slot budget).
+ *
+ * A cache holds, per layer, M device slots of one expert each (its three
+ * FP16 matrices). Its state lives on the host: the expert of each slot (-1
+ * empty), the clock value of each slot's last use, and whether the current
+ * window's predictions claimed the slot. Decisions:
+ *   - replacement: an empty slot first (lowest index), else the least
+ *     recently used one (ties to the lower index) among those allowed;
+ *   - the clock advances by one for each prefetch call per layer (every slot
+ *     it claims or loads gets that value), for the hit group of a
+ *     verification, and for each miss's computation.
+ * Functions taking a cache are not thread-safe on the same cache. These
+ * calls (unlike the kernels above) allocate host memory and HIP events in
+ * smoe_cache_create and free them in smoe_cache_destroy.
+ * ==================================================================== */
+typedef struct smoe_expert_cache smoe_expert_cache;
+
+/*
+ * Create a cache of L layers, E experts per layer, M slots per layer.
+ *   pool          device [L][M][expert_bytes], caller-owned: slot s of
+ *                 layer l at pool + (l*M + s) * expert_bytes
+ *   host_experts  host [L][E][expert_bytes] (allocate with hipHostMalloc so
+ *                 the copies are asynchronous), caller-owned
+ * Both NULL: a cache that only takes decisions (no device, no copies; the
+ * verify_layer call is then refused). expert_bytes: a multiple of 16; for
+ * verify_layer it must be 3 * I * H * 2 (wg [I][H], wu [I][H], wd [H][I]
+ * fp16, in this order, each row-major or each tiled by smoe_tile_weights).
+ * Creates two HIP events per slot on the current device.
+ */
+smoe_status smoe_cache_create(int L, int E, int M, size_t expert_bytes, void* pool,
+                              const void* host_experts, smoe_expert_cache** cache);
+smoe_status smoe_cache_destroy(smoe_expert_cache* cache);
+
+/* Start a draft window: no slot is claimed. */
+smoe_status smoe_cache_begin_window(smoe_expert_cache* cache);
+
+/* Copy the state out (host arrays [L][M]; any may be NULL). */
+smoe_status smoe_cache_state(const smoe_expert_cache* cache, int32_t* slot_expert,
+                             int64_t* last_use, int32_t* claimed, int64_t* clock);
+
+/*
+ * Install a state (host arrays [L][M]: the expert of each slot or -1, each
+ * slot's last use in [0, clock]); no slot is claimed. With device memory,
+ * every cached expert is copied into its slot on copy_stream.
+ */
+smoe_status smoe_cache_set_state(smoe_expert_cache* cache, const int32_t* slot_expert,
+                                 const int64_t* last_use, int64_t clock, void* copy_stream);
+
+/*
+ * Prefetch at a chunk boundary, from the ELB's top-M plan
+ * (smoe_elb_accumulate_topm's plan_ids / plan_counts, copied to the host).
+ * For each layer l: the selection is the plan's experts with a positive
+ * count, in ranking order, at most M of them; the selected experts already
+ * cached are claimed first; then each selected expert not cached takes, in
+ * ranking order, a slot that is not claimed (replacement rule above) and is
+ * claimed, until no unclaimed slot is left. A claimed slot is not taken by
+ * another expert until the next window.
+ *   plan_ids, plan_counts  host int32 [L][plan_M]
+ *   loads     host int32 [L*M][4] (out): (layer, expert, slot, evicted expert
+ *             or -1) of every copy, in the order they were decided
+ *   n_loads   (out) number of loads; full (out, may be NULL): 1 if no slot
+ *             of any layer is left unclaimed (the planner's Final Cleanup)
+ * With device memory each load is enqueued on copy_stream (after the last
+ * computation that read the slot).
+ */
+smoe_status smoe_cache_prefetch(smoe_expert_cache* cache, const int32_t* plan_ids,
+                                const int32_t* plan_counts, int plan_M, int32_t* loads,
+                                int* n_loads, int* full, void* copy_stream);
+
+/*
+ * The planner's next chunk boundary after b for a batch of n_transfer
+ * experts: b + n with the smallest n >= 1 such that n * draft_us_per_token
+ * >= t_io, where t_io = n_transfer * expert_bytes / (h2d_gb_per_s * 1000)
+ * microseconds (double precision, in this order); capped at K.
+ */
+smoe_status smoe_prefetch_next_boundary(int b, int K, int n_transfer, double expert_bytes,
+                                        double h2d_gb_per_s, double draft_us_per_token,
+                                        int* next_b);
+
+/*
+ * Verification decisions for one layer (no device work): expert_counts
+ * host int32 [E] (tokens the target router sent to each expert). The
+ * required experts (count > 0) split into hits (cached) and misses. The
+ * schedule, host int32 [E][5] (out), lists in compute order
+ * (expert, slot, kind, evicted, wait):
+ *   - first the hits in ascending expert ID: kind 0, evicted = expert,
+ *     wait -1; they form one computation (group 0) and their slots are
+ *     protected until it ends;
+ *   - then the misses in ascending expert ID, each its own computation
+ *     (group 1 + j for the j-th miss): kind 1, the slot it is copied into,
+ *     the expert it evicts (-1 for an empty slot), and wait = -1 when the
+ *     slot was free or unprotected (replacement rule), else the group whose
+ *     end releases it: slots come back in the order their computations end
+ *     (the hit group's slots in slot order, then each miss's slot).
+ * The state is updated (slots, last uses).
+ */
+smoe_status smoe_cache_verify_plan(smoe_expert_cache* cache, int layer,
+                                   const int32_t* expert_counts, int32_t* schedule,
+                                   int* n_schedule);
+
+/*
+ * The verification FFN of one layer with the cache: the decisions of
+ * smoe_cache_verify_plan, then, on compute_stream, the hit group's
+ * smoe_fp16_expert_ffn_mapped call (with the FP16 shared experts when
+ * shared_I > 0) and, for each miss, its copy on copy_stream followed by its
+ * own mapped FFN call on compute_stream. Events order every copy after the
+ * slot's last computation and every computation after its slot's copy, so
+ * the hits run while the misses are copied; nothing waits on the host.
+ *
+ *   expert_counts   host int32 [E] (this layer's alignment counts, which the
+ *                   caller copied back from the device)
+ *   x .. shared_out as in smoe_fp16_expert_ffn (T, k, H, I; sorted_slots and
+ *                   expert_offsets from the alignment of the target router's
+ *                   IDs; tiled as in smoe_fp16_expert_ffn_mapped)
+ *   workspace_shared  FFN workspace for (T, k, I, shared_I) (hit group), or
+ *                   NULL when shared_I = 0; workspace_routed a distinct one
+ *                   for (T, k, I, 0) (misses). Each follows the workspace
+ *                   contract.
+ *   schedule, n_schedule  as in smoe_cache_verify_plan (may be NULL)
+ * slot_out rows of every required expert's slots are written (the call's
+ * experts are all the target router's); shared_out as usual. Checks run
+ * before the state changes or anything is enqueued; a HIP failure after
+ * that returns SMOE_EHIP with the decisions already taken.
+ */
+smoe_status smoe_cache_verify_layer(smoe_expert_cache* cache, int layer,
+                                    const int32_t* expert_counts, const void* x, int T, int k,
+                                    int H, int I, int tiled, const int32_t* sorted_slots,
+                                    const int32_t* expert_offsets, int shared_I,
+                                    const void* shared_wg, const void* shared_wu,
+                                    const void* shared_wd, void* workspace_shared,
+                                    size_t workspace_shared_bytes, void* workspace_routed,
+                                    size_t workspace_routed_bytes, float* slot_out,
+                                    float* shared_out, int32_t* schedule, int* n_schedule,
+                                    void* compute_stream, void* copy_stream);
 
 #ifdef __cplusplus
 }

@@ -54,6 +54,20 @@ _SIGNATURES = {
     "smoe_tile_weights": (_i, [_p, _p, _i, _i, _i, _i, _p, _p, _p]),
     "smoe_w4a16_expert_ffn_noalloc": (_i, [_p, _i, _i, _i, _i, _i, _i, _p, _p, _p, _p, _p, _p,
                                            _p, _p, _i, _p, _p, _p, _p, _p, _p]),
+    "smoe_fp16_expert_ffn_mapped": (_i, [_p, _i, _i, _i, _i, _i, _p, _p, _p, _i, _i, _p,
+                                         _p, _p, _i, _p, _p, _p, _p, _sz, _p, _p, _p]),
+    "smoe_ffn_workspace_clear": (_i, [_p, _sz, _p]),
+    "smoe_cache_create": (_i, [_i, _i, _i, _sz, _p, _p, _p]),
+    "smoe_cache_destroy": (_i, [_p]),
+    "smoe_cache_begin_window": (_i, [_p]),
+    "smoe_cache_state": (_i, [_p, _p, _p, _p, _p]),
+    "smoe_cache_set_state": (_i, [_p, _p, _p, ctypes.c_int64, _p]),
+    "smoe_cache_prefetch": (_i, [_p, _p, _p, _i, _p, _p, _p, _p]),
+    "smoe_prefetch_next_boundary": (_i, [_i, _i, _i, ctypes.c_double, ctypes.c_double,
+                                         ctypes.c_double, _p]),
+    "smoe_cache_verify_plan": (_i, [_p, _i, _p, _p, _p]),
+    "smoe_cache_verify_layer": (_i, [_p, _i, _p, _p, _i, _i, _i, _i, _i, _p, _p, _i, _p, _p, _p,
+                                     _p, _sz, _p, _sz, _p, _p, _p, _p, _p, _p]),
 }
 # the tiled-layout calls take the same arguments as their row-major forms
 for _name in ("smoe_w4a16_expert_ffn", "smoe_fp16_expert_ffn", "smoe_moe_layer_w4a16"):
@@ -319,6 +333,38 @@ def smoe_fp16_expert_ffn(x, k: int, E: int, I: int, wg, wu, wd, sorted_slots, ex
         _ptr(slot_out, torch.float32, "slot_out"), so, _stream(stream)))
 
 
+def smoe_fp16_expert_ffn_mapped(x, k: int, E: int, I: int, wg, wu, wd, n_matrices: int,
+                                expert_matrix, sorted_slots, expert_offsets, workspace,
+                                slot_out, shared=None, shared_out=None, stream=None, *,
+                                tiled: bool = False) -> None:
+    """wg, wu, wd: fp16 bases of n_matrices matrices each (views into one pool
+    may overlap); expert_matrix: host int32 [E] (a sequence or NumPy array),
+    the matrix of each expert, -1 = not in this call."""
+    T, H = x.shape
+    sI, sg, su, sd, so = _shared_args(shared, shared_out)
+    for name, t in (("wg", wg), ("wu", wu), ("wd", wd)):
+        _need(t, n_matrices * I * H, name)
+    table = (ctypes.c_int32 * E)(*[int(v) for v in list(expert_matrix)[:E]])
+    if len(list(expert_matrix)) < E:
+        raise ValueError(f"expert_matrix holds {len(list(expert_matrix))} entries, the call needs {E}")
+    _ffn_sizes(T, k, E, H, sI, sorted_slots, expert_offsets, slot_out, shared, shared_out)
+    _check("smoe_fp16_expert_ffn_mapped", _lib.smoe_fp16_expert_ffn_mapped(
+        _ptr(x, torch.float16, "x"), T, k, E, H, I,
+        _ptr(wg, torch.float16, "wg"), _ptr(wu, torch.float16, "wu"),
+        _ptr(wd, torch.float16, "wd"), 1 if tiled else 0, n_matrices,
+        ctypes.cast(table, ctypes.c_void_p),
+        _ptr(sorted_slots, torch.int32, "sorted_slots"),
+        _ptr(expert_offsets, torch.int32, "expert_offsets"), sI, sg, su, sd,
+        _ptr(workspace, torch.uint8, "workspace"), workspace.numel(),
+        _ptr(slot_out, torch.float32, "slot_out"), so, _stream(stream)))
+
+
+def smoe_ffn_workspace_clear(workspace, stream=None) -> None:
+    """Zero a FFN workspace with a fill kernel (graph-capturable)."""
+    _check("smoe_ffn_workspace_clear", _lib.smoe_ffn_workspace_clear(
+        _ptr(workspace, torch.uint8, "workspace"), workspace.numel(), _stream(stream)))
+
+
 def smoe_combine(slot_out, topk_w, shared_out, shared_gate, y, stream=None) -> None:
     T, k = topk_w.shape
     H = y.shape[1]
@@ -425,3 +471,131 @@ def smoe_tile_weights(w, scales, E: int, N: int, K: int, group_size: int, w_tile
         E, N, K, group_size, _ptr(w_tiled, wdt, "w_tiled"),
         _ptr(scales_tiled, torch.float16, "scales_tiled") if group_size else None,
         _stream(stream)))
+
+
+# ---------------------------------------------------------------- expert cache
+# Host arrays cross the boundary as NumPy arrays (C-contiguous, the stated
+# dtype); the cache itself is an opaque handle (an int).
+
+def _np_ptr(a, dtype, name: str):
+    import numpy as np
+    if not isinstance(a, np.ndarray) or a.dtype != dtype or not a.flags.c_contiguous:
+        raise TypeError(f"{name} must be a C-contiguous numpy {np.dtype(dtype).name} array")
+    return a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _host_ptr(t: Optional[torch.Tensor], name: str) -> Optional[int]:
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor) or t.is_cuda or not t.is_contiguous():
+        raise TypeError(f"{name} must be a contiguous host torch.Tensor")
+    return t.data_ptr()
+
+
+def smoe_cache_create(L: int, E: int, M: int, expert_bytes: int, pool=None,
+                      host_experts=None) -> int:
+    """pool: device tensor of >= L*M*expert_bytes bytes; host_experts: host
+    (pinned) tensor of >= L*E*expert_bytes bytes; both None for a cache that
+    only takes decisions."""
+    if pool is not None and pool.numel() * pool.element_size() < L * M * expert_bytes:
+        raise ValueError("pool is smaller than L*M*expert_bytes")
+    if host_experts is not None and (host_experts.numel() * host_experts.element_size()
+                                     < L * E * expert_bytes):
+        raise ValueError("host_experts is smaller than L*E*expert_bytes")
+    h = ctypes.c_void_p()
+    _check("smoe_cache_create", _lib.smoe_cache_create(
+        L, E, M, expert_bytes, _ptr(pool, None, "pool"), _host_ptr(host_experts, "host_experts"),
+        ctypes.byref(h)))
+    return h.value
+
+
+def smoe_cache_destroy(cache: int) -> None:
+    _check("smoe_cache_destroy", _lib.smoe_cache_destroy(cache))
+
+
+def smoe_cache_begin_window(cache: int) -> None:
+    _check("smoe_cache_begin_window", _lib.smoe_cache_begin_window(cache))
+
+
+def smoe_cache_state(cache: int, L: int, M: int):
+    """(slot_expert int32 [L][M], last_use int64 [L][M], claimed int32 [L][M], clock)."""
+    import numpy as np
+    se = np.empty((L, M), np.int32)
+    lu = np.empty((L, M), np.int64)
+    cl = np.empty((L, M), np.int32)
+    clock = ctypes.c_int64()
+    _check("smoe_cache_state", _lib.smoe_cache_state(
+        cache, _np_ptr(se, np.int32, "slot_expert"), _np_ptr(lu, np.int64, "last_use"),
+        _np_ptr(cl, np.int32, "claimed"), ctypes.byref(clock)))
+    return se, lu, cl, clock.value
+
+
+def smoe_cache_set_state(cache: int, slot_expert, last_use, clock: int, copy_stream=None) -> None:
+    import numpy as np
+    _check("smoe_cache_set_state", _lib.smoe_cache_set_state(
+        cache, _np_ptr(slot_expert, np.int32, "slot_expert"),
+        _np_ptr(last_use, np.int64, "last_use"), clock,
+        None if copy_stream is None else _stream(copy_stream)))
+
+
+def smoe_cache_prefetch(cache: int, plan_ids, plan_counts, L: int, M: int, copy_stream=None):
+    """plan_ids / plan_counts: host int32 [L][plan_M]. Returns (loads int32
+    [n][4], full)."""
+    import numpy as np
+    if plan_ids.shape != plan_counts.shape or plan_ids.ndim != 2 or plan_ids.shape[0] != L:
+        raise ValueError("plan_ids and plan_counts must both be [L][plan_M]")
+    loads = np.empty((max(L * M, 1), 4), np.int32)
+    n, full = ctypes.c_int(), ctypes.c_int()
+    _check("smoe_cache_prefetch", _lib.smoe_cache_prefetch(
+        cache, _np_ptr(plan_ids, np.int32, "plan_ids"),
+        _np_ptr(plan_counts, np.int32, "plan_counts"), plan_ids.shape[1],
+        _np_ptr(loads, np.int32, "loads"), ctypes.byref(n), ctypes.byref(full),
+        None if copy_stream is None else _stream(copy_stream)))
+    return loads[:n.value].copy(), bool(full.value)
+
+
+def smoe_prefetch_next_boundary(b: int, K: int, n_transfer: int, expert_bytes: float,
+                                h2d_gb_per_s: float, draft_us_per_token: float) -> int:
+    out = ctypes.c_int()
+    _check("smoe_prefetch_next_boundary", _lib.smoe_prefetch_next_boundary(
+        b, K, n_transfer, float(expert_bytes), float(h2d_gb_per_s), float(draft_us_per_token),
+        ctypes.byref(out)))
+    return out.value
+
+
+def smoe_cache_verify_plan(cache: int, layer: int, expert_counts):
+    """expert_counts: host int32 [E]. Returns the schedule int32 [n][5]."""
+    import numpy as np
+    E = expert_counts.shape[0]
+    sched = np.empty((max(E, 1), 5), np.int32)
+    n = ctypes.c_int()
+    _check("smoe_cache_verify_plan", _lib.smoe_cache_verify_plan(
+        cache, layer, _np_ptr(expert_counts, np.int32, "expert_counts"),
+        _np_ptr(sched, np.int32, "schedule"), ctypes.byref(n)))
+    return sched[:n.value].copy()
+
+
+def smoe_cache_verify_layer(cache: int, layer: int, expert_counts, x, k: int, I: int,
+                            sorted_slots, expert_offsets, workspace_shared, workspace_routed,
+                            slot_out, shared=None, shared_out=None, tiled: bool = False,
+                            compute_stream=None, copy_stream=None):
+    """Returns the schedule int32 [n][5] (see smoe_cache_verify_plan)."""
+    import numpy as np
+    T, H = x.shape
+    E = expert_counts.shape[0]
+    sI, sg, su, sd, so = _shared_args(shared, shared_out)
+    _ffn_sizes(T, k, E, H, sI, sorted_slots, expert_offsets, slot_out, shared, shared_out)
+    sched = np.empty((max(E, 1), 5), np.int32)
+    n = ctypes.c_int()
+    wss = workspace_shared
+    _check("smoe_cache_verify_layer", _lib.smoe_cache_verify_layer(
+        cache, layer, _np_ptr(expert_counts, np.int32, "expert_counts"),
+        _ptr(x, torch.float16, "x"), T, k, H, I, 1 if tiled else 0,
+        _ptr(sorted_slots, torch.int32, "sorted_slots"),
+        _ptr(expert_offsets, torch.int32, "expert_offsets"), sI, sg, su, sd,
+        _ptr(wss, torch.uint8, "workspace_shared"), 0 if wss is None else wss.numel(),
+        _ptr(workspace_routed, torch.uint8, "workspace_routed"), workspace_routed.numel(),
+        _ptr(slot_out, torch.float32, "slot_out"), so,
+        _np_ptr(sched, np.int32, "schedule"), ctypes.byref(n),
+        _stream(compute_stream), _stream(copy_stream)))
+    return sched[:n.value].copy()

@@ -96,7 +96,6 @@
 #include <type_traits>
 
 #include "ffn_device.hpp"
-#include "ffn_stream.hpp"
 #include "smoe_blocks.hpp"  // route_check (the layer call validates every step)
 
 namespace smoe {
@@ -107,13 +106,16 @@ constexpr int kThreads = kWavesPerWg * kWave;
 constexpr int kMaxChunk = 32;              // slots per chunk (two MFMA column groups)
 constexpr int kCpOff = (kMaxE + 1 + 3) / 4 * 4;  // chunk prefix table, 16-byte aligned
 constexpr int kTkOff = kCpOff + kMaxE + 1;     // work-ticket slots (2 words)
-constexpr int kTabInts = kTkOff + 2;
+constexpr int kMatOff = kTkOff + 4;          // expert -> weight matrix table
+constexpr int kTabInts = kMatOff + kMaxE;
 constexpr int kPools = 8;                  // work-ticket counters per stage
 constexpr int kUnit = 2;                   // consecutive items per ticket
 #ifndef SMOE_FFN_STATIC_PERMILLE
 #define SMOE_FFN_STATIC_PERMILLE 900
 #endif
 constexpr int kStaticPermille = SMOE_FFN_STATIC_PERMILLE;  // share of the even split taken up front
+constexpr int kHdrStamp = 2;               // header words 2..5: the workspace stamp
+constexpr int kHdrSpoiled = 6;             // header word 6: stamp mismatch seen
 constexpr int kHdrCtr1 = 8;                // header words of the stage-1 counters
 constexpr int kHdrCtr2 = kHdrCtr1 + kPools;
 constexpr int kTabBytes = (kTabInts * 4 + 15) / 16 * 16;  // offsets, chunk prefix
@@ -182,12 +184,22 @@ struct FfnArgs {
   int rows_lds;                 // staged rows the LDS holds (largest chunk)
   int xres;                     // stage 1: all T rows of x held in LDS for the whole launch
   Group grp[2];
+  int has_mat;                  // mat holds the routed experts' weight matrices
+  int32_t mat[kMaxE];           // matrix of expert e (-1: not in this call); else matrix e
 };
+
+// The launch's argument read in place from the kernel-argument segment (its
+// only argument, at offset 0): indexing mat[] of the by-value argument with a
+// run-time index would make the compiler copy the whole argument to scratch.
+typedef const __attribute__((address_space(4))) FfnArgs ConstFfnArgs;
+__device__ __forceinline__ ConstFfnArgs* ffn_kargs() {
+  return (ConstFfnArgs*)(__builtin_amdgcn_kernarg_segment_ptr());
+}
 
 // One item: part `part` of row tile `tile` of chunk `chunk` of group `grp`
 // (expert e, positions [seg0, seg0 + m) of the group's slots).
 struct Item {
-  int grp, chunk, tile, part, e, seg0, m;
+  int grp, chunk, tile, part, e, me, seg0, m;  // me: weight matrix of expert e
 };
 
 
@@ -201,6 +213,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
   int* s_off = reinterpret_cast<int*>(smem);
   int* s_cp = s_off + kCpOff;
   int* s_tk = s_off + kTkOff;
+  int* s_mat = s_off + kMatOff;
   int* s_slots = reinterpret_cast<int*>(smem + kTabBytes);  // all slots, or the chunk's
   uint8_t* xs = smem + a.xs_off;
 
@@ -216,6 +229,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
   // (when they fit LDS) and the call counter
   static_assert(kThreads > kMaxE, "one offset per thread");
   const int offv = tid <= E ? a.offsets[tid] : 0;
+  const int matv = a.has_mat && tid < E ? ffn_kargs()->mat[tid] : tid;
   constexpr int kSlotsPer = kMaxSlotsLds / kThreads;
   int slv[kSlotsPer];
   if (a.slots_lds) {
@@ -228,6 +242,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
   const int ep = a.hdr[STAGE == 1 ? 0 : 1];
   float* gu = a.gu + ((STAGE == 1 ? ep : ep - 1) & 1) * a.gu_buf;  // this call's g/u
   if (tid <= E) s_off[tid] = min(max(offv, 0), a.S);  // clamped to [0, S]
+  if (tid < E) s_mat[tid] = matv;
   // (stage 1 with x resident keeps the token of each sorted slot instead)
   constexpr bool xres = XRES != 0;
   if (a.slots_lds) {
@@ -237,14 +252,48 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
         s_slots[tid + j * kThreads] =
             !xres ? slv[j] : (slv[j] >= 0 && slv[j] < a.S ? slv[j] / a.k : 0);
   }
+  // Workspace stamp: the (T, k, I, shared I) the buffer serves, all zero on
+  // a zeroed buffer. Stage 1 of the first call writes it; a call of another
+  // shape marks the workspace spoiled (its g/u layout differs, so the
+  // buffers no longer start at zero), and from then on stage 2 writes NaN
+  // outputs instead of wrong sums, until the caller zeroes the buffer again.
+  const int stamp_t = a.hdr[kHdrStamp], stamp_k = a.hdr[kHdrStamp + 1];
+  const int stamp_i = a.hdr[kHdrStamp + 2], stamp_s = a.hdr[kHdrStamp + 3];
+  const int spoiled = a.hdr[kHdrSpoiled];
   if (b == 0) {
-    if (tid == 0) a.hdr[STAGE == 1 ? 1 : 0] = STAGE == 1 ? ep + 1 : ep;
+    if (tid == 0) {
+      a.hdr[STAGE == 1 ? 1 : 0] = STAGE == 1 ? ep + 1 : ep;
+      if (STAGE == 1) {
+        const int my_i = a.grp[0].N, my_s = a.n_groups > 1 ? a.grp[1].N : 0;
+        if ((stamp_t | stamp_k | stamp_i | stamp_s) == 0) {
+          a.hdr[kHdrStamp] = a.T;
+          a.hdr[kHdrStamp + 1] = a.k;
+          a.hdr[kHdrStamp + 2] = my_i;
+          a.hdr[kHdrStamp + 3] = my_s;
+        } else if (stamp_t != a.T || stamp_k != a.k || stamp_i != my_i || stamp_s != my_s) {
+          a.hdr[kHdrSpoiled] = 1;
+        }
+      }
+    }
     // the other stage's ticket counters start its next launch at zero
     if (tid < kPools)
       __hip_atomic_store(a.hdr + (STAGE == 1 ? kHdrCtr2 : kHdrCtr1) + tid, 0, __ATOMIC_RELAXED,
                          __HIP_MEMORY_SCOPE_AGENT);
   }
   __syncthreads();
+  if (STAGE == 2 && spoiled) {
+    // every output row NaN (this workgroup's share)
+    const float qnan = __builtin_nanf("");
+    const long long n_slot = static_cast<long long>(a.S) * a.H / 4;
+    const long long tot = n_slot + (a.n_groups > 1 ? static_cast<long long>(a.T) * a.H / 4 : 0);
+    for (long long i = static_cast<long long>(b) * kThreads + tid; i < tot;
+         i += static_cast<long long>(gridDim.x) * kThreads) {
+      f32x4* dst = i < n_slot ? reinterpret_cast<f32x4*>(a.grp[0].out) + i
+                              : reinterpret_cast<f32x4*>(a.grp[1].out) + (i - n_slot);
+      *dst = f32x4{qnan, qnan, qnan, qnan};
+    }
+    return;
+  }
 
   // ---- work list: chunk prefix over the routed experts
   const int csz0 = a.grp[0].csz;
@@ -253,7 +302,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int e = 4 * lane + i;
-      n[i] = e < E ? (max(s_off[e + 1] - s_off[e], 0) + csz0 - 1) / csz0 : 0;
+      // (experts left out of the call have no chunks)
+      n[i] = e < E && s_mat[e] >= 0 ? (max(s_off[e + 1] - s_off[e], 0) + csz0 - 1) / csz0 : 0;
       tot += n[i];
     }
     const int incl = wave_inclusive_scan(tot);
@@ -338,7 +388,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
     if (STAGE != 1) return;
     float* other = a.gu + ((ep + 1) & 1) * a.gu_buf;
     const long long n0 = a.gu_buf / 4;
-    const long long n1 = n0 + static_cast<long long>(a.S) * a.H / 4;
+    // every row of slot_out, or with a matrix table only the rows of the
+    // call's experts (below): the others keep what earlier calls wrote
+    const long long n1 = n0 + (a.has_mat ? 0 : static_cast<long long>(a.S) * a.H / 4);
     const long long tot = n1 + (a.n_groups > 1 ? static_cast<long long>(a.T) * a.H / 4 : 0);
     const long long per = (tot + gridDim.x - 1) / gridDim.x;
     const long long lo = per * b, hi = min(tot, lo + per);
@@ -347,6 +399,20 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
                    : i < n1 ? reinterpret_cast<f32x4*>(a.grp[0].out) + (i - n0)
                             : reinterpret_cast<f32x4*>(a.grp[1].out) + (i - n1);
       *dst = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    }
+    if (a.has_mat) {
+      const int kept = s_off[E];
+      for (int p = b; p < kept; p += gridDim.x) {
+        int lo_e = 0, hi_e = E;  // the expert of position p: s_off[lo_e] <= p < s_off[hi_e]
+        while (hi_e - lo_e > 1) {
+          const int mid = (lo_e + hi_e) >> 1;
+          if (s_off[mid] <= p) lo_e = mid; else hi_e = mid;
+        }
+        const int row = a.sorted_slots[p];
+        if (s_mat[lo_e] < 0 || row < 0 || row >= a.S) continue;
+        f32x4* dst = reinterpret_cast<f32x4*>(a.grp[0].out) + static_cast<long long>(row) * (a.H / 4);
+        for (int c = tid; c < a.H / 4; c += kThreads) dst[c] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+      }
     }
   };
   if (cur < 0) {  // whole workgroup
@@ -371,6 +437,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
 #pragma unroll
       for (int i = 0; i < 4; ++i) n += __popcll(__ballot(4 * lane + i < E && cp[i] <= it.chunk));
       it.e = uniform(max(n - 1, 0));
+      it.me = uniform(s_mat[it.e]);
       it.seg0 = s_off[it.e] + (it.chunk - s_cp[it.e]) * csz0;
       it.m = min(csz0, s_off[it.e + 1] - it.seg0);
     } else {
@@ -381,6 +448,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
       it.chunk = ct / tiles;
       it.tile = ct - it.chunk * tiles;
       it.e = 0;
+      it.me = 0;
       it.seg0 = it.chunk * csz;
       it.m = min(csz, a.T - it.seg0);
     }
@@ -423,14 +491,14 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
         // reads the last slice instead (loaded, never stored)
         const int sl = min(row_of(it.tile, m) >> 4, gr.N / 16 - 1);
         const long long t0 = static_cast<long long>(sl) * gr.nblk;
-        wp[m] = wm + it.e * gr.w_estride + t0 * (16 * kBlockBytes) + 16 * lane;
-        if (WK == kInt4) sp[m] = l_fmt == kInt4 ? sm + it.e * gr.s_estride + (t0 * 16 + r16) * NQ
+        wp[m] = wm + it.me * gr.w_estride + t0 * (16 * kBlockBytes) + 16 * lane;
+        if (WK == kInt4) sp[m] = l_fmt == kInt4 ? sm + it.me * gr.s_estride + (t0 * 16 + r16) * NQ
                                                 : sm;
       } else {
         const int row = min(row_of(it.tile, m), gr.N - 1);  // rows past N: loaded, never stored
-        wp[m] = wm + it.e * gr.w_estride + static_cast<long long>(row) * gr.w_rstride + lane_kb;
+        wp[m] = wm + it.me * gr.w_estride + static_cast<long long>(row) * gr.w_rstride + lane_kb;
         if (WK == kInt4)  // (FP16 groups: null + 0)
-          sp[m] = sm + it.e * gr.s_estride + static_cast<long long>(row) * gr.s_rstride;
+          sp[m] = sm + it.me * gr.s_estride + static_cast<long long>(row) * gr.s_rstride;
       }
     }
   };
@@ -929,8 +997,7 @@ int tiles_of(long long N, int rows_per_wave) {
 }
 
 // Workspace layout: call counter (2 words, padded to 256 bytes) | two g/u
-// buffers, each [2][S][I] fp32 (routed) followed by [2][T][Is] fp32 (shared)
-// | the streaming FFN's fp16 h ([S][I] routed, then [T][Is] shared).
+// buffers, each [2][S][I] fp32 (routed) followed by [2][T][Is] fp32 (shared).
 constexpr size_t kEpochBytes = 256;
 long long gu_floats(long long T, long long k, long long I, long long Is) {
   return 2 * T * k * I + 2 * T * Is;
@@ -939,7 +1006,7 @@ size_t gu_region_bytes(long long T, long long k, long long I, long long Is) {
   return kEpochBytes + static_cast<size_t>(2 * gu_floats(T, k, I, Is)) * sizeof(float);
 }
 size_t workspace_bytes(long long T, long long k, long long I, long long Is) {
-  return gu_region_bytes(T, k, I, Is) + stream_h_bytes(T, k, I, Is);
+  return gu_region_bytes(T, k, I, Is);
 }
 
 // Weights of one group as the entry points hand them over.
@@ -1154,35 +1221,6 @@ smoe_status build_plans(const char* who, StagePlans& p, const void* x, int T, in
   return SMOE_OK;
 }
 
-#ifndef SMOE_STREAM_FFN
-#define SMOE_STREAM_FFN 0
-#endif
-
-// Tiled weights and a short window: the streaming FFN (ffn_stream.hip), whose
-// fp16 h lives in the last region of the workspace. kStreamNotApplicable
-// (nothing enqueued) otherwise.
-smoe_status try_stream(const char* who, const GroupWeights& r, const void* x, int T, int k,
-                       int H, const int32_t* sorted_slots, const int32_t* offsets, int shared_I,
-                       const void* swg, const void* swu, const void* swd, void* workspace,
-                       float* slot_out, float* shared_out, hipStream_t s) {
-  if (!SMOE_STREAM_FFN || !r.tiled) return kStreamNotApplicable;
-  StreamCall c{};
-  c.fmt = r.fmt;
-  c.G = r.G;
-  c.x = x;
-  c.T = T; c.k = k; c.E = r.E; c.H = H; c.I = r.I;
-  c.wg = r.wg; c.wu = r.wu; c.wd = r.wd;
-  c.sg = r.sg; c.su = r.su; c.sd = r.sd;
-  c.Is = shared_I;
-  c.swg = swg; c.swu = swu; c.swd = swd;
-  c.sorted_slots = sorted_slots;
-  c.offsets = offsets;
-  c.h = static_cast<uint8_t*>(workspace) + gu_region_bytes(T, k, r.I, shared_I);
-  c.slot_out = slot_out;
-  c.shared_out = shared_I > 0 ? shared_out : nullptr;
-  return stream_ffn(c, s, who);
-}
-
 // clear_ws: zero the workspace bytes this call uses before its launches
 // (the no-allocation entry point, whose workspace other calls share).
 smoe_status w4a16_ffn(int tiled,
@@ -1219,9 +1257,6 @@ smoe_status w4a16_ffn(int tiled,
                    shared_wg, shared_wu, shared_wd, slot_out, shared_out);
   if (st != SMOE_OK) return st;
   hipStream_t s = as_stream(stream);
-  st = try_stream(who, r, x, T, k, H, sorted_slots, expert_offsets, shared_I, shared_wg,
-                  shared_wu, shared_wd, workspace, slot_out, shared_out, s);
-  if (st != kStreamNotApplicable) return st;
   if (clear_ws) {
     const long long n16 = static_cast<long long>(gu_region_bytes(T, k, I, shared_I) / 16);
     const int grid = static_cast<int>(std::min<long long>((n16 + 255) / 256, 2048));
@@ -1240,12 +1275,15 @@ smoe_status w4a16_ffn(int tiled,
 #undef SMOE_FFN_NC
 }
 
+// mat / n_mat: the expert -> weight matrix table of smoe_fp16_expert_ffn_mapped
+// (null: expert e is matrix e).
 smoe_status fp16_ffn(int tiled,
     const void* x, int T, int k, int E, int H, int I, const void* wg, const void* wu,
     const void* wd, const int32_t* sorted_slots, const int32_t* expert_offsets, int shared_I,
     const void* shared_wg, const void* shared_wu, const void* shared_wd, void* workspace,
-    size_t workspace_bytes_, float* slot_out, float* shared_out, void* stream) {
-  const char* who = tiled ? "fp16_expert_ffn_tiled" : "fp16_expert_ffn";
+    size_t workspace_bytes_, float* slot_out, float* shared_out, void* stream,
+    const int32_t* mat = nullptr, int n_mat = 0, const char* who = nullptr) {
+  if (who == nullptr) who = tiled ? "fp16_expert_ffn_tiled" : "fp16_expert_ffn";
   smoe_status st = check_common(who, x, T, k, E, H, I, sorted_slots, expert_offsets, shared_I,
                                 shared_wg, shared_wu, shared_wd, workspace, workspace_bytes_,
                                 slot_out, shared_out);
@@ -1263,10 +1301,12 @@ smoe_status fp16_ffn(int tiled,
   st = build_plans(who, p, x, T, k, H, sorted_slots, expert_offsets, workspace, r, shared_I,
                    shared_wg, shared_wu, shared_wd, slot_out, shared_out);
   if (st != SMOE_OK) return st;
+  if (mat != nullptr) {  // (host table; an index outside the arrays leaves the expert out)
+    p.a1.has_mat = p.a2.has_mat = 1;
+    for (int e = 0; e < E; ++e)
+      p.a1.mat[e] = p.a2.mat[e] = mat[e] >= 0 && mat[e] < n_mat ? mat[e] : -1;
+  }
   hipStream_t s = as_stream(stream);
-  st = try_stream(who, r, x, T, k, H, sorted_slots, expert_offsets, shared_I, shared_wg,
-                  shared_wu, shared_wd, workspace, slot_out, shared_out, s);
-  if (st != kStreamNotApplicable) return st;
   return p.nc == 2 ? launch_ffn<kFp16, 128, 2>(p, s) : launch_ffn<kFp16, 128, 1>(p, s);
 }
 
@@ -1416,6 +1456,41 @@ extern "C" smoe_status smoe_fp16_expert_ffn_tiled(
   clear_error();
   return fp16_ffn(1, x, T, k, E, H, I, wg, wu, wd, sorted_slots, expert_offsets, shared_I, shared_wg,
                   shared_wu, shared_wd, workspace, workspace_bytes_, slot_out, shared_out, stream);
+}
+
+extern "C" smoe_status smoe_fp16_expert_ffn_mapped(
+    const void* x, int T, int k, int E, int H, int I, const void* wg, const void* wu,
+    const void* wd, int tiled, int n_matrices, const int32_t* expert_matrix,
+    const int32_t* sorted_slots, const int32_t* expert_offsets, int shared_I,
+    const void* shared_wg, const void* shared_wu, const void* shared_wd, void* workspace,
+    size_t workspace_bytes_, float* slot_out, float* shared_out, void* stream) {
+  clear_error();
+  const char* who = "fp16_expert_ffn_mapped";
+  SMOE_REQUIRE(tiled == 0 || tiled == 1, SMOE_EINVAL, "%s: tiled must be 0 or 1 (got %d)", who,
+               tiled);
+  SMOE_REQUIRE(n_matrices > 0, SMOE_EINVAL, "%s: need n_matrices > 0 (got %d)", who,
+               n_matrices);
+  SMOE_REQUIRE(T == 0 || expert_matrix != nullptr, SMOE_EINVAL, "%s: null expert_matrix", who);
+  return fp16_ffn(tiled, x, T, k, E, H, I, wg, wu, wd, sorted_slots, expert_offsets, shared_I,
+                  shared_wg, shared_wu, shared_wd, workspace, workspace_bytes_, slot_out,
+                  shared_out, stream, expert_matrix, n_matrices, who);
+}
+
+extern "C" smoe_status smoe_ffn_workspace_clear(void* workspace, size_t workspace_bytes_,
+                                                void* stream) {
+  clear_error();
+  SMOE_REQUIRE(workspace != nullptr && (reinterpret_cast<uintptr_t>(workspace) & 255u) == 0,
+               SMOE_EINVAL, "ffn_workspace_clear: the workspace must be non-null and 256-byte "
+               "aligned");
+  SMOE_REQUIRE(workspace_bytes_ % 16 == 0, SMOE_EINVAL,
+               "ffn_workspace_clear: workspace_bytes must be a multiple of 16 (got %zu)",
+               workspace_bytes_);
+  if (workspace_bytes_ == 0) return SMOE_OK;
+  const long long n16 = static_cast<long long>(workspace_bytes_ / 16);
+  const int grid = static_cast<int>(std::min<long long>((n16 + 255) / 256, 2048));
+  hipLaunchKernelGGL(zero_kernel, dim3(grid), dim3(256), 0, as_stream(stream),
+                     static_cast<f32x4*>(workspace), n16);
+  return check_launch("ffn_workspace_clear");
 }
 
 extern "C" smoe_status smoe_moe_layer_w4a16(

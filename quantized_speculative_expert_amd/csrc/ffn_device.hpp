@@ -1,5 +1,5 @@
-// Device helpers of the expert FFN kernels (ffn.hip, ffn_stream.hip):
-// vector types, bit casts and the table-free INT4 dequantisation.
+// Device helpers of the expert FFN kernel (ffn.hip): vector types, global
+// loads and stores, bit casts and the table-free INT4 dequantisation.
 #pragma once
 
 #include "smoe_internal.hpp"

@@ -90,9 +90,13 @@ class DeviceLayer:
         self.sorted_slots = torch.empty(S, **i32)
         self.active = torch.empty(E, **i32)
         self.n_active = torch.empty(1, **i32)
-        # zero-filled once; the FFN calls keep it consistent from then on
+        # zero-filled once; the FFN calls keep it consistent from then on. A
+        # workspace serves one (T, k, I, shared_I): the routed calls with the
+        # shared experts fused use this one, those without them their own
         ws = _lib.smoe_ffn_workspace_bytes(T, k, E, H, I, Is)
         self.workspace = torch.zeros(ws, dtype=torch.uint8, device=d)
+        self.routed_ws = (torch.zeros(_lib.smoe_ffn_workspace_bytes(T, k, E, H, I, 0),
+                                      dtype=torch.uint8, device=d) if Is else self.workspace)
         self.slot_out = torch.empty((S, H), **f32)
         self.y = torch.empty((T, H), dtype=torch.float16, device=d)
         self.shared_gate = torch.empty(T, **f32) if self.shared_gate_w is not None else None
@@ -186,15 +190,16 @@ class DeviceLayer:
         if with_shared and self.shared_out is not None:
             shared = (self.sg16, self.su16, self.sd16)
             shared_out = self.shared_out
+        ws = self.workspace if shared is not None else self.routed_ws
         if target:
             self._call("smoe_fp16_expert_ffn")(self.x, c.k, c.E, c.I, self.wg16, self.wu16, self.wd16,
-                                      self.sorted_slots, self.offsets, self.workspace,
+                                      self.sorted_slots, self.offsets, ws,
                                       self.slot_out, shared=shared, shared_out=shared_out,
                                       stream=stream)
         else:
             self._call("smoe_w4a16_expert_ffn")(self.x, c.k, c.E, c.I, c.G, self.wg_q, self.wg_s,
                                        self.wu_q, self.wu_s, self.wd_q, self.wd_s,
-                                       self.sorted_slots, self.offsets, self.workspace,
+                                       self.sorted_slots, self.offsets, ws,
                                        self.slot_out, shared=shared, shared_out=shared_out,
                                        stream=stream)
 

@@ -698,6 +698,96 @@ def test_fp16_ffn_shapes(smoe, E, k, T, H, I, tiled):
     assert row_rel_err(got, ref) <= ROW_TOL
 
 
+def _pool(smoe, wg, wu, wd, slot_of, M, tiled):
+    """Device pool [M][3][I*H] fp16 holding expert e's (wg, wu, wd) at slot
+    slot_of[e] (-1: not resident), and the three base views into it."""
+    E, I, H = wg.shape
+    msz = I * H
+    pool = torch.zeros(M * 3 * msz, dtype=torch.float16, device="cuda")
+    for e in range(E):
+        s = int(slot_of[e])
+        if s < 0:
+            continue
+        for j, w in enumerate((wg[e], wu[e], wd[e])):
+            n, kk = w.shape
+            t = dev(np.ascontiguousarray(w))
+            if tiled:
+                t = tile_dev(smoe, t, None, 1, n, kk, 0)[0]
+            pool[(3 * s + j) * msz:(3 * s + j + 1) * msz] = t.reshape(-1)
+    return pool, pool[0:], pool[msz:], pool[2 * msz:]
+
+
+@pytest.mark.parametrize("tiled", [False, True], ids=["rows", "tiled"])
+def test_fp16_ffn_mapped_disjoint_calls(smoe, tiled):
+    # experts placed at scattered slots of a pool; a first call over some of
+    # them (the resident ones), a second over the rest: together they fill
+    # slot_out exactly like one unmapped call, and rows outside a call keep
+    # what they held
+    E, k, T, H, I, M = 8, 2, 17, 256, 384, 11
+    rng = np.random.default_rng(7)
+    x = rng.standard_normal((T, H)).astype(np.float16)
+    wg = (rng.standard_normal((E, I, H)) * 0.02).astype(np.float16)
+    wu = (rng.standard_normal((E, I, H)) * 0.02).astype(np.float16)
+    wd = (rng.standard_normal((E, H, I)) * 0.02).astype(np.float16)
+    ids = np.stack([rng.permutation(E)[:k] for _ in range(T)]).astype(np.int32)
+    ids[3, 1] = -1  # a dropped slot: written by neither call
+    slot_of = rng.permutation(M)[:E].astype(np.int32)
+    pool, pg, pu, pd = _pool(smoe, wg, wu, wd, slot_of, M, tiled)
+    al = oracle.align_by_expert(ids, E)
+    ref = oracle.routed_ffn_expertwise(x, ids, lambda e: (wg[e], wu[e], wd[e]))
+    first = np.zeros(E, bool)
+    first[[0, 2, 3, 6]] = True
+    tables = [np.where(first, 3 * slot_of, -1), np.where(~first, 3 * slot_of, -1)]
+    ws = torch.zeros(smoe.smoe_ffn_workspace_bytes(T, k, E, H, I, 0), dtype=torch.uint8,
+                     device="cuda")
+    out = torch.full((T * k, H), 7.0, dtype=torch.float32, device="cuda")
+    xs, ss, offs = dev(x), dev(al["sorted_slots"]), dev(al["offsets"])
+    slot_expert = ids.reshape(-1)
+    for c, tab in enumerate(tables):
+        smoe.smoe_fp16_expert_ffn_mapped(xs, k, E, I, pg, pu, pd, 3 * M - 2, tab, ss, offs, ws,
+                                         out, tiled=tiled)
+        got = host(out)
+        done = np.isin(slot_expert, np.nonzero(first if c == 0 else np.ones(E, bool))[0])
+        assert row_rel_err(got[done], ref[done]) <= ROW_TOL
+        assert (got[~done] == 7.0).all()
+    assert (host(out)[3 * k + 1] == 7.0).all()
+
+
+def test_ffn_workspace_stamp_detects_a_shape_change(smoe):
+    # a workspace zeroed for one window and then used for another without
+    # zeroing again gives NaN outputs (not wrong sums) until it is cleared
+    E, k, H, I = 8, 2, 256, 256
+    rng = np.random.default_rng(3)
+    wg = (rng.standard_normal((E, I, H)) * 0.02).astype(np.float16)
+    wu = (rng.standard_normal((E, I, H)) * 0.02).astype(np.float16)
+    wd = (rng.standard_normal((E, H, I)) * 0.02).astype(np.float16)
+    W = [dev(w) for w in (wg, wu, wd)]
+    ws = torch.zeros(smoe.smoe_ffn_workspace_bytes(17, k, E, H, I, 0), dtype=torch.uint8,
+                     device="cuda")
+
+    def call(T):
+        x = rng.standard_normal((T, H)).astype(np.float16)
+        ids = np.stack([rng.permutation(E)[:k] for _ in range(T)]).astype(np.int32)
+        al = oracle.align_by_expert(ids, E)
+        out = torch.zeros((T * k, H), dtype=torch.float32, device="cuda")
+        smoe.smoe_fp16_expert_ffn(dev(x), k, E, I, *W, dev(al["sorted_slots"]),
+                                  dev(al["offsets"]), ws, out)
+        ref = oracle.routed_ffn_expertwise(x, ids, lambda e: (wg[e], wu[e], wd[e]))
+        return host(out), ref
+
+    for _ in range(2):  # the same shape twice: fine
+        got, ref = call(17)
+        assert row_rel_err(got, ref) <= ROW_TOL
+    got, _ = call(9)  # another T on the same workspace: spoiled
+    assert np.isnan(got).all()
+    got, _ = call(17)  # stays spoiled, also for the first shape
+    assert np.isnan(got).all()
+    smoe.smoe_ffn_workspace_clear(ws)
+    for T in (9, 9):  # zeroed: serves the new shape
+        got, ref = call(T)
+        assert row_rel_err(got, ref) <= ROW_TOL
+
+
 @pytest.mark.parametrize("tiled", [False, True], ids=["rows", "tiled"])
 def test_phi_draft_and_target(smoe, tiled):
     # both expert FFN calls of the Phi-shaped window against the oracle, on
@@ -795,6 +885,22 @@ def test_layer_draft_matches_oracle(smoe, name, mode):
         pid, pc = oracle.elb_topm(ref_cnt, L.cfg.elb_M)
         assert np.array_equal(host(d.elb_counts), ref_cnt)
         assert np.array_equal(host(d.plan_ids), pid) and np.array_equal(host(d.plan_counts), pc)
+
+
+def test_layer_fused_separate_fused_on_one_layer(smoe):
+    # the shared experts fused into the routed FFN, then in a call of their
+    # own, then fused again, on one DeviceLayer: every run matches the oracle
+    # (each mode keeps a workspace of its own shape)
+    from quantized_speculative_expert_amd.layer import DeviceLayer
+    L = layer("dsv2")
+    ref = ref_layer("dsv2", "draft")
+    d = DeviceLayer(L, with_target=False)
+    for fuse in (True, False, True, False):
+        d.y.fill_(float("nan"))
+        d.run(fuse_shared=fuse)
+        y = host(d.y)
+        assert np.isfinite(y).all()
+        assert row_rel_err(y, ref["y64"]) <= ROW_TOL
 
 
 @pytest.mark.parametrize("tiled", [False, True], ids=["rows", "tiled"])
