@@ -187,3 +187,52 @@ def test_prefetch_then_verify_all_hits(smoe):
         _, _, _, sched = s.verify(smoe, l, ids)
         assert (sched[:, 2] == O.HIT).all()
     s.close(smoe)
+
+
+# ------------------------------------------------------------------ whole window
+
+def test_speculative_window_with_prefetch_and_cached_verification(smoe):
+    # 3 layers, 16 experts, top-2, a K=8 window, 6 slots per layer: the
+    # draft's routing drives the prefetch exactly as the model's planner
+    # decides; verification decisions equal the model's; y of every layer
+    # equals the oracle's composition on the device's routing
+    import dataclasses
+    from quantized_speculative_expert_amd.offload import OffloadStack
+    from workload import make_layer, make_router
+    from workload.configs import MoEConfig
+    from workload.gen import zipf_bias
+    cfg = MoEConfig(name="offload-test", E=16, k=2, H=256, I=256, G=128, T=9, shared_I=256,
+                    elb_M=6)
+    L, M, K = 3, 6, cfg.T - 1
+    draft_inp = make_layer(dataclasses.replace(cfg, T=1), seed=4, layer=0)
+    zipf = [zipf_bias(cfg.E, 1.0, 4, l).astype(np.float32) for l in range(L)]
+    routers = [make_router(cfg, 4, l) for l in range(L)]
+    st = OffloadStack(cfg, draft_inp, L, M, zipf=zipf, routers=routers, seed=4, tiled=False)
+    model = O.CacheModel(L, M)
+    rng = np.random.default_rng(4)
+    bw, us = 20.0, 150.0
+    for w in range(3):
+        xd = (rng.standard_normal((L, K, cfg.H)) * 1.0).astype(np.float16)
+        xt = np.concatenate([xd + (0.05 * rng.standard_normal(xd.shape)).astype(np.float16),
+                             rng.standard_normal((L, 1, cfg.H)).astype(np.float16)], axis=1)
+        rec = torch.empty((K, L, cfg.k), dtype=torch.int32, device="cuda")
+        out = st.draft_window(torch.from_numpy(xd).cuda(), True, 2, bw, us, record=rec)
+        routing = host(rec)
+        want = O.plan_window(routing, cfg.E, model, 2, st.expert_bytes, bw, us)
+        assert out["chunks"] == want["chunks"]
+        assert [(b, [tuple(x) for x in ld.tolist()]) for b, ld in out["loads"]] == \
+            want["boundaries"]
+        xt_dev = torch.from_numpy(np.ascontiguousarray(xt)).cuda()
+        for l in range(L):
+            sched = st.verify_layer(l, xt_dev[l])
+            counts = host(st.t_counts)
+            assert [tuple(r) for r in sched.tolist()] == model.verify(l, [int(c) for c in counts])
+            ids, wts = host(st.t_ids), host(st.t_w)
+            hw = st.host[l].numpy()
+            load = lambda e: (hw[e, 0].reshape(cfg.I, cfg.H), hw[e, 1].reshape(cfg.I, cfg.H),
+                              hw[e, 2].reshape(cfg.H, cfg.I))
+            slot_ref = oracle.routed_ffn_expertwise(xt[l], ids, load)
+            sh = tuple(draft_inp.__getattribute__(n) for n in ("sg16", "su16", "sd16"))
+            y_ref = oracle.combine(slot_ref, wts, oracle.shared_ffn(xt[l], *sh))[0]
+            assert row_rel_err(host(st.y[l]), y_ref) <= ROW_TOL
+    st.close()
