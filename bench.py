@@ -76,6 +76,19 @@ def parse_args():
     p.add_argument("--compare", action="store_true",
                    help="also time the same routed-expert work as one W4A16 call per active "
                         "expert and as one batched call over FP16 weights")
+    p.add_argument("--offload", action="store_true",
+                   help="instead of the layer throughput: speculative windows over a stack "
+                        "whose FP16 target experts live in pinned host memory (draft with "
+                        "ELB-driven prefetch, cached verification), with and without the "
+                        "prefetch and with every expert resident")
+    p.add_argument("--offload-layers", type=int, default=4,
+                   help="layers of the offloaded stack (--offload)")
+    p.add_argument("--offload-windows", type=int, default=6,
+                   help="timed windows per mode (--offload), after two untimed ones")
+    p.add_argument("--specfit", action="store_true",
+                   help="instead of the layer throughput: SpecFit subtree selection on the host "
+                        "(18-node top-2 pools of depth 5, K = 7, 48 layers x 128 experts, "
+                        "top-8), the library's search against the brute-force oracle")
     p.add_argument("--cpu-reps", type=int, default=10,
                    help="full layers the CPU reference runs for cpu_baseline (0 = skip)")
     return p.parse_args()
@@ -300,6 +313,195 @@ def compare_ffn(base, layers, fused: bool, stream, batched_us: float) -> dict:
                      "FP16 = the batched call over FP16 routed weights (4x the bytes)")}
 
 
+def specfit_bench(args) -> int:
+    """Selection time per verification cycle: the library's depth-first search
+    against the oracle's brute force on the same seeded pools (Qwen3-30B-A3B
+    shape of the SpecFit page: 48 MoE layers, 128 experts, top-8; pools of 18
+    nodes from top-2 expansion to depth 5; K = 7), with a half-resident
+    expert cache. Both run on this host, one thread."""
+    import numpy as np
+
+    from quantized_speculative_expert_amd import _lib
+    import oracle.specfit as SF
+
+    L, E, k, n, K = 48, 128, 8, 18, 7
+    reps = max(1, min(args.steps, 50))
+    rng = np.random.default_rng(0)
+    pools = []
+    for _ in range(reps):
+        parent, depth, prob, kids = [], [], [], {}
+        frontier = [(-1, 0, 1.0)]
+        while len(parent) < n and frontier:
+            i = int(rng.integers(0, len(frontier)))
+            v, dv, pv = frontier[i]
+            if kids.get(v, 0) >= 2 or dv >= 5:
+                frontier.pop(i)
+                continue
+            kids[v] = kids.get(v, 0) + 1
+            q = float(pv * rng.uniform(0.2, 0.95))
+            parent.append(v)
+            depth.append(dv + 1)
+            prob.append(q)
+            frontier.append((len(parent) - 1, dv + 1, q))
+        sets_ = [[set(rng.choice(E, k, replace=False).tolist()) for _ in range(L)]
+                 for _ in range(n + 1)]
+        res = [set(rng.choice(E, E // 2, replace=False).tolist()) for _ in range(L)]
+        bits = np.zeros((n + 1, L, 2), np.uint64)
+        for r, node in enumerate(sets_):
+            for l, es in enumerate(node):
+                for e in es:
+                    bits[r, l, e // 64] |= np.uint64(1) << np.uint64(e % 64)
+        rbits = np.zeros((L, 2), np.uint64)
+        for l, es in enumerate(res):
+            for e in es:
+                rbits[l, e // 64] |= np.uint64(1) << np.uint64(e % 64)
+        b = np.cumsum(rng.uniform(5.0, 10.0, K + 1))
+        pools.append((np.array(parent, np.int32), np.array(prob), bits, rbits, b, sets_, res))
+    beta = 0.05
+    t_nat, agree, visited = [], 0, 0
+    for parent, prob, bits, rbits, b, _, _ in pools:
+        t0 = time.perf_counter()
+        sel, r, ev = _lib.smoe_specfit_select(parent, prob, bits, K, b, beta, rbits, E=E)
+        t_nat.append(time.perf_counter() - t0)
+        visited = ev
+    n_or = min(3, reps)
+    t_or = []
+    for parent, prob, bits, rbits, b, sets_, res in pools[:n_or]:
+        t0 = time.perf_counter()
+        want, wr, legal = SF.select(parent.tolist(), prob.tolist(), sets_[0], sets_[1:], K,
+                                    b.tolist(), beta, res)
+        t_or.append(time.perf_counter() - t0)
+        sel, r, ev = _lib.smoe_specfit_select(parent, prob, bits, K, b, beta, rbits, E=E)
+        agree += int(sel == want and r == wr and ev == legal)
+    med = float(np.median(t_nat)) * 1e6
+    out = {"metric": "SpecFit subtree selection: us per verification cycle (host)",
+           "value": round(med, 2), "unit": "us", "higher_is_better": False, "n_gpus": 0,
+           "data": "synthetic",
+           "config": {"workload": f"{reps} pools of {n} nodes (top-2 expansion, depth <= 5), "
+                                  f"K = {K}, {L} layers x {E} experts, top-{k}, half the "
+                                  f"experts resident, beta {beta}; seed 0",
+                      "legal_subtrees_per_pool": visited},
+           "cpu_baseline": {"value": round(float(np.median(t_or)) * 1e6, 1), "unit": "us",
+                            "cores": 1, "kind": "oracle",
+                            "sample": f"brute force over every subset of <= {K} nodes on the "
+                                      f"first {n_or} pools"},
+           "oracle_agrees": f"{agree}/{n_or}",
+           "pages_reference_ms": 2.82}
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+OFFLOAD_ZIPF_S = 0.7  # router skew giving ~32 distinct experts per 16 draft tokens (of 64)
+
+
+def offload_bench(args) -> int:
+    """Speculative windows (K = 16 draft tokens, a 17-token verification) over
+    a stack of dsv2-shaped layers whose FP16 target experts (17.3 MB each)
+    live in pinned host memory, with M = 32 device slots per layer. Three
+    modes on the same seeded windows: the ELB-driven prefetch planner on,
+    off (verification loads every miss itself), and every expert resident
+    (M = E, no copies). Per window: draft time, verification time, copies,
+    hits and misses. The verification's bound is the larger of its copy
+    time at the measured host-to-device bandwidth and its compute time."""
+    import dataclasses
+
+    import numpy as np
+    import torch
+
+    from quantized_speculative_expert_amd.offload import OffloadStack, measure_h2d
+    from workload import get_config, make_layer, make_router
+    from workload.gen import zipf_bias
+
+    cfg = get_config("dsv2")
+    L, M, K, b1 = args.offload_layers, cfg.elb_M, cfg.T - 1, 2
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    log(f"offload: {L} dsv2 layers, {M} slots per layer, K={K}")
+    draft_inp = make_layer(dataclasses.replace(cfg, T=1), seed=0, layer=0)
+    routers = [make_router(cfg, 0, l) for l in range(L)]
+    zipf = [zipf_bias(cfg.E, OFFLOAD_ZIPF_S, 0, l) for l in range(L)]
+    rng = np.random.default_rng(0)
+    n_win = args.offload_windows + 2
+    xd = [(rng.standard_normal((L, K, cfg.H))).astype(np.float16) for _ in range(n_win)]
+    xt = [np.concatenate([x + (0.05 * rng.standard_normal(x.shape)).astype(np.float16),
+                          rng.standard_normal((L, 1, cfg.H)).astype(np.float16)], axis=1)
+          for x in xd]
+    gbps = measure_h2d(dev)
+    log(f"host-to-device copy: {gbps:.1f} GB/s")
+
+    def run(mode: str):
+        st = OffloadStack(cfg, draft_inp, L, cfg.E if mode == "resident" else M, zipf=zipf,
+                          routers=routers, seed=0, tiled=True, device=dev)
+        if mode == "resident":  # every expert in its slot before the first window
+            slots = np.tile(np.arange(cfg.E, dtype=np.int32), (L, 1))
+            import quantized_speculative_expert_amd._lib as lib
+            lib.smoe_cache_set_state(st.cache, slots, np.zeros((L, cfg.E), np.int64), 0,
+                                     copy_stream=st.copy_stream)
+            torch.cuda.synchronize(dev)
+        # draft time per token (all layers), from the second of two untimed
+        # windows without prefetch (the first pays for first launches)
+        xdev = torch.from_numpy(xd[0]).to(dev)
+        for _ in range(2):
+            torch.cuda.synchronize(dev)
+            t0 = time.perf_counter()
+            st.draft_window(xdev, False, b1, gbps, 1.0)
+            torch.cuda.synchronize(dev)
+        us_tok = 1e6 * (time.perf_counter() - t0) / K
+        compute = torch.cuda.current_stream(dev)
+        rows = []
+        for w in range(n_win):
+            xdev = torch.from_numpy(xd[w]).to(dev)
+            xtdev = torch.from_numpy(np.ascontiguousarray(xt[w])).to(dev)
+            torch.cuda.synchronize(dev)
+            t0 = time.perf_counter()
+            plan = st.draft_window(xdev, mode == "planner", b1, gbps, us_tok)
+            # the draft is done when its stream is; prefetch copies may still
+            # be in flight and the verification starts at once
+            compute.synchronize()
+            t1 = time.perf_counter()
+            scheds = st.verify_window(xtdev)
+            torch.cuda.synchronize(dev)
+            t2 = time.perf_counter()
+            hits = sum(int((s[:, 2] == 0).sum()) for s in scheds)
+            misses = sum(int((s[:, 2] == 1).sum()) for s in scheds)
+            loads = sum(len(ld) for _, ld in plan["loads"])
+            rows.append({"draft_ms": 1e3 * (t1 - t0), "verify_ms": 1e3 * (t2 - t1),
+                         "prefetched": loads, "hits": hits, "misses": misses,
+                         "chunks": len(plan["chunks"])})
+        st.close()
+        del st
+        torch.cuda.empty_cache()
+        timed = rows[2:]
+        mean = {k: round(float(np.mean([r[k] for r in timed])), 3) for k in timed[0]}
+        mean["draft_us_per_token"] = round(us_tok, 1)
+        return mean
+
+    res = {m: run(m) for m in ("planner", "no-prefetch", "resident")}
+    eb = 3 * cfg.I * cfg.H * 2
+    for m, r in res.items():
+        copy_ms = r["misses"] * eb / (gbps * 1e6)
+        r["verify_copy_bound_ms"] = round(copy_ms, 3)
+        r["window_ms"] = round(r["draft_ms"] + r["verify_ms"], 3)
+    comp = res["resident"]["verify_ms"]
+    for m, r in res.items():
+        bound = max(r["verify_copy_bound_ms"], comp)
+        r["verify_bound_frac"] = round(bound / r["verify_ms"], 4) if r["verify_ms"] else None
+    out = {
+        "metric": "speculative window with offloaded FP16 target experts: window ms",
+        "unit": "ms", "higher_is_better": False, "n_gpus": 1, "data": "synthetic",
+        "config": {"workload": (f"{L} dsv2-shaped layers (64 experts, top-6, H 2048, I 1408, "
+                                f"FP16 target experts 17.3 MB each in pinned host memory), "
+                                f"{M} device slots per layer, K={K} draft tokens then a "
+                                f"{cfg.T}-token verification; draft INT4 layers resident; "
+                                f"router Zipf({OFFLOAD_ZIPF_S}) skew; b_1={b1}; seed 0"),
+                   "layers": L, "M": M, "K": K, "windows": args.offload_windows},
+        "h2d_gbps": round(gbps, 2),
+        "modes": res,
+    }
+    print(json.dumps(out), flush=True)
+    return 0
+
+
 def percentiles(xs):
     import numpy as np
     a = np.asarray(xs, dtype=float)
@@ -316,6 +518,9 @@ def main() -> int:
               file=sys.stderr)
         return 2
 
+    if args.specfit:
+        return specfit_bench(args)
+
     import torch
 
     if not torch.cuda.is_available():
@@ -323,6 +528,8 @@ def main() -> int:
         return 1
     if args.copy_calibration > 0:
         return copy_calibration(args.copy_calibration, args.steps)
+    if args.offload:
+        return offload_bench(args)
     from quantized_speculative_expert_amd.layer import DeviceLayer
     from workload import get_config, make_layer
 

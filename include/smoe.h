@@ -631,6 +631,43 @@ smoe_status smoe_cache_verify_layer(smoe_expert_cache* cache, int layer,
                                     float* shared_out, int32_t* schedule, int* n_schedule,
                                     void* compute_stream, void* copy_stream);
 
+/*
+ * SpecFit verification-subtree selection (host): the exact search over the
+ * draft pool's legal subtrees.   SpecFit page, sections 3.1 (legal subtree:
+ * ancestor-closed, at most K nodes; top-2 expansion, depth <= 5, <= 18
+ * nodes, K = min(7, pool size)), 3.2 (reward = 1 + sum of the selected
+ * nodes' path probabilities; cycle time = an intercept by node count + beta
+ * times the per-layer expert-union feature), 3.3 (the largest reward / time)
+ * and appendix A.3 (depth-first enumeration, parent before descendant, with
+ * incremental expert bitmaps).
+ *
+ *   n            pool nodes (0 .. 64); parent int32 [n]: -1 for a child of the
+ *                root, else an earlier node (parents precede their children)
+ *   path_prob    double [n], the drafter's path probability of each node
+ *   expert_bits  uint64 [n + 1][L][W], W = ceil(E / 64): row 0 the root's
+ *                experts (the committed token, always verified), row v + 1
+ *                node v's; bit e of layer l = expert e activated
+ *   resident_bits uint64 [L][W] (experts already in the device cache, which
+ *                cost nothing) or NULL (every expert costs)
+ *   K            size limit (the search uses min(K, n)); intercepts double
+ *                [min(K, n) + 1] > 0, intercept[s] for s selected nodes; beta >= 0
+ * Selection: the legal subtree S maximising
+ *   (1 + sum_{v in S, ascending v} path_prob[v]) / (intercept[|S|] + beta * F(S)),
+ * F(S) = sum over layers of popcount((root | nodes of S) & ~resident), each
+ * step one double operation; ties to fewer nodes, then the smaller
+ * ascending node list. The empty subtree (root only) is legal.
+ *   selected     int32 [min(K, n)] (out), ascending; n_selected (out);
+ *   ratio (out, may be NULL); n_evaluated (out, may be NULL): legal subtrees
+ *   visited.
+ * Drafting goes on after a level only while the selection holds a node of
+ * that level (the caller's check).
+ */
+smoe_status smoe_specfit_select(int n, const int32_t* parent, const double* path_prob, int L,
+                                int E, const uint64_t* expert_bits,
+                                const uint64_t* resident_bits, int K, const double* intercepts,
+                                double beta, int32_t* selected, int* n_selected, double* ratio,
+                                int64_t* n_evaluated);
+
 #ifdef __cplusplus
 }
 #endif

@@ -66,6 +66,8 @@ _SIGNATURES = {
     "smoe_prefetch_next_boundary": (_i, [_i, _i, _i, ctypes.c_double, ctypes.c_double,
                                          ctypes.c_double, _p]),
     "smoe_cache_verify_plan": (_i, [_p, _i, _p, _p, _p]),
+    "smoe_specfit_select": (_i, [_i, _p, _p, _i, _i, _p, _p, _i, _p, ctypes.c_double, _p, _p,
+                                 _p, _p]),
     "smoe_cache_verify_layer": (_i, [_p, _i, _p, _p, _i, _i, _i, _i, _i, _p, _p, _i, _p, _p, _p,
                                      _p, _sz, _p, _sz, _p, _p, _p, _p, _p, _p]),
 }
@@ -599,3 +601,28 @@ def smoe_cache_verify_layer(cache: int, layer: int, expert_counts, x, k: int, I:
         _np_ptr(sched, np.int32, "schedule"), ctypes.byref(n),
         _stream(compute_stream), _stream(copy_stream)))
     return sched[:n.value].copy()
+
+
+# ---------------------------------------------------------------- SpecFit
+
+def smoe_specfit_select(parent, path_prob, expert_bits, K: int, intercepts, beta: float,
+                        resident_bits=None, E: Optional[int] = None):
+    """parent int32 [n]; path_prob float64 [n]; expert_bits uint64 [n + 1][L][W]
+    (row 0 the root); resident_bits uint64 [L][W] or None; intercepts
+    float64 [min(K, n) + 1]. Returns (selected nodes, ratio, legal subtrees
+    visited)."""
+    import numpy as np
+    n = int(parent.shape[0])
+    L, W = int(expert_bits.shape[1]), int(expert_bits.shape[2])
+    E = 64 * W if E is None else E
+    sel = np.empty(max(min(K, n), 1), np.int32)
+    ns, ratio, ev = ctypes.c_int(), ctypes.c_double(), ctypes.c_int64()
+    _check("smoe_specfit_select", _lib.smoe_specfit_select(
+        n, _np_ptr(parent, np.int32, "parent") if n else None,
+        _np_ptr(path_prob, np.float64, "path_prob") if n else None, L, E,
+        _np_ptr(expert_bits, np.uint64, "expert_bits"),
+        None if resident_bits is None else _np_ptr(resident_bits, np.uint64, "resident_bits"),
+        K, _np_ptr(intercepts, np.float64, "intercepts"), float(beta),
+        _np_ptr(sel, np.int32, "selected"), ctypes.byref(ns), ctypes.byref(ratio),
+        ctypes.byref(ev)))
+    return sel[:ns.value].tolist(), ratio.value, ev.value
