@@ -229,7 +229,8 @@ def routed_ffn_tokenwise(x16: np.ndarray, ids: np.ndarray, load: ExpertLoader,
     """Per-slot expert outputs, token by token (the plain definition).
 
     slot_out[t*k + j] = FFN_{ids[t, j]}(x[t]); `load(e)` returns float64
-    (Wg, Wu, Wd) of expert e. Returns float64 [T*k][H].
+    (Wg, Wu, Wd) of expert e. A negative ID is a slot routed to no expert
+    (dropped by the alignment): its row is zero. Returns float64 [T*k][H].
     """
     x = np.asarray(x16)
     T, k = ids.shape
@@ -238,6 +239,8 @@ def routed_ffn_tokenwise(x16: np.ndarray, ids: np.ndarray, load: ExpertLoader,
     for t in range(T):
         for j in range(k):
             e = int(ids[t, j])
+            if e < 0:
+                continue
             if e not in cache:
                 cache[e] = load(e)
             out[t * k + j] = swiglu(x[t:t + 1].astype(F64), *cache[e],
@@ -252,13 +255,14 @@ def routed_ffn_expertwise(x16: np.ndarray, ids: np.ndarray, load: ExpertLoader,
     The Specter paper's verification reorder: gather the tokens routed to
     each expert into one sub-batch, run that expert once on the sub-batch,
     scatter each row back to its slot. Each row is the same definition as
-    in routed_ffn_tokenwise. Returns float64 [T*k][H].
+    in routed_ffn_tokenwise (negative IDs: zero rows). Returns float64
+    [T*k][H].
     """
     x = np.asarray(x16)
     T, k = ids.shape
     flat = np.asarray(ids, dtype=np.int64).ravel()
     out = np.zeros((T * k, x.shape[1]), dtype=F64)
-    for e in np.unique(flat):
+    for e in np.unique(flat[flat >= 0]):
         slots = np.flatnonzero(flat == e)
         tokens = slots // k
         wg, wu, wd = load(int(e))

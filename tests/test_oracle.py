@@ -350,6 +350,28 @@ def test_expertwise_equals_tokenwise():
     assert np.allclose(a, b, rtol=1e-12, atol=1e-15)
 
 
+def test_dropped_slots_give_zero_rows():
+    # a slot routed to no expert (ID -1, dropped by the alignment) receives
+    # nothing: its row is zero in both forms, and every other row is the one
+    # it would have without the drop (the loader is never asked for -1)
+    cfg, x, ids, mats = _tiny_int4_layer(3)
+    dropped = ids.copy()
+    dropped[[0, 5, 9], [1, 0, 1]] = -1
+    asked = []
+
+    def load(e):
+        asked.append(e)
+        return mats[e]
+
+    for fn in (oracle.routed_ffn_tokenwise, oracle.routed_ffn_expertwise):
+        asked.clear()
+        out = fn(x, dropped, load)
+        full = fn(x, ids, lambda e: mats[e])
+        gone = dropped.reshape(-1) < 0
+        assert (out[gone] == 0).all() and -1 not in asked
+        assert np.array_equal(out[~gone], full[~gone])
+
+
 def test_routed_single_expert_is_dense_mlp():
     cfg, x, ids, mats = _tiny_int4_layer(1)
     ids1 = np.full((cfg.T, 1), 5, np.int32)
