@@ -222,7 +222,10 @@ def cpu_baseline(cfg_name: str, reps: int):
                        f"top-{cfg.elb_M}, INT4 dequantise + float64 SwiGLU of the touched "
                        f"experts, shared experts, combine) in {dt:.1f} s; BLAS matmuls on "
                        f"{cores} threads, the rest single-threaded NumPy; then {reps1} on one "
-                       f"BLAS thread"),
+                       f"BLAS thread ({cfg.T * reps1 / dt1:.2f} tokens/s): the time goes to "
+                       f"single-threaded NumPy (the stated-order router dot products and the "
+                       f"INT4 dequantisation), so the baseline is effectively single-threaded "
+                       f"whatever `cores` says"),
             "ms_per_layer": 1e3 * dt / reps,
             "single_thread_value": cfg.T * reps1 / dt1,
             "gbps": nbytes * reps / dt / 1e9,

@@ -96,6 +96,7 @@
 #include <type_traits>
 
 #include "ffn_device.hpp"
+#include "ffn_wide.hpp"
 #include "smoe_blocks.hpp"  // route_check (the layer call validates every step)
 
 namespace smoe {
@@ -1005,9 +1006,13 @@ long long gu_floats(long long T, long long k, long long I, long long Is) {
 size_t gu_region_bytes(long long T, long long k, long long I, long long Is) {
   return kEpochBytes + static_cast<size_t>(2 * gu_floats(T, k, I, Is)) * sizeof(float);
 }
+// (long windows also keep the fp16 h of the long-window FFN after that)
 size_t workspace_bytes(long long T, long long k, long long I, long long Is) {
-  return gu_region_bytes(T, k, I, Is);
+  const long long S = T * k;
+  const bool wide = S >= kWideMinSlots && S <= kWideMaxSlots;
+  return gu_region_bytes(T, k, I, Is) + (wide ? wide_h_bytes(T, k, I, Is) : 0);
 }
+
 
 // Weights of one group as the entry points hand them over.
 struct GroupWeights {
@@ -1221,6 +1226,33 @@ smoe_status build_plans(const char* who, StagePlans& p, const void* x, int T, in
   return SMOE_OK;
 }
 
+// Tiled weights and a long window: the long-window FFN (ffn_wide.hip), whose
+// fp16 h lives after the g/u region of the workspace. Returns false (nothing
+// enqueued) when it does not apply.
+bool try_wide(smoe_status& st, const char* who, const GroupWeights& r, const void* x, int T,
+              int k, int H, const int32_t* sorted_slots, const int32_t* offsets, int shared_I,
+              const void* swg, const void* swu, const void* swd, void* workspace,
+              float* slot_out, float* shared_out, hipStream_t s) {
+  if (!r.tiled) return false;
+  WideCall c{};
+  c.fmt = r.fmt;
+  c.G = r.G;
+  c.x = x;
+  c.T = T; c.k = k; c.E = r.E; c.H = H; c.I = r.I;
+  c.wg = r.wg; c.wu = r.wu; c.wd = r.wd;
+  c.sg = r.sg; c.su = r.su; c.sd = r.sd;
+  c.Is = shared_I;
+  c.swg = swg; c.swu = swu; c.swd = swd;
+  c.sorted_slots = sorted_slots;
+  c.offsets = offsets;
+  c.h = static_cast<uint8_t*>(workspace) + gu_region_bytes(T, k, r.I, shared_I);
+  c.slot_out = slot_out;
+  c.shared_out = shared_I > 0 ? shared_out : nullptr;
+  if (!wide_applicable(c)) return false;
+  st = wide_ffn(c, s, who);
+  return true;
+}
+
 // clear_ws: zero the workspace bytes this call uses before its launches
 // (the no-allocation entry point, whose workspace other calls share).
 smoe_status w4a16_ffn(int tiled,
@@ -1257,6 +1289,9 @@ smoe_status w4a16_ffn(int tiled,
                    shared_wg, shared_wu, shared_wd, slot_out, shared_out);
   if (st != SMOE_OK) return st;
   hipStream_t s = as_stream(stream);
+  if (try_wide(st, who, r, x, T, k, H, sorted_slots, expert_offsets, shared_I, shared_wg,
+               shared_wu, shared_wd, workspace, slot_out, shared_out, s))
+    return st;
   if (clear_ws) {
     const long long n16 = static_cast<long long>(gu_region_bytes(T, k, I, shared_I) / 16);
     const int grid = static_cast<int>(std::min<long long>((n16 + 255) / 256, 2048));
@@ -1307,6 +1342,10 @@ smoe_status fp16_ffn(int tiled,
       p.a1.mat[e] = p.a2.mat[e] = mat[e] >= 0 && mat[e] < n_mat ? mat[e] : -1;
   }
   hipStream_t s = as_stream(stream);
+  if (mat == nullptr &&
+      try_wide(st, who, r, x, T, k, H, sorted_slots, expert_offsets, shared_I, shared_wg,
+               shared_wu, shared_wd, workspace, slot_out, shared_out, s))
+    return st;
   return p.nc == 2 ? launch_ffn<kFp16, 128, 2>(p, s) : launch_ffn<kFp16, 128, 1>(p, s);
 }
 

@@ -572,6 +572,69 @@ def test_w4a16_ffn_shapes(smoe, E, k, T, H, I, G, tiled):
     assert err <= ROW_TOL, err
 
 
+def _long_window_ids(rng, T, k, E, skew, drop):
+    # Zipf-skewed routing (some experts take several 64-slot chunks, some
+    # none), optionally with dropped slots
+    p = 1.0 / np.arange(1, E + 1) ** skew
+    p /= p.sum()
+    perm = rng.permutation(E)
+    ids = np.stack([perm[rng.choice(E, k, replace=False, p=p)] for _ in range(T)]).astype(np.int32)
+    if drop:
+        ids[rng.random(ids.shape) < drop] = -1
+    return ids
+
+
+@pytest.mark.parametrize("E,k,T,H,I,G,Is,drop", [
+    (8, 2, 600, 256, 384, 128, 0, 0.0),      # 150 slots per expert: 3 chunks each
+    (16, 4, 300, 384, 256, 64, 256, 0.0),    # with the shared expert (5 chunks of 64 tokens)
+    (64, 6, 200, 256, 256, 32, 384, 0.02),   # skewed, g32, dropped slots
+    (32, 8, 512, 128, 128, 128, 128, 0.0),   # 4096 slots, the longest window taken
+])
+def test_w4a16_ffn_long_window(smoe, E, k, T, H, I, G, Is, drop):
+    # windows of at least 1024 slots over tiled weights take the long-window
+    # FFN: every slot row against the oracle
+    rng = np.random.default_rng(T + E)
+    q = _synthetic_int4(E, H, I, G, seed=E + T)
+    x = rng.standard_normal((T, H)).astype(np.float16)
+    ids = _long_window_ids(rng, T, k, E, 1.1, drop)
+    shared = None
+    if Is:
+        shared = tuple((rng.standard_normal(sh) * 0.02).astype(np.float16)
+                       for sh in ((Is, H), (Is, H), (H, Is)))
+    got = run_w4a16(smoe, x, ids, E, I, G, q["wg_q"], q["wg_s"], q["wu_q"], q["wu_s"],
+                    q["wd_q"], q["wd_s"], shared=shared, calls=2, tiled=True)
+    if shared is not None:
+        got, got_s = got
+        assert row_rel_err(got_s, oracle.shared_ffn(x, *shared)) <= ROW_TOL
+    ref = oracle.routed_ffn_expertwise(x, ids, lambda e: tuple(
+        oracle.dequant_int4(q[n + "_q"][e], q[n + "_s"][e], G) for n in ("wg", "wu", "wd")))
+    assert np.isfinite(got).all()
+    assert row_rel_err(got, ref) <= ROW_TOL
+    dropped = ids.reshape(-1) < 0
+    assert (got[dropped] == 0).all()
+
+
+@pytest.mark.parametrize("Is", [0, 256])
+def test_fp16_ffn_long_window(smoe, Is):
+    E, k, T, H, I = 12, 4, 300, 256, 384
+    rng = np.random.default_rng(77 + Is)
+    x = rng.standard_normal((T, H)).astype(np.float16)
+    wg = (rng.standard_normal((E, I, H)) * 0.02).astype(np.float16)
+    wu = (rng.standard_normal((E, I, H)) * 0.02).astype(np.float16)
+    wd = (rng.standard_normal((E, H, I)) * 0.02).astype(np.float16)
+    ids = _long_window_ids(rng, T, k, E, 1.1, 0.0)
+    shared = None
+    if Is:
+        shared = tuple((rng.standard_normal(sh) * 0.02).astype(np.float16)
+                       for sh in ((Is, H), (Is, H), (H, Is)))
+    got = run_fp16(smoe, x, ids, E, I, wg, wu, wd, shared=shared, calls=2, tiled=True)
+    if shared is not None:
+        got, got_s = got
+        assert row_rel_err(got_s, oracle.shared_ffn(x, *shared)) <= ROW_TOL
+    ref = oracle.routed_ffn_expertwise(x, ids, lambda e: (wg[e], wu[e], wd[e]))
+    assert row_rel_err(got, ref) <= ROW_TOL
+
+
 def test_w4a16_ffn_one_hot_expert(smoe):
     # every slot on one expert: many chunks of the same expert
     E, k, T, H, I, G = 8, 1, 300, 256, 256, 64
