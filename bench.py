@@ -41,7 +41,8 @@ MIN_ROTATION_BYTES = 1 << 30    # rotate weight copies over at least this many b
 FFN_CALLS_PER_GRAPH = 8         # expert-FFN calls per timing graph
 PROFILES = os.path.join(ROOT, "profiles")
 FFN_SOURCES = [os.path.join(ROOT, "quantized_speculative_expert_amd", "csrc", f)
-               for f in ("ffn.hip", "smoe_internal.hpp")]
+               for f in ("ffn.hip", "ffn_device.hpp", "ffn_wide.hip", "ffn_wide.hpp",
+                         "smoe_internal.hpp")]
 
 
 def log(msg: str) -> None:

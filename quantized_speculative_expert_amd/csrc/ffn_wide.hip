@@ -410,7 +410,11 @@ __global__ __launch_bounds__(kWThreads, 1) void wide_ffn_kernel(WArgs a) {
   };
   // one block at k offset kk within the phase
   auto compute = [&](const Entry& en, const Cur& cu, int kk) __attribute__((always_inline)) {
-    auto live = [&](int cg) __attribute__((always_inline)) { return 16 * cg < cur_m; };
+    // Every column group is computed, also past the chunk's positions (their
+    // rows repeat the last staged one and are never stored): with a run-time
+    // skip per column group between the MFMAs, the g32 kernels gave wrong
+    // rows at a ring depth of four blocks, and without the branches they do
+    // not.
     if (WK == kInt4 && cu.fmt == kInt4) {
 #pragma unroll
       for (int m = 0; m < NMAT; ++m) {
@@ -429,7 +433,6 @@ __global__ __launch_bounds__(kWThreads, 1) void wide_ffn_kernel(WArgs a) {
           const float sc = static_cast<float>(bitcast<_Float16>(sbits));
 #pragma unroll
           for (int cg = 0; cg < NC; ++cg) {
-            if (!live(cg)) continue;
             f32x4 t = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
             for (int qq = 0; qq < PER; ++qq) {
@@ -446,7 +449,6 @@ __global__ __launch_bounds__(kWThreads, 1) void wide_ffn_kernel(WArgs a) {
     } else {
 #pragma unroll
       for (int cg = 0; cg < NC; ++cg) {
-        if (!live(cg)) continue;
         const f16x8 A = lds16(arow[cg] + 2 * (kk + 8 * g));
 #pragma unroll
         for (int m = 0; m < NMAT; ++m)

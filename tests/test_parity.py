@@ -588,6 +588,7 @@ def _long_window_ids(rng, T, k, E, skew, drop):
     (8, 2, 600, 256, 384, 128, 0, 0.0),      # 150 slots per expert: 3 chunks each
     (16, 4, 300, 384, 256, 64, 256, 0.0),    # with the shared expert (5 chunks of 64 tokens)
     (64, 6, 200, 256, 256, 32, 384, 0.02),   # skewed, g32, dropped slots
+    (64, 6, 200, 256, 256, 32, 0, 0.0),      # g32 alone (wrong rows once, with per-column-group branches)
     (32, 8, 512, 128, 128, 128, 128, 0.0),   # 4096 slots, the longest window taken
 ])
 def test_w4a16_ffn_long_window(smoe, E, k, T, H, I, G, Is, drop):
