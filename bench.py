@@ -86,6 +86,11 @@ def parse_args():
                    help="layers of the offloaded stack (--offload)")
     p.add_argument("--offload-windows", type=int, default=6,
                    help="timed windows per mode (--offload), after two untimed ones")
+    p.add_argument("--stack", action="store_true",
+                   help="time every layer of a multi-layer config (batch: 26 layers of 544 "
+                        "tokens) as one step: each layer with its own activations, router and "
+                        "weights, the activation counter accumulated over the stack and ranked "
+                        "once at its end")
     p.add_argument("--specfit", action="store_true",
                    help="instead of the layer throughput: SpecFit subtree selection on the host "
                         "(18-node top-2 pools of depth 5, K = 7, 48 layers x 128 experts, "
@@ -317,6 +322,109 @@ def compare_ffn(base, layers, fused: bool, stream, batched_us: float) -> dict:
                      "FP16 = the batched call over FP16 routed weights (4x the bytes)")}
 
 
+def stack_bench(args) -> int:
+    """The whole layer stack as one step: every layer is the draft layer
+    (routing, alignment, ELB update of its own counter row, W4A16 FFN with the
+    shared experts, combine) over its own activations, router, Zipf router
+    skew and device copy of the expert weights (the generated experts of
+    layer 0, copied once per layer, so that every layer streams distinct
+    bytes). The counter rows accumulate over the stack; the last layer ranks
+    the top-M plan over all of them. One HIP graph holds the stack."""
+    import torch
+    from quantized_speculative_expert_amd.layer import DeviceLayer
+    from workload import get_config, make_activations, make_layer, make_router
+    from workload.gen import zipf_bias
+
+    cfg = get_config(args.config)
+    if cfg.layers < 2:
+        raise SystemExit(f"--stack needs a multi-layer config ({cfg.name} has one layer)")
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    log(f"generating {cfg.name} layer 0 (seed 0)")
+    inp = make_layer(cfg, seed=0, layer=0)
+    base = DeviceLayer(inp, device=dev, elb_layers=cfg.layers, tiled=args.layout == "tiled")
+    del inp
+    runners = [base]
+    for l in range(1, cfg.layers):
+        r = base.with_weight_copy()
+        r.x = torch.from_numpy(make_activations(cfg, 0, l)).to(dev)
+        r.w_router.copy_(torch.from_numpy(make_router(cfg, 0, l)))
+        if cfg.zipf_s > 0:
+            r.router_bias.copy_(torch.from_numpy(zipf_bias(cfg.E, cfg.zipf_s, 0, l)))
+        runners.append(r)
+    log(f"{cfg.layers} layers x {base.weight_bytes() / 2**20:.1f} MiB of weights resident")
+    L = cfg.layers
+
+    def step():
+        for l, r in enumerate(runners):
+            r.run(layer=l, rank=l == L - 1)
+
+    # eager once, layer by layer, to count each layer's active experts
+    n_active = []
+    for l, r in enumerate(runners):
+        r.run(layer=l, rank=l == L - 1)
+        n_active.append(int(base.n_active.item()))
+    torch.cuda.synchronize()
+    cap = torch.cuda.Stream(device=dev)
+    cap.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(cap):
+        with torch.cuda.graph(g, stream=cap):
+            step()
+    torch.cuda.current_stream().wait_stream(cap)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    log(f"warmup {args.warmup} stack steps")
+    for _ in range(args.warmup):
+        g.replay()
+    torch.cuda.synchronize()
+    K = args.steps
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(K + 1)]
+    log(f"timing {K} stack steps")
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ev[0].record(stream)
+    for i in range(K):
+        g.replay()
+        ev[i + 1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    step_us = [1e3 * ev[i].elapsed_time(ev[i + 1]) for i in range(K)]
+    total = sum(layer_bytes(base, n)["total"] for n in n_active)
+    gbps = total * K / wall / 1e9
+    out = {
+        "metric": f"batched {L}-layer stack tokens/sec (one step = every layer once)",
+        "value": round(cfg.T * K / wall, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(1e3 * wall / K, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16",
+        "data": "synthetic",
+        "config": {
+            "workload": (f"{cfg.name}: {cfg.description}; seed 0; all {L} layers per step, "
+                         "each with its own activations, router and weight copy"),
+            "T": cfg.T, "E": cfg.E, "k": cfg.k, "H": cfg.H, "I": cfg.I, "G": cfg.G,
+            "shared_I": cfg.shared_I, "elb_M": cfg.elb_M, "layers": L,
+            "weight_layout": args.layout,
+        },
+        "stack_us": {k_: round(v, 2) for k_, v in percentiles(step_us).items()},
+        "layer_us_mean": round(sum(step_us) / len(step_us) / L, 2),
+        "n_active": n_active,
+        "stack_bytes": total,
+        "hbm_gbps": round(gbps, 1),
+        "hbm_frac": round(gbps / PEAK_HBM_GBPS, 4),
+        "roofline": None,
+        "cpu_baseline": None,
+    }
+    print(json.dumps(out), flush=True)
+    return 0
+
+
 def specfit_bench(args) -> int:
     """Selection time per verification cycle: the library's depth-first search
     against the oracle's brute force on the same seeded pools (Qwen3-30B-A3B
@@ -534,6 +642,8 @@ def main() -> int:
         return copy_calibration(args.copy_calibration, args.steps)
     if args.offload:
         return offload_bench(args)
+    if args.stack:
+        return stack_bench(args)
     from quantized_speculative_expert_amd.layer import DeviceLayer
     from workload import get_config, make_layer
 

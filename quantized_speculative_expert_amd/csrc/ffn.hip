@@ -27,7 +27,9 @@
 //   row tile is 128 rows of gate and up (stage 1) or 256 rows of down
 //   (stage 2): 16 / 32 rows per wave of an 8-wave workgroup. The reduction
 //   dim K is cut into parts of D blocks (4 in stage 1, 3 in stage 2, whose
-//   work is smaller and so is cut finer). An item is (chunk, row tile, part);
+//   work is smaller and so is cut finer; 2 in an INT4 stage 1 with 32-slot
+//   chunks and x not resident, whose accumulators and staged rows leave no
+//   registers for a deeper ring without spilling). An item is (chunk, row tile, part);
 //   the shared expert's items come first, the routed experts' after them,
 //   so the static runs below hold the shared tiles (every token: the
 //   widest items) and the dynamic tail is made of routed items.
@@ -133,9 +135,14 @@ constexpr int kRowPad = 16;                // bytes of padding per staged row
 #endif
 constexpr int kD1 = SMOE_FFN_D1;           // blocks per item, stage 1 (8 KB per wave)
 constexpr int kD2 = SMOE_FFN_D2;           // blocks per item, stage 2 (finer: fewer items per WG)
-constexpr int stage_d(int stage) { return stage == 1 ? kD1 : kD2; }
+constexpr int kD1Narrow = 2;               // stage 1, INT4, NC = 2, x staged per item
+constexpr int stage_d(int stage, int wk, int nc, int xres) {
+  return stage == 2 ? kD2 : (wk == kInt4 && nc == 2 && !xres ? kD1Narrow : kD1);
+}
 // staged phases are whole INT4 items of the stage
-constexpr int phase_k(int stage) { return stage_d(stage) * 128; }
+constexpr int phase_k(int stage, int wk, int nc, int xres) {
+  return stage_d(stage, wk, nc, xres) * 128;
+}
 #ifndef SMOE_FFN_MAX_WG
 #define SMOE_FFN_MAX_WG 512
 #endif
@@ -208,7 +215,7 @@ template <int WK, int G, int STAGE, int NC, int XRES>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) void ffn_kernel(
     FfnArgs a) {
   static_assert(XRES == 0 || STAGE == 1, "x is resident in stage 1 only");
-  constexpr int D = stage_d(STAGE);
+  constexpr int D = stage_d(STAGE, WK, NC, XRES);
   constexpr int NQ = WK == kInt4 ? 128 / G : 1;  // INT4 group scales per block
   extern __shared__ __align__(16) uint8_t smem[];
   int* s_off = reinterpret_cast<int*>(smem);
@@ -243,7 +250,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
   const int ep = a.hdr[STAGE == 1 ? 0 : 1];
   float* gu = a.gu + ((STAGE == 1 ? ep : ep - 1) & 1) * a.gu_buf;  // this call's g/u
   if (tid <= E) s_off[tid] = min(max(offv, 0), a.S);  // clamped to [0, S]
-  if (tid < E) s_mat[tid] = matv;
+  if (a.has_mat && tid < E) s_mat[tid] = matv;
   // (stage 1 with x resident keeps the token of each sorted slot instead)
   constexpr bool xres = XRES != 0;
   if (a.slots_lds) {
@@ -304,7 +311,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
     for (int i = 0; i < 4; ++i) {
       const int e = 4 * lane + i;
       // (experts left out of the call have no chunks)
-      n[i] = e < E && s_mat[e] >= 0 ? (max(s_off[e + 1] - s_off[e], 0) + csz0 - 1) / csz0 : 0;
+      n[i] = e < E && (!a.has_mat || s_mat[e] >= 0)
+                 ? (max(s_off[e + 1] - s_off[e], 0) + csz0 - 1) / csz0 : 0;
       tot += n[i];
     }
     const int incl = wave_inclusive_scan(tot);
@@ -438,7 +446,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
 #pragma unroll
       for (int i = 0; i < 4; ++i) n += __popcll(__ballot(4 * lane + i < E && cp[i] <= it.chunk));
       it.e = uniform(max(n - 1, 0));
-      it.me = uniform(s_mat[it.e]);
+      it.me = a.has_mat ? uniform(s_mat[it.e]) : it.e;
       it.seg0 = s_off[it.e] + (it.chunk - s_cp[it.e]) * csz0;
       it.m = min(csz0, s_off[it.e + 1] - it.seg0);
     } else {
@@ -1057,9 +1065,13 @@ struct StagePlans {
 // LDS layout of a stage: the table, the sorted slots, then rows_lds staged
 // rows of the phase length (a multiple of whole INT4 items, balanced over
 // the phases that the longest K needs).
+int xs_offset(long long S) {
+  return kTabBytes + static_cast<int>(((S <= kMaxSlotsLds ? S : kMaxChunk) * 4 + 15) / 16 * 16);
+}
+
 int plan_lds(FfnArgs& a, int kmax, int kunit) {
   a.slots_lds = a.S <= kMaxSlotsLds ? 1 : 0;
-  a.xs_off = kTabBytes + ((a.slots_lds ? a.S : kMaxChunk) * 4 + 15) / 16 * 16;
+  a.xs_off = xs_offset(a.S);
   const int per_row = (kLdsBudget - a.xs_off) / a.rows_lds;
   const int kph_cap = std::max(kunit, (per_row - kRowPad) / 2 / kunit * kunit);
   const int phases = (kmax + kph_cap - 1) / kph_cap;
@@ -1087,6 +1099,13 @@ void make_plans(StagePlans& p, const void* x, int T, int k, int H, const int32_t
   a1.rows_lds = 1;
   for (int i = 0; i < n_groups; ++i) a1.rows_lds = std::max(a1.rows_lds, gw[i].csz);
   p.nc = a1.rows_lds > 16 ? 2 : 1;
+  // stage 1 keeps all of x in LDS when it fits beside the table and the
+  // sorted slots and the routed chunks are narrow: items then never restage
+  // and the tail goes out one item at a time. Decided first: it sets the
+  // stage-1 item size.
+  const long long xres_bytes = xs_offset(S) + static_cast<long long>(T) * (2 * H + kRowPad);
+  const bool xres = S <= kMaxSlotsLds && gw[0].csz <= 16 && xres_bytes <= kLdsBudget;
+  const int d1 = stage_d(1, gw[0].fmt, p.nc, xres);
   FfnArgs& a2 = p.a2;
   a2 = a1;
   p.items1 = p.items2 = 0;
@@ -1094,25 +1113,21 @@ void make_plans(StagePlans& p, const void* x, int T, int k, int H, const int32_t
   for (int i = 0; i < n_groups; ++i) {
     const GroupWeights& w = gw[i];
     const long long chunks = i == 0 ? a1.chunks_upper : (T + w.csz - 1) / w.csz;
-    set_matrix(a1.grp[i], w, w.I, H, w.wg, w.sg, stage_d(1));
+    set_matrix(a1.grp[i], w, w.I, H, w.wg, w.sg, d1);
     a1.grp[i].w1 = static_cast<const uint8_t*>(w.wu);
     a1.grp[i].s1 = static_cast<const uint16_t*>(w.su);
     a1.grp[i].tiles = tiles_of(w.I, 16);
     p.items1 += chunks * a1.grp[i].tiles * a1.grp[i].parts;
-    set_matrix(a2.grp[i], w, H, w.I, w.wd, w.sd, stage_d(2));
+    set_matrix(a2.grp[i], w, H, w.I, w.wd, w.sd, stage_d(2, gw[0].fmt, p.nc, 0));
     a2.grp[i].w1 = nullptr;
     a2.grp[i].s1 = nullptr;
     a2.grp[i].tiles = tiles_of(H, 32);
     p.items2 += chunks * a2.grp[i].tiles * a2.grp[i].parts;
     kmax2 = std::max(kmax2, w.I);
   }
-  p.lds1 = plan_lds(a1, H, phase_k(1));
-  p.lds2 = plan_lds(a2, kmax2, phase_k(2));
-  // stage 1 keeps all of x in LDS when it fits beside the table and the
-  // sorted slots and the routed chunks are narrow: items then never restage
-  // and the tail goes out one item at a time
-  const long long xres_bytes = a1.xs_off + static_cast<long long>(T) * (2 * H + kRowPad);
-  if (a1.slots_lds && gw[0].csz <= 16 && xres_bytes <= kLdsBudget) {
+  p.lds1 = plan_lds(a1, H, phase_k(1, gw[0].fmt, p.nc, xres));
+  p.lds2 = plan_lds(a2, kmax2, phase_k(2, gw[0].fmt, p.nc, 0));
+  if (xres) {
     a1.xres = 1;
     a1.rows_lds = T;
     a1.kph = H;
