@@ -98,6 +98,7 @@
 #include <type_traits>
 
 #include "ffn_device.hpp"
+#include "decode.hpp"
 #include "ffn_wide.hpp"
 #include "smoe_blocks.hpp"  // route_check (the layer call validates every step)
 
@@ -1014,11 +1015,13 @@ long long gu_floats(long long T, long long k, long long I, long long Is) {
 size_t gu_region_bytes(long long T, long long k, long long I, long long Is) {
   return kEpochBytes + static_cast<size_t>(2 * gu_floats(T, k, I, Is)) * sizeof(float);
 }
-// (long windows also keep the fp16 h of the long-window FFN after that)
-size_t workspace_bytes(long long T, long long k, long long I, long long Is) {
+// (long windows also keep the fp16 h of the long-window FFN after that,
+// one-token windows the region of the single-token layer)
+size_t workspace_bytes(long long T, long long k, long long H, long long I, long long Is) {
   const long long S = T * k;
   const bool wide = S >= kWideMinSlots && S <= kWideMaxSlots;
-  return gu_region_bytes(T, k, I, Is) + (wide ? wide_h_bytes(T, k, I, Is) : 0);
+  return gu_region_bytes(T, k, I, Is) + (wide ? wide_h_bytes(T, k, I, Is) : 0) +
+         (T == 1 ? decode_region_bytes(k, H, I, Is) : 0);
 }
 
 
@@ -1189,7 +1192,7 @@ smoe_status check_common(const char* who, const void* x, int T, int k, int E, in
   if (T == 0) return SMOE_OK;
   SMOE_REQUIRE(x && sorted_slots && offsets && workspace && slot_out, SMOE_EINVAL,
                "%s: null pointer", who);
-  const size_t need = workspace_bytes(T, k, I, shared_I);
+  const size_t need = workspace_bytes(T, k, H, I, shared_I);
   SMOE_REQUIRE(ws_bytes >= need, SMOE_EINVAL, "%s: workspace of %zu bytes is below the %zu needed",
                who, ws_bytes, need);
   SMOE_REQUIRE(aligned16(x) && (reinterpret_cast<uintptr_t>(workspace) & 255u) == 0 &&
@@ -1413,6 +1416,35 @@ smoe_status moe_layer(int tiled,
   st = build_plans(who, p, x, T, k, H, sorted_slots, expert_offsets, workspace, r, shared_I,
                    shared_wg, shared_wu, shared_wd, slot_out, shared_out);
   if (st != SMOE_OK) return st;
+  if (tiled && decode_applicable(T, k, E, H, I, shared_I, group_size)) {
+    // one token: the single-token layer, two launches with the routing
+    // inside the first (same outputs as the steps below)
+    DecodeCall c{};
+    c.f.r = ra;
+    c.f.counts = expert_counts;
+    c.f.offsets = expert_offsets;
+    c.f.sorted_slots = sorted_slots;
+    c.f.active = active_experts;
+    c.f.n_active = n_active;
+    c.f.elb_counts = elb_counts;
+    c.f.plan_ids = plan_ids;
+    c.f.plan_counts = plan_counts;
+    c.f.L = L;
+    c.f.layer = layer;
+    c.f.M = elb_counts != nullptr ? M : 0;
+    c.f.elb_clear = (elb_flags & SMOE_ELB_CLEAR_AFTER) ? 1 : 0;
+    c.G = group_size;
+    c.I = I;
+    c.Is = shared_I;
+    c.wg = wg_q; c.wu = wu_q; c.wd = wd_q;
+    c.sg = wg_s; c.su = wu_s; c.sd = wd_s;
+    c.swg = shared_wg; c.swu = shared_wu; c.swd = shared_wd;
+    c.region = static_cast<uint8_t*>(workspace) + gu_region_bytes(T, k, I, shared_I);
+    c.slot_out = slot_out;
+    c.shared_out = shared_I > 0 ? shared_out : nullptr;
+    c.y = y;
+    return decode_layer(c, as_stream(stream), who);
+  }
   // (the steps' own checks pass again; they enqueue the launches)
   st = smoe_route_align_elb(x, w_router, logit_bias, T, H, E, k, flags, topk_ids, topk_w,
                             logits, shared_gate_w, shared_gate, expert_counts, expert_offsets,
@@ -1433,7 +1465,7 @@ using namespace smoe;
 
 extern "C" size_t smoe_ffn_workspace_bytes(int T, int k, int E, int H, int I, int shared_I) {
   if (T <= 0 || k <= 0 || E <= 0 || H <= 0 || I <= 0 || shared_I < 0) return 0;
-  return workspace_bytes(T, k, I, shared_I);
+  return workspace_bytes(T, k, H, I, shared_I);
 }
 
 extern "C" smoe_status smoe_w4a16_expert_ffn(
@@ -1460,7 +1492,7 @@ extern "C" smoe_status smoe_w4a16_expert_ffn_noalloc(
                "%s: group size must be 32, 64 or 128 (got %d)", who, group_size);
   // the size limit first: it needs no device
   if (T > 0 && k > 0 && E > 0 && H > 0 && I > 0 && shared_I >= 0) {
-    const size_t need = workspace_bytes(T, k, I, shared_I);
+    const size_t need = workspace_bytes(T, k, H, I, shared_I);
     SMOE_REQUIRE(need <= SMOE_NOALLOC_SCRATCH_BYTES, SMOE_EUNSUPPORTED,
                  "%s: the window needs %zu bytes of workspace, above the %zu bytes of the "
                  "library's static workspace (T=%d k=%d I=%d shared_I=%d); use "

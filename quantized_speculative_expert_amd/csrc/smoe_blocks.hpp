@@ -360,9 +360,12 @@ struct alignas(16) RouteBlockSmem {
 // top-k of tokens w, w + NT/64, ... (the IDs also go to LDS), then
 // align_block_t sorts the slots from LDS, then elb_block updates the
 // layer's counter row and ranks every layer. The results equal those of the
-// three separate kernels.
+// three separate kernels. With `staged`, the caller has already put the
+// T x E logits in sm.lg, followed by the T raw shared-gate dots (when the
+// layer has a gate), and the block reads neither from global memory.
 template <int NT>
-__device__ __forceinline__ void route_align_elb_block(const FusedArgs& f, RouteBlockSmem<NT>& sm) {
+__device__ __forceinline__ void route_align_elb_block(const FusedArgs& f, RouteBlockSmem<NT>& sm,
+                                                      bool staged = false) {
   constexpr int kWaves = NT / kWave;
   const RouteArgs& a = f.r;
   const int wave = threadIdx.x / kWave;
@@ -376,8 +379,8 @@ __device__ __forceinline__ void route_align_elb_block(const FusedArgs& f, RouteB
   int* sel = &sm.al.exp_off[0] + wave * kMaxK;
   // all logits in one round trip when they fit, then the top-k from LDS
   const int n_lg = a.T * a.E;
-  const bool lg_in_lds = n_lg <= kFusedMaxLogits;
-  if (lg_in_lds) {
+  const bool lg_in_lds = staged || n_lg <= kFusedMaxLogits;
+  if (lg_in_lds && !staged) {
     for (int i = threadIdx.x; i < n_lg; i += NT) sm.lg[i] = a.logits[i];
     __syncthreads();
   }
@@ -391,8 +394,10 @@ __device__ __forceinline__ void route_align_elb_block(const FusedArgs& f, RouteB
       a.wout[static_cast<size_t>(t) * a.k + lane] = w;
       sm.ids[t * a.k + lane] = id;
     }
-    if (a.gate != nullptr && a.gate_w != nullptr && lane == 0)
-      a.gate[t] = 1.0f / (1.0f + expf(-a.gate[t]));
+    if (a.gate != nullptr && a.gate_w != nullptr && lane == 0) {
+      const float raw = staged ? sm.lg[n_lg + t] : a.gate[t];
+      a.gate[t] = 1.0f / (1.0f + expf(-raw));
+    }
   }
   __syncthreads();
   const int S = a.T * a.k;
