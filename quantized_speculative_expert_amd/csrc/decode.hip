@@ -20,8 +20,9 @@
 //       workgroup 0 then gathers them and runs the top-k, the alignment
 //       and the ELB update (the same block as smoe_route_align_elb) for
 //       the call's outputs;
-//     - the shared experts need no routing: their workgroups stream from
-//       the first cycle, while the router runs;
+//     - the shared experts need no routing: their workgroups stream as soon
+//       as the router rows are out (so that the rows' loads do not queue
+//       behind the stream), while the routed workgroups take the top-k;
 //     - each routed workgroup loads its activations, gathers the published
 //       router rows and takes the top-k itself (the same wave routine as
 //       the routing calls, so the same experts), then streams two 16-row
@@ -70,6 +71,7 @@ struct DArgs {
   const uint8_t *swg, *swu, *swd;       // shared FP16, tiled
   int E, H, I, Is, k;
   int nL, nS, nR;                       // router / shared / routed workgroups of launch 1
+  int sp;                               // launch 2: parts of the shared expert's down K
   int* ctl;                             // [kCtlTimeout]
   uint64_t* lgw;                        // [E + 1]: router rows (row E: the raw gate dot)
   _Float16* h_r;                        // [k][I]
@@ -216,10 +218,102 @@ __device__ __forceinline__ float row_sum(float v) {
 }
 
 struct UpSmem {
-  RouteBlockSmem<kDT> route;   // workgroup 0: the routing block; routed workgroups: the top-k
+  float lg[kMaxE + 1];         // the router rows (workgroup 0 and the routed workgroups)
+  uint64_t keys[kMaxE];        // the top-k's scratch
+  int sel[kMaxK];
+  int ids[kMaxK];              // workgroup 0: the top-k
+  int pre[kMaxE];              // workgroup 0: the layer's counter row, read first
+  int row[kMaxE];              // workgroup 0: a counter row being ranked
   float red[kDW][2][2][16];    // [wave][slab][gate, up][row]
   int bcast;
 };
+
+// The routing outputs of the one token, from its router rows in sm.lg: the
+// same values as route_align_elb_block gives at T = 1, without its general
+// machinery (k slots, each a distinct expert):
+//   top-k and weights (the same wave routine), the shared gate's sigmoid;
+//   counts[e] = 1 for a picked expert, offsets[e] = picked experts below e,
+//   sorted_slots[offsets[ids[j]]] = j, active = the picked experts
+//   ascending (then -1), n_active = k;
+//   ELB: the layer's row gains one per picked expert; every layer's row is
+//   ranked (count descending, ID ascending) into its top-M plan; with the
+//   clear flag every row is then zeroed.
+// Every output word is written once, after the loads; the barriers order
+// LDS only.
+__device__ void single_token_route(const FusedArgs& f, UpSmem& sm, int tid, int wave, int lane) {
+  const RouteArgs& a = f.r;
+  const int E = a.E, k = a.k;
+  if (wave == 0) {
+    int id;
+    float w;
+    wave_topk(sm.lg, E, k, a.flags, sm.keys, sm.sel, &id, &w);
+    if (lane < k) {
+      a.ids[lane] = id;
+      a.wout[lane] = w;
+      sm.ids[lane] = id;
+    }
+    if (a.gate != nullptr && a.gate_w != nullptr && lane == 0)
+      a.gate[0] = 1.0f / (1.0f + expf(-sm.lg[E]));
+    if (lane == 0) {
+      f.offsets[E] = k;
+      f.n_active[0] = k;
+    }
+  }
+  block_sync_lds();
+  if (tid < E) {
+    int below = 0, picked = 0;
+    for (int j = 0; j < k; ++j) {
+      below += sm.ids[j] < tid ? 1 : 0;
+      picked += sm.ids[j] == tid ? 1 : 0;
+    }
+    f.counts[tid] = picked;
+    f.offsets[tid] = below;
+    // active[i]: the picked expert with i picked experts below it
+    int act = -1;
+    for (int j = 0; j < k; ++j) {
+      int r = 0;
+      for (int i = 0; i < k; ++i) r += sm.ids[i] < sm.ids[j] ? 1 : 0;
+      if (r == tid) act = sm.ids[j];
+    }
+    f.active[tid] = act;
+  }
+  if (tid < k) {
+    int pos = 0;
+    for (int i = 0; i < k; ++i) pos += sm.ids[i] < sm.ids[tid] ? 1 : 0;
+    f.sorted_slots[pos] = tid;
+  }
+  if (f.elb_counts == nullptr) return;
+  for (int l = 0; l < f.L; ++l) {
+    int32_t* crow = f.elb_counts + static_cast<size_t>(l) * E;
+    block_sync_lds();  // (the previous layer's ranking is done with sm.row)
+    if (tid < E) {
+      int v;
+      if (l == f.layer) {
+        int add = 0;
+        for (int j = 0; j < k; ++j) add += sm.ids[j] == tid ? 1 : 0;
+        v = sm.pre[tid] + add;
+        if (add != 0) crow[tid] = v;
+      } else {
+        v = crow[tid];
+      }
+      sm.row[tid] = v;
+    }
+    block_sync_lds();
+    if (f.M > 0 && tid < E) {
+      const int c = sm.row[tid];
+      int place = 0;
+      for (int e2 = 0; e2 < E; ++e2) {
+        const int c2 = sm.row[e2];
+        place += (c2 > c || (c2 == c && e2 < tid)) ? 1 : 0;
+      }
+      if (place < f.M) {
+        f.plan_ids[static_cast<size_t>(l) * f.M + place] = tid;
+        if (f.plan_counts != nullptr) f.plan_counts[static_cast<size_t>(l) * f.M + place] = c;
+      }
+    }
+    if (f.elb_clear && tid < E) crow[tid] = 0;
+  }
+}
 
 template <int G>
 __global__ __launch_bounds__(kDT) __attribute__((amdgpu_waves_per_eu(4))) void decode_up_kernel(
@@ -234,24 +328,31 @@ __global__ __launch_bounds__(kDT) __attribute__((amdgpu_waves_per_eu(4))) void d
   const _Float16* x = a.f.r.x;
   const bool gate_row = a.f.r.gate_w != nullptr;
 
-  // ---- router rows; workgroup 0 then routes, aligns and counts
+  // ---- router rows, published; workgroup 0 then routes, aligns, counts
   if (b < a.nL) {
+    // (workgroup 0 reads the layer's counter row before anything is stored)
+    const int pre =
+        b == 0 && a.f.elb_counts != nullptr && tid < a.E
+            ? a.f.elb_counts[static_cast<size_t>(a.f.layer) * a.E + tid] : 0;
     const int r = b * kDW + wave;
     if (r < a.E || (r == a.E && gate_row)) {
       const float v = router_row(a.f.r, r, lane);
       if (lane == 0) st_word(a.lgw + r, kTag | bitcast<uint32_t>(v));
     }
     if (b != 0) return;
-    // every row into LDS (the logits, then the raw gate dot), and out
+    if (tid < a.E) sm.pre[tid] = pre;
     const int nrow = a.E + (gate_row ? 1 : 0);
-    int ok = 1;
-    if (wave == 0) ok = gather_rows(a.lgw, nrow, sm.route.lg, lane) ? 1 : 0;
-    if (!__syncthreads_or(!ok)) {
-      for (int i = tid; i < a.E; i += kDT) a.f.r.logits[i] = sm.route.lg[i];
-      route_align_elb_block<kDT>(a.f, sm.route, true);
-    } else if (tid == 0) {
-      st_agent(a.ctl + kCtlTimeout, 1);
+    if (wave == 0) {
+      const bool ok = gather_rows(a.lgw, nrow, sm.lg, lane);
+      if (lane == 0) sm.bcast = ok ? 1 : 0;
     }
+    block_sync_lds();
+    if (!sm.bcast) {
+      if (tid == 0) st_agent(a.ctl + kCtlTimeout, 1);
+      return;
+    }
+    if (tid < a.E) a.f.r.logits[tid] = sm.lg[tid];
+    single_token_route(a.f, sm, tid, wave, lane);
     return;
   }
 
@@ -268,6 +369,13 @@ __global__ __launch_bounds__(kDT) __attribute__((amdgpu_waves_per_eu(4))) void d
     const int nblk = a.H / 32;
     const long long t0 = static_cast<long long>(sl) * nblk;
     constexpr int NB = 4;
+    // The router rows go first: their few loads would otherwise queue behind
+    // this stream and hold up every routed workgroup. (A timing gate only:
+    // the shared expert needs no routing, and the wait is bounded.)
+    if (tid == 0)
+      for (int n = 0; n < kSpinLimit && !(ld_word(a.lgw + a.E - 1) & kTag); ++n)
+        __builtin_amdgcn_s_sleep(2);
+    block_sync_lds();
     for (int b0 = wave; b0 < nblk; b0 += NB * kDW) {
       u32x4 tg[NB], tu[NB];
       f16x8 xo[NB];
@@ -306,18 +414,17 @@ __global__ __launch_bounds__(kDT) __attribute__((amdgpu_waves_per_eu(4))) void d
     }
     // slot j's expert: the top-k of the published router rows
     if (wave == 0) {
-      const bool ok = gather_rows(a.lgw, a.E, sm.route.lg, lane);
+      const bool ok = gather_rows(a.lgw, a.E, sm.lg, lane);
       int id = -1;
-      float w;
+      float w = 0.0f;
       if (ok) {
-        uint64_t* keys = reinterpret_cast<uint64_t*>(&sm.route.al.wave_cnt[0][0]);
-        wave_topk(sm.route.lg, a.E, a.k, a.f.r.flags, keys, &sm.route.al.exp_off[0], &id, &w);
+        wave_topk(sm.lg, a.E, a.k, a.f.r.flags, sm.keys, sm.sel, &id, &w);
       } else if (lane == 0) {
         st_agent(a.ctl + kCtlTimeout, 1);
       }
       if (lane == j) sm.bcast = ok ? id : -1;
     }
-    __syncthreads();
+    block_sync_lds();
     const int e = sm.bcast;
     if (e >= 0 && e < a.E) {
       constexpr int NQ = 128 / G;
@@ -369,7 +476,7 @@ __global__ __launch_bounds__(kDT) __attribute__((amdgpu_waves_per_eu(4))) void d
       sm.red[wave][h][1][lane] = us[h];
     }
   }
-  __syncthreads();
+  block_sync_lds();
   _Float16* const o = wave == 0 ? out[0] : out[1];
   if (wave < 2 && lane < 16 && o != nullptr) {
     float gv = 0.0f, uv = 0.0f;
@@ -383,23 +490,29 @@ __global__ __launch_bounds__(kDT) __attribute__((amdgpu_waves_per_eu(4))) void d
   }
 }
 
-constexpr int kSharedParts = 2;         // parts of a shared down slab
+constexpr int kDW2 = 8;                 // waves per workgroup of launch 2
+constexpr int kDT2 = kDW2 * kWave;
+constexpr int kMaxSharedParts = 8;      // parts of the shared expert's down K
 
-// (four workgroups per CU: every workgroup of the launch is resident at once)
+// Launch 2: one workgroup per (16-row slab of the output, part): a routed
+// slot's down rows (I / 128 blocks), or a share of the shared expert's K.
+// The slab's last part gathers the others. Launch 2 also clears the router
+// words for the next call.
+// (four workgroups per CU: about every workgroup of the launch is resident)
 template <int G>
-__global__ __launch_bounds__(kDT) __attribute__((amdgpu_waves_per_eu(8))) void decode_down_kernel(
+__global__ __launch_bounds__(kDT2) __attribute__((amdgpu_waves_per_eu(8))) void decode_down_kernel(
     DArgs a) {
-  __shared__ float red[kDW][16];
+  __shared__ float red[kDW2][16];
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
   const int lane = tid & 63;
   const int g = lane >> 4;
   const int r16 = lane & 15;
-  const int np = a.k + (a.Is > 0 ? kSharedParts : 0);
-  const int sl = blockIdx.x / np, part = blockIdx.x - sl * np;
-  // launch 1 is over: its words back to zero for the next call
   if (blockIdx.x == 0)
-    for (int i = tid; i <= a.E; i += kDT) st_word(a.lgw + i, 0);
+    for (int i = tid; i <= a.E; i += kDT2) st_word(a.lgw + i, 0);
+  const int np = a.k + a.sp;
+  const int item = blockIdx.x;
+  const int sl = item / np, part = item - sl * np;
   uint32_t dq_lo = 0x000F000Fu, dq_hi = 0x00F000F0u, dq_magic = 0x64006400u;
   asm volatile("" : "+v"(dq_lo), "+v"(dq_hi), "+v"(dq_magic));
   float acc = 0.0f;
@@ -412,13 +525,13 @@ __global__ __launch_bounds__(kDT) __attribute__((amdgpu_waves_per_eu(8))) void d
       const _Float16* h = a.h_r + static_cast<long long>(part) * a.I;
       constexpr int NQ = 128 / G;
       constexpr int NB = 2;
-      for (int b0 = wave; b0 < nblk; b0 += NB * kDW) {
+      for (int b0 = wave; b0 < nblk; b0 += NB * kDW2) {
         u32x4 tw[NB];
         Scales<G> sw[NB];
         f16x8 ho[NB][4];
 #pragma unroll
         for (int i = 0; i < NB; ++i) {
-          const int bk = min(b0 + i * kDW, nblk - 1);  // (past the end: loaded, not used)
+          const int bk = min(b0 + i * kDW2, nblk - 1);  // (past the end: loaded, not used)
           const long long t = t0 + bk;
           tw[i] = gload<u32x4>(a.wd + t * 1024 + 16 * lane);
           sw[i] = load_scales<G>(a.sd + (t * 16 + r16) * NQ);
@@ -428,46 +541,47 @@ __global__ __launch_bounds__(kDT) __attribute__((amdgpu_waves_per_eu(8))) void d
         }
 #pragma unroll
         for (int i = 0; i < NB; ++i)
-          if (b0 + i * kDW < nblk) acc += dot_int4<G>(tw[i], sw[i], ho[i], dq_lo, dq_hi, dq_magic);
+          if (b0 + i * kDW2 < nblk)
+            acc += dot_int4<G>(tw[i], sw[i], ho[i], dq_lo, dq_hi, dq_magic);
       }
     }
   } else {
     // ---- one part of the shared down matrix's K (FP16, K = Is)
-    const int q2 = part - a.k;
+    const int q = part - a.k;
     const int nblk = a.Is / 32;
-    const int lo = q2 * nblk / kSharedParts, hi = (q2 + 1) * nblk / kSharedParts;
+    const int lo = q * nblk / a.sp, hi = (q + 1) * nblk / a.sp;
     const long long t0 = static_cast<long long>(sl) * nblk;
     constexpr int NB = 6;
-    for (int b0 = lo + wave; b0 < hi; b0 += NB * kDW) {
+    for (int b0 = lo + wave; b0 < hi; b0 += NB * kDW2) {
       u32x4 tw[NB];
       f16x8 ho[NB];
 #pragma unroll
       for (int i = 0; i < NB; ++i) {
-        const int bk = min(b0 + i * kDW, hi - 1);
+        const int bk = min(b0 + i * kDW2, hi - 1);
         tw[i] = gload<u32x4>(a.swd + (t0 + bk) * 1024 + 16 * lane);
         ho[i] = gload<f16x8>(a.h_s + bk * 32 + 8 * g);
       }
 #pragma unroll
       for (int i = 0; i < NB; ++i)
-        if (b0 + i * kDW < hi) acc = dot8(bitcast<f16x8>(tw[i]), ho[i], acc);
+        if (b0 + i * kDW2 < hi) acc = dot8(bitcast<f16x8>(tw[i]), ho[i], acc);
     }
   }
 
   // ---- this part's 16 rows; the slab's last part combines them all
   acc = row_sum(acc);
   if (lane < 16) red[wave][lane] = acc;
-  __syncthreads();
+  block_sync_lds();
   if (wave != 0 || lane >= 16) return;
   float v = 0.0f;
 #pragma unroll
-  for (int w = 0; w < kDW; ++w) v += red[w][lane];
+  for (int w = 0; w < kDW2; ++w) v += red[w][lane];
   uint64_t* ws = a.partw + static_cast<long long>(sl) * np * 16 + lane;
   if (part != np - 1) {
     st_word(ws + part * 16, kTag | bitcast<uint32_t>(v));
     return;
   }
   // the other parts' words, all polled in each round, then back to zero
-  constexpr int kMaxParts = kMaxK + kSharedParts;
+  constexpr int kMaxParts = kMaxK + kMaxSharedParts;
   float pv[kMaxParts];
   bool have[kMaxParts];
 #pragma unroll
@@ -504,7 +618,8 @@ __global__ __launch_bounds__(kDT) __attribute__((amdgpu_waves_per_eu(8))) void d
   if (a.Is > 0) {
     float sh = 0.0f;
 #pragma unroll
-    for (int q = 0; q < kSharedParts; ++q) sh += pv[a.k + q];
+    for (int q = 0; q < kMaxSharedParts; ++q)
+      if (q < a.sp) sh += pv[a.k + q];
     a.shared_out[n] = sh;
     const float gate = a.f.r.gate != nullptr && a.f.r.gate_w != nullptr ? a.f.r.gate[0] : 1.0f;
     yv += gate * sh;
@@ -522,15 +637,21 @@ smoe_status launch_decode(const DArgs& a, hipStream_t st, const char* who) {
   hipLaunchKernelGGL(decode_up_kernel<G>, dim3(grid1), dim3(kDT), 0, st, a);
   smoe_status s = check_launch(who);
   if (s != SMOE_OK) return s;
-  const int np = a.k + (a.Is > 0 ? kSharedParts : 0);
-  hipLaunchKernelGGL(decode_down_kernel<G>, dim3(a.H / 16 * np), dim3(kDT), 0, st, a);
+  hipLaunchKernelGGL(decode_down_kernel<G>, dim3(a.H / 16 * (a.k + a.sp)), dim3(kDT2), 0, st, a);
   return check_launch(who);
 }
 
 }  // namespace
 
+// parts of the shared expert's down K: about four routed slots' blocks each
+int shared_parts(long long I, long long Is) {
+  if (Is <= 0) return 0;
+  const long long per = 4 * (I / 128), nblk = Is / 32;
+  return static_cast<int>(std::min<long long>(kMaxSharedParts, std::max(1ll, (nblk + per - 1) / per)));
+}
+
 size_t decode_region_bytes(long long k, long long H, long long I, long long Is) {
-  const long long np = k + (Is > 0 ? kSharedParts : 0);
+  const long long np = k + shared_parts(I, Is);
   return 256 + round256((kMaxE + 1) * 8) + round256(k * I * 2) + round256(Is * 2) +
          round256(H / 16 * np * 16 * 8);
 }
@@ -561,6 +682,7 @@ smoe_status decode_layer(const DecodeCall& c, hipStream_t st, const char* who) {
   a.nL = (a.E + (gate_row ? 1 : 0) + kDW - 1) / kDW;
   a.nS = a.Is / 16;
   a.nR = a.k * ((a.I / 16 + 1) / 2);
+  a.sp = shared_parts(a.I, a.Is);
   uint8_t* p = static_cast<uint8_t*>(c.region);
   a.ctl = reinterpret_cast<int*>(p);
   p += 256;

@@ -32,7 +32,7 @@ __global__ __launch_bounds__(kElbThreads) void elb_kernel(
   const int i = l - layer_begin;
   const int32_t* lid =
       (ids != nullptr && i >= 0 && i < n_layers) ? ids + static_cast<size_t>(i) * S : nullptr;
-  elb_block(cnt + static_cast<size_t>(l) * E, E, lid, S, M,
+  elb_block(cnt + static_cast<size_t>(l) * E, E, lid, lid != nullptr, S, M,
             plan_ids + static_cast<size_t>(l) * M,
             plan_counts != nullptr ? plan_counts + static_cast<size_t>(l) * M : nullptr, clear,
             hist, row);

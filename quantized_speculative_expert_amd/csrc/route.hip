@@ -153,7 +153,7 @@ __global__ __launch_bounds__(kTopkWaves * kWave) void topk_kernel(RouteArgs a) {
 // slots. The results equal those of the three separate kernels.
 __global__ __launch_bounds__(kAlignThreads) void topk_align_elb_kernel(FusedArgs f) {
   __shared__ RouteBlockSmem<kAlignThreads> sm;
-  route_align_elb_block<kAlignThreads>(f, sm);
+  route_align_elb_block(f, sm);
 }
 
 }  // namespace

@@ -10,6 +10,17 @@
 
 namespace smoe {
 
+// Workgroup barrier that orders LDS only. The blocks below hand over LDS
+// data between threads; their global outputs each go to an address that
+// one thread writes once and no thread of the block reads back, so the
+// barrier need not wait for the stores to complete (a full __syncthreads
+// waits for every store in flight, a memory round trip per barrier).
+__device__ __forceinline__ void block_sync_lds() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 // ------------------------------------------------------------------ top-k
 
 // Increasing map float -> uint32 with -0.0 and +0.0 sent to the same key.
@@ -43,7 +54,7 @@ __device__ __forceinline__ void wave_topk_n(const float* l, int E, int k, int fl
     else if (e < ((E + 7) & ~7)) lds_keys[e] = 0ull;
   }
   __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront", "local");
   int rank[NK];
 #pragma unroll
   for (int i = 0; i < NK; ++i) rank[i] = 0;
@@ -63,7 +74,7 @@ __device__ __forceinline__ void wave_topk_n(const float* l, int E, int k, int fl
     if (e < E && rank[i] < k) lds_sel[rank[i]] = e;
   }
   __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront", "local");
   // softmax over all E logits, evaluated at the selected experts
   const float mx = l[lds_sel[0]];
   float s = 0.0f;
@@ -106,6 +117,7 @@ struct alignas(16) AlignSmemT {
   int wave_base[NT / kWave][kMaxE];  // slots of expert e in earlier waves
   int exp_off[kMaxE + 1];
   int act_pos[kMaxE];
+  int act_list[kMaxE];               // the active list, -1 past its end
 };
 using AlignSmem = AlignSmemT<kAlignThreads>;
 
@@ -131,7 +143,7 @@ __device__ __forceinline__ void align_block_t(const int32_t* ids, int S, int E, 
 
   for (int i = threadIdx.x; i < kWaves * kMaxE; i += NT)
     (&sm.wave_cnt[0][0])[i] = 0;
-  __syncthreads();
+  block_sync_lds();
 
   // contiguous run of whole 64-slot chunks per wave
   const int nchunks = (S + kWave - 1) / kWave;
@@ -158,7 +170,7 @@ __device__ __forceinline__ void align_block_t(const int32_t* ids, int S, int E, 
     const int s = c * kWave + lane;
     count(s < S ? ids[s] : -1);
   }
-  __syncthreads();
+  block_sync_lds();
 
   // per expert: total, per-wave bases (only waves that own slots count)
   const int busy_waves = per_wave > 0 ? min(kWaves, (nchunks + per_wave - 1) / per_wave) : 0;
@@ -171,7 +183,7 @@ __device__ __forceinline__ void align_block_t(const int32_t* ids, int S, int E, 
     counts[e] = run;
     sm.exp_off[e] = run;  // scanned below
   }
-  __syncthreads();
+  block_sync_lds();
 
   // exclusive scan over experts (E <= 256, 4 per lane of wave 0) and the
   // ascending active list
@@ -207,21 +219,24 @@ __device__ __forceinline__ void align_block_t(const int32_t* ids, int S, int E, 
       n_active[0] = nact;
     }
   }
-  __syncthreads();
+  block_sync_lds();
 
+  // (each output word written once: the active list is built in LDS first)
   for (int e = threadIdx.x; e < E; e += NT) {
     offsets[e] = sm.exp_off[e];
-    active[e] = -1;
+    sm.act_list[e] = -1;
   }
-  __syncthreads();
+  block_sync_lds();
   for (int e = threadIdx.x; e < E; e += NT)
-    if (sm.act_pos[e] >= 0) active[sm.act_pos[e]] = e;
+    if (sm.act_pos[e] >= 0) sm.act_list[sm.act_pos[e]] = e;
+  block_sync_lds();
+  for (int e = threadIdx.x; e < E; e += NT) active[e] = sm.act_list[e];
   for (int p = sm.exp_off[E] + threadIdx.x; p < S; p += NT) sorted_slots[p] = -1;
 
   // pass 2: stable placement; wave_cnt becomes the running count per wave
   for (int i = lane; i < E; i += kWave) sm.wave_cnt[wave][i] = 0;
   __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup");
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup", "local");
   auto place = [&](int c, int e) {
     const int s = c * kWave + lane;
     const bool valid = e >= 0 && e < E;
@@ -234,10 +249,10 @@ __device__ __forceinline__ void align_block_t(const int32_t* ids, int S, int E, 
     // the highest-ranked lane of each group advances its expert's counter
     const bool last = valid && (same >> lane) == 1ull;
     __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup");
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup", "local");
     if (last) sm.wave_cnt[wave][e] += rank + 1;
     __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup");
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup", "local");
   };
 #pragma unroll
   for (int j = 0; j < kCached; ++j)
@@ -262,25 +277,30 @@ __device__ __forceinline__ void align_block(const int32_t* ids, int S, int E, in
 // the number of experts ahead of it in (count descending, ID ascending)
 // order, and experts placed below M write themselves into the plan; then,
 // with `clear`, the row is zeroed. hist and row are LDS scratch of kMaxE.
-__device__ __forceinline__ void elb_block(int32_t* crow, int E, const int32_t* lid, int S, int M,
-                                          int32_t* plan_ids, int32_t* plan_counts, int clear,
-                                          int* hist, int* row) {
+// With PRE, `pre` (LDS) already holds the row as crow had it, read before
+// the block wrote anything (a load issued after stores waits for them).
+// `lid` is read only with `add` (so one pointer serves every layer).
+template <bool PRE = false>
+__device__ __forceinline__ void elb_block(int32_t* crow, int E, const int32_t* lid, bool add,
+                                          int S, int M, int32_t* plan_ids, int32_t* plan_counts,
+                                          int clear, int* hist, int* row,
+                                          const int* pre = nullptr) {
   const int nt = blockDim.x;
   for (int e = threadIdx.x; e < E; e += nt) hist[e] = 0;
-  __syncthreads();
-  if (lid != nullptr) {
+  block_sync_lds();
+  if (add) {
     for (int s = threadIdx.x; s < S; s += nt) {
       const int e = lid[s];
       if (e >= 0 && e < E) atomicAdd(&hist[e], 1);
     }
   }
-  __syncthreads();
+  block_sync_lds();
   for (int e = threadIdx.x; e < E; e += nt) {
-    const int v = crow[e] + hist[e];
+    const int v = (PRE ? pre[e] : crow[e]) + hist[e];
     row[e] = v;
     if (hist[e] != 0) crow[e] = v;
   }
-  __syncthreads();
+  block_sync_lds();
   if (M > 0) {
     // expert e's place counted by kParts consecutive lanes, each over a
     // share of the row, summed with shuffles within the lane group
@@ -347,13 +367,16 @@ smoe_status route_check(const void* x, const float* w_router, const float* logit
                         float* logits, const float* shared_gate_w, float* shared_gate,
                         RouteArgs& a);
 
-template <int NT>
+// (NLG: logits the block can stage, at least T * E, plus T for a staged
+// shared gate)
+template <int NT, int NLG = kFusedMaxLogits>
 struct alignas(16) RouteBlockSmem {
   AlignSmemT<NT> al;
   int ids[kFusedMaxSlots];
   int hist[kMaxE];
   int row[kMaxE];
-  float lg[kFusedMaxLogits];
+  int pre[kMaxE];                     // the layer's counter row, read first
+  float lg[NLG];
 };
 
 // One workgroup of NT threads, after the router logits: wave w takes the
@@ -363,8 +386,9 @@ struct alignas(16) RouteBlockSmem {
 // three separate kernels. With `staged`, the caller has already put the
 // T x E logits in sm.lg, followed by the T raw shared-gate dots (when the
 // layer has a gate), and the block reads neither from global memory.
-template <int NT>
-__device__ __forceinline__ void route_align_elb_block(const FusedArgs& f, RouteBlockSmem<NT>& sm,
+template <int NT, int NLG>
+__device__ __forceinline__ void route_align_elb_block(const FusedArgs& f,
+                                                      RouteBlockSmem<NT, NLG>& sm,
                                                       bool staged = false) {
   constexpr int kWaves = NT / kWave;
   const RouteArgs& a = f.r;
@@ -378,38 +402,49 @@ __device__ __forceinline__ void route_align_elb_block(const FusedArgs& f, RouteB
   uint64_t* keys = reinterpret_cast<uint64_t*>(&sm.al.wave_cnt[0][0]) + wave * kMaxE;
   int* sel = &sm.al.exp_off[0] + wave * kMaxK;
   // all logits in one round trip when they fit, then the top-k from LDS
+  // Global loads first (the logits unless staged, the layer's counter row):
+  // any load issued after a store waits for that store's round trip.
   const int n_lg = a.T * a.E;
-  const bool lg_in_lds = staged || n_lg <= kFusedMaxLogits;
-  if (lg_in_lds && !staged) {
+  const bool lg_in_lds = staged || n_lg <= NLG;
+  if (lg_in_lds && !staged)
     for (int i = threadIdx.x; i < n_lg; i += NT) sm.lg[i] = a.logits[i];
-    __syncthreads();
-  }
+  if (f.elb_counts != nullptr)
+    for (int e = threadIdx.x; e < a.E; e += NT)
+      sm.pre[e] = f.elb_counts[static_cast<size_t>(f.layer) * a.E + e];
+  block_sync_lds();
+  const bool want_gate = a.gate != nullptr && a.gate_w != nullptr;
   for (int t = wave; t < a.T; t += kWaves) {
     int id;
     float w;
-    const float* lrow = (lg_in_lds ? sm.lg : a.logits) + static_cast<size_t>(t) * a.E;
-    wave_topk(lrow, a.E, a.k, a.flags, keys, sel, &id, &w);
+    float raw = 0.0f;
+    if (want_gate && lane == 0) raw = staged ? sm.lg[n_lg + t] : a.gate[t];
+    // (two calls, so that each reads through its own address space)
+    if (lg_in_lds)
+      wave_topk(sm.lg + t * a.E, a.E, a.k, a.flags, keys, sel, &id, &w);
+    else
+      wave_topk(a.logits + static_cast<size_t>(t) * a.E, a.E, a.k, a.flags, keys, sel, &id, &w);
     if (lane < a.k) {
       a.ids[static_cast<size_t>(t) * a.k + lane] = id;
       a.wout[static_cast<size_t>(t) * a.k + lane] = w;
       sm.ids[t * a.k + lane] = id;
     }
-    if (a.gate != nullptr && a.gate_w != nullptr && lane == 0) {
-      const float raw = staged ? sm.lg[n_lg + t] : a.gate[t];
-      a.gate[t] = 1.0f / (1.0f + expf(-raw));
-    }
+    if (want_gate && lane == 0) a.gate[t] = 1.0f / (1.0f + expf(-raw));
   }
-  __syncthreads();
+  block_sync_lds();
   const int S = a.T * a.k;
   align_block_t<NT>(sm.ids, S, a.E, f.counts, f.offsets, f.sorted_slots, f.active, f.n_active,
                     sm.al);
   if (f.elb_counts == nullptr) return;
   for (int l = 0; l < f.L; ++l) {
-    __syncthreads();
-    elb_block(f.elb_counts + static_cast<size_t>(l) * a.E, a.E, l == f.layer ? sm.ids : nullptr,
-              S, f.M, f.plan_ids + static_cast<size_t>(l) * f.M,
-              f.plan_counts != nullptr ? f.plan_counts + static_cast<size_t>(l) * f.M : nullptr,
-              f.elb_clear, sm.hist, sm.row);
+    block_sync_lds();
+    int32_t* crow = f.elb_counts + static_cast<size_t>(l) * a.E;
+    int32_t* pid = f.plan_ids + static_cast<size_t>(l) * f.M;
+    int32_t* pc = f.plan_counts != nullptr ? f.plan_counts + static_cast<size_t>(l) * f.M : nullptr;
+    if (l == f.layer)
+      elb_block<true>(crow, a.E, sm.ids, true, S, f.M, pid, pc, f.elb_clear, sm.hist, sm.row,
+                      sm.pre);
+    else
+      elb_block(crow, a.E, sm.ids, false, S, f.M, pid, pc, f.elb_clear, sm.hist, sm.row);
   }
 }
 

@@ -3,8 +3,9 @@ with one token runs the router, top-k, alignment, ELB update, routed and
 shared experts and the combine in two launches of its own. Every output of
 the call is checked against the oracle (integers and logits bit for bit,
 floats within the layer tolerance), against the step-by-step calls on the
-same runner, and over repeated calls on one workspace (the call's counters
-and flag must be back at zero after each call). Needs an MI355X."""
+same runner, and over repeated calls on one workspace (the words the
+call's workgroups hand values over with must be back at zero after each
+call). Needs an MI355X."""
 
 import numpy as np
 import pytest
@@ -67,6 +68,7 @@ def outputs(d):
     out = {"logits": host(d.logits), "ids": host(d.topk_ids), "w": host(d.topk_w),
            "counts": host(d.counts), "offsets": host(d.offsets),
            "sorted_slots": host(d.sorted_slots), "n_active": host(d.n_active),
+           "active": host(d.active),
            "slot_out": host(d.slot_out), "y": host(d.y),
            "elb_counts": host(d.elb_counts), "plan_ids": host(d.plan_ids),
            "plan_counts": host(d.plan_counts)}
@@ -82,7 +84,7 @@ def check_against_oracle(got, L, ref):
     assert np.array_equal(got["logits"], ref["logits"])
     assert np.array_equal(got["ids"], ref["ids"])
     np.testing.assert_allclose(got["w"], ref["w"], rtol=W_RTOL, atol=1e-7)
-    for key in ("counts", "offsets", "sorted_slots"):
+    for key in ("counts", "offsets", "sorted_slots", "active"):
         assert np.array_equal(got[key], ref[key]), key
     assert int(got["n_active"][0]) == int(ref["n_active"])
     assert row_rel_err(got["slot_out"], ref["slot_out"]) <= ROW_TOL
@@ -122,8 +124,8 @@ def test_decode_layer_equals_step_calls(smoe, name):
     d.elb_counts.zero_()
     d.run()
     b = outputs(d)
-    for key in ("logits", "ids", "counts", "offsets", "sorted_slots", "n_active", "elb_counts",
-                "plan_ids", "plan_counts"):
+    for key in ("logits", "ids", "counts", "offsets", "sorted_slots", "active", "n_active",
+                "elb_counts", "plan_ids", "plan_counts"):
         assert np.array_equal(a[key], b[key]), key
     np.testing.assert_allclose(a["w"], b["w"], rtol=1e-6, atol=0)
     assert row_rel_err(a["slot_out"], b["slot_out"]) <= ROW_TOL
@@ -131,10 +133,10 @@ def test_decode_layer_equals_step_calls(smoe, name):
 
 
 def test_decode_layer_repeats_bit_for_bit(smoe):
-    # ten calls in a row on one workspace, eagerly and replayed from a HIP
-    # graph, with the step-by-step calls in between: every call finds its
-    # counters and flag at zero, and the sums have a fixed order, so every
-    # output is the same bit for bit
+    # calls in a row on one workspace, eagerly and replayed from a HIP graph,
+    # with the step-by-step calls in between: every call finds its hand-over
+    # words at zero, and the sums have a fixed order, so every output is the
+    # same bit for bit
     from quantized_speculative_expert_amd.layer import DeviceLayer
     L, ref = case("dsv2_t1")
     d = DeviceLayer(L, tiled=True, with_target=False)
@@ -184,3 +186,52 @@ def test_decode_layer_rows_layout_takes_step_calls(smoe):
     d = DeviceLayer(L, tiled=False, with_target=False)
     d.run(one_call=True)
     check_against_oracle(outputs(d), L, ref)
+
+
+@pytest.mark.parametrize("flags,elb_flags", [(0, 0), (1, 1)], ids=["plain", "renorm-clear"])
+def test_decode_layer_routing_outputs_multi_layer(smoe, flags, elb_flags):
+    # The one-call layer at T = 1 with the routing flags, a three-layer
+    # activation counter (this call's layer 1, random prior counts) and the
+    # clear flag: every routing output, the counter and every layer's plan
+    # equal those of smoe_route_align_elb from the same state, bit for bit
+    # (weights within float32 rounding of the same formula)
+    from quantized_speculative_expert_amd.layer import DeviceLayer
+    L, _ = case("g32_gate_skew")
+    d = DeviceLayer(L, tiled=True, with_target=False)
+    cfg = L.cfg
+    M = 4
+    rng = np.random.default_rng(11)
+    prior = torch.from_numpy(rng.integers(0, 3, (3, cfg.E)).astype(np.int32)).cuda()
+
+    def bufs():
+        return {"ids": torch.empty((1, cfg.k), dtype=torch.int32, device="cuda"),
+                "w": torch.empty((1, cfg.k), dtype=torch.float32, device="cuda"),
+                "lg": torch.empty((1, cfg.E), dtype=torch.float32, device="cuda"),
+                "gate": torch.empty(1, dtype=torch.float32, device="cuda"),
+                "counts": torch.empty(cfg.E, dtype=torch.int32, device="cuda"),
+                "offsets": torch.empty(cfg.E + 1, dtype=torch.int32, device="cuda"),
+                "sorted": torch.empty(cfg.k, dtype=torch.int32, device="cuda"),
+                "active": torch.empty(cfg.E, dtype=torch.int32, device="cuda"),
+                "nact": torch.empty(1, dtype=torch.int32, device="cuda"),
+                "elb": prior.clone(),
+                "pid": torch.full((3, M), -7, dtype=torch.int32, device="cuda"),
+                "pc": torch.full((3, M), -7, dtype=torch.int32, device="cuda")}
+
+    a, b = bufs(), bufs()
+    d._call("smoe_moe_layer_w4a16")(
+        d.x, d.w_router, d.router_bias, cfg.k, flags, a["ids"], a["w"], a["lg"],
+        d.shared_gate_w, a["gate"], a["counts"], a["offsets"], a["sorted"], a["active"],
+        a["nact"], a["elb"], 1, M, a["pid"], a["pc"], elb_flags, cfg.I, cfg.G, d.wg_q, d.wg_s,
+        d.wu_q, d.wu_s, d.wd_q, d.wd_s, d.workspace, d.slot_out, d.y,
+        shared=(d.sg16, d.su16, d.sd16), shared_out=d.shared_out)
+    smoe.smoe_route_align_elb(d.x, d.w_router, d.router_bias, cfg.k, flags, b["ids"], b["w"],
+                              b["lg"], d.shared_gate_w, b["gate"], b["counts"], b["offsets"],
+                              b["sorted"], b["active"], b["nact"], elb_counts=b["elb"], layer=1,
+                              M=M, plan_ids=b["pid"], plan_counts=b["pc"], elb_flags=elb_flags)
+    for key in a:
+        if key == "w":
+            np.testing.assert_allclose(host(a[key]), host(b[key]), rtol=1e-6, atol=0)
+        else:
+            assert np.array_equal(host(a[key]), host(b[key])), key
+    if elb_flags:
+        assert not host(a["elb"]).any()
