@@ -216,30 +216,25 @@ __global__ __launch_bounds__(kWThreads, 1) void wide_ffn_kernel(WArgs a) {
   };
   auto decode = [&](int item) __attribute__((always_inline)) {
     It it;
-    // Within an expert the items go tile by tile, and within a tile chunk
-    // by chunk: consecutive items of a workgroup's range then read the same
-    // weight rows, which the second time come from the caches.
     if (item < n1) {
-      const int t = item / n1c;
+      const int c = item / tiles1;
       it.grp = 1;
       it.e = 0;
-      it.tile = t;
-      it.seg0 = (item - t * n1c) * ch1;
+      it.tile = item - c * tiles1;
+      it.seg0 = c * ch1;
       it.m = min(ch1, a.T - it.seg0);
     } else {
       const int ri = item - static_cast<int>(n1);
-      int lo_e = 0, hi_e = E;  // s_cp[lo_e] * tiles0 <= ri < s_cp[hi_e] * tiles0
+      const int rc = ri / tiles0;
+      it.grp = 0;
+      it.tile = ri - rc * tiles0;
+      int lo_e = 0, hi_e = E;  // s_cp[lo_e] <= rc < s_cp[hi_e]
       while (hi_e - lo_e > 1) {
         const int mid = (lo_e + hi_e) >> 1;
-        if (s_cp[mid] * tiles0 <= ri) lo_e = mid; else hi_e = mid;
+        if (s_cp[mid] <= rc) lo_e = mid; else hi_e = mid;
       }
-      const int ce = s_cp[lo_e + 1] - s_cp[lo_e];  // chunks of the expert (>= 1 here)
-      const int local = ri - s_cp[lo_e] * tiles0;
-      const int t = local / ce;
-      it.grp = 0;
       it.e = lo_e;
-      it.tile = t;
-      it.seg0 = s_off[lo_e] + (local - t * ce) * ch0;
+      it.seg0 = s_off[lo_e] + (rc - s_cp[lo_e]) * ch0;
       it.m = min(ch0, s_off[lo_e + 1] - it.seg0);
     }
     it.grp = uniform(it.grp);
@@ -600,8 +595,7 @@ smoe_status wide_ffn(const WideCall& c, hipStream_t st, const char* who) {
   // shared expert, which carries every token, in launches of its own with
   // chunks of 128 tokens (8 column groups), so that its weights stream half
   // as often. Two phase buffers of a chunk's rows fit the LDS either way.
-  constexpr int kRoutedNC = 4;
-  constexpr int kSharedNC = 8;
+  constexpr int kRoutedNC = 4, kSharedNC = 8;
   auto base = [&](WArgs& a, int nc) {
     a = WArgs{};
     a.sorted_slots = c.sorted_slots;
@@ -688,11 +682,9 @@ smoe_status wide_ffn(const WideCall& c, hipStream_t st, const char* who) {
     }
   };
   smoe_status r = routed(1);
-  if (r == SMOE_OK && shared)
-    r = launch_wide<kFp16, 128, 1, kSharedNC>(s1, items_s1, st, who);
+  if (r == SMOE_OK && shared) r = launch_wide<kFp16, 128, 1, kSharedNC>(s1, items_s1, st, who);
   if (r == SMOE_OK) r = routed(2);
-  if (r == SMOE_OK && shared)
-    r = launch_wide<kFp16, 128, 2, kSharedNC>(s2, items_s2, st, who);
+  if (r == SMOE_OK && shared) r = launch_wide<kFp16, 128, 2, kSharedNC>(s2, items_s2, st, who);
   return r;
 }
 
