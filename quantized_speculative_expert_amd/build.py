@@ -7,6 +7,7 @@ Every call recompiles all sources.
 from __future__ import annotations
 
 import os
+import re
 import shutil
 import subprocess
 import sys
@@ -44,6 +45,21 @@ def sources():
     return sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith(".hip"))
 
 
+def scratch_users(remarks: str):
+    """(kernel, bytes per lane) of every kernel the compiler's resource
+    remarks show with scratch memory."""
+    out, name = [], None
+    for line in remarks.splitlines():
+        m = re.search(r"remark: Function Name: (\S+)", line)
+        if m:
+            name = m.group(1)
+            continue
+        m = re.search(r"remark:\s+ScratchSize \[bytes/lane\]: (\d+)", line)
+        if m and name is not None and int(m.group(1)) > 0:
+            out.append((name, int(m.group(1))))
+    return out
+
+
 def build(verbose: bool = False, extra_flags=None) -> str:
     """Compile every HIP source and link libsmoe.so; returns the library path."""
     hipcc = _hipcc()
@@ -52,13 +68,18 @@ def build(verbose: bool = False, extra_flags=None) -> str:
 
     def compile_one(src: str) -> str:
         obj = os.path.join(BUILD_DIR, os.path.basename(src) + ".o")
-        cmd = [hipcc, *flags, "-c", src, "-o", obj]
+        # the resource-usage remarks name every kernel's scratch use
+        cmd = [hipcc, *flags, "-Rpass-analysis=kernel-resource-usage", "-c", src, "-o", obj]
         r = subprocess.run(cmd, capture_output=True, text=True)
         if r.returncode != 0:
             raise RuntimeError(f"hipcc failed for {src}:\n{r.stdout}\n{r.stderr}")
+        spills = scratch_users(r.stderr)
+        if spills:
+            raise RuntimeError(f"{os.path.basename(src)}: kernels use scratch memory (register "
+                               "spills): " + ", ".join(f"{k} ({b} B/lane)" for k, b in spills))
         if verbose:
             out = "\n".join(l for l in (r.stdout + r.stderr).splitlines()
-                            if "packed-fp32-ops" not in l)
+                            if "packed-fp32-ops" not in l and "remark:" not in l)
             if out.strip():
                 print(out)
         return obj
