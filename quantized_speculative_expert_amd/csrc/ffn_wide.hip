@@ -53,7 +53,7 @@ constexpr int kWStageNB = 16;                 // staging loads in flight per lan
 #define SMOE_WIDE_RING 4
 #endif
 constexpr int kWRing = SMOE_WIDE_RING;        // weight blocks in flight per streamer
-constexpr int kWTabInts = 2 * (kMaxE + 4) + kWideMaxSlots;
+constexpr int kWTabInts = 2 * (kMaxE + 4) + kWideMaxSlots + 4;  // + the step counters
 constexpr int kWTabBytes = (kWTabInts * 4 + 15) / 16 * 16;
 // Positions per chunk: 64 for the routed experts (4 MFMA column groups,
 // k-phases of 512). The FP16 shared gate/up take 128 tokens (8 column
@@ -104,12 +104,30 @@ __device__ __forceinline__ ConstWArgs* wkargs() {
 }
 
 // Workgroup barrier that orders LDS only: every barrier here hands over LDS
-// data (tables, staged rows); a full fence would wait for the weight loads
-// in flight too.
+// data (tables); a full fence would wait for the weight loads in flight too.
 __device__ __forceinline__ void lds_barrier() {
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
   __builtin_amdgcn_s_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+// The staged steps are handed over with counters in LDS instead of
+// barriers: a staging wave adds one to ready[b] when its rows of a step are
+// in buffer b, a streamer adds one to done[b] when it has read its last
+// block of a step from buffer b. Each side waits only for what it needs,
+// so the twelve waves do not meet at every step. A wait gives up after
+// about 0.1 s (it cannot be reached unless a wave of the workgroup died).
+constexpr int kStepSpin = 1 << 22;
+__device__ __forceinline__ void step_wait(int* ctr, int target) {
+  for (int i = 0; i < kStepSpin &&
+                  __hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) < target;
+       ++i)
+    __builtin_amdgcn_s_sleep(1);
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+__device__ __forceinline__ void step_signal(int* ctr, int lane) {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");  // this wave's LDS accesses done
+  if (lane == 0) __hip_atomic_fetch_add(ctr, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
 }
 
 template <typename P>
@@ -139,12 +157,17 @@ struct WCtx {
   const int* s_off;         // expert offsets, clamped to [0, S]
   const int* s_cp;          // routed chunks before each expert
   const int* s_slots;       // stage 1: token of each position; stage 2: its slot
+  int* ready;               // [2] staging waves' step counters per buffer
+  int* done;                // [2] streamers' step counters per buffer
   int n1;                   // shared items (they come first)
   int E, T;
   int wave, lane;
 };
 
-__device__ __forceinline__ It decode_item(const WCtx& c, int item) {
+// `eh` is the caller's expert hint: -1 (a binary search), or an expert at
+// or before the item's (the items of a range come in expert order, so the
+// scan from the previous item's expert ends after a step or two).
+__device__ __forceinline__ It decode_item(const WCtx& c, int item, int& eh) {
   ConstWArgs* ka = wkargs();
   It it;
   if (item < c.n1) {
@@ -161,11 +184,18 @@ __device__ __forceinline__ It decode_item(const WCtx& c, int item) {
     const int rc = ri / tiles0;
     it.grp = 0;
     it.tile = ri - rc * tiles0;
-    int lo_e = 0, hi_e = c.E;  // s_cp[lo_e] <= rc < s_cp[hi_e]
-    while (hi_e - lo_e > 1) {
-      const int mid = (lo_e + hi_e) >> 1;
-      if (c.s_cp[mid] <= rc) lo_e = mid; else hi_e = mid;
+    int e = eh;  // the expert with s_cp[e] <= rc < s_cp[e + 1]
+    if (e < 0) {
+      int hi_e = c.E;
+      e = 0;
+      while (hi_e - e > 1) {
+        const int mid = (e + hi_e) >> 1;
+        if (c.s_cp[mid] <= rc) e = mid; else hi_e = mid;
+      }
     }
+    while (e + 1 < c.E && uniform(c.s_cp[e + 1]) <= rc) ++e;
+    eh = e;
+    const int lo_e = e;
     it.e = lo_e;
     it.seg0 = c.s_off[lo_e] + (rc - c.s_cp[lo_e]) * ch0;
     it.m = min(ch0, c.s_off[lo_e + 1] - it.seg0);
@@ -184,7 +214,7 @@ __device__ __forceinline__ int phases_of(int grp) {
 }
 
 // The staging waves: every (item, phase) of [lo, hi) in order, into the
-// buffer of its step's parity, one LDS barrier per step. Lane c of a
+// buffer of its step's parity. Lane c of a
 // staging wave copies the 16-byte piece c of every fourth row (a row of a
 // phase is at most 64 pieces), so a piece costs an add for its address and
 // a row's token is looked up once.
@@ -221,12 +251,12 @@ __device__ __forceinline__ void staging_loop(const WCtx& c, int lo, int hi) {
     }
   };
   int step = 0;
-  It it = decode_item(c, lo);
+  int eh = -1;
+  It it = decode_item(c, lo, eh);
   int p = 0;
   stage(it, 0, 0);
-  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the rows are in LDS
+  step_signal(c.ready, lane);
   for (int item = lo;;) {
-    lds_barrier();  // B_step: step staged, the buffer of step - 1 is free
     // the next step: next phase of this item, or the next item's first
     int nitem = item, np = p + 1;
     if (np >= phases_of(it.grp)) {
@@ -234,9 +264,11 @@ __device__ __forceinline__ void staging_loop(const WCtx& c, int lo, int hi) {
       np = 0;
     }
     if (nitem >= hi) break;
-    const It nit = nitem == item ? it : decode_item(c, nitem);
-    stage(nit, np, (step + 1) & 1);
-    __builtin_amdgcn_s_waitcnt(0x0F70);
+    const It nit = nitem == item ? it : decode_item(c, nitem, eh);
+    const int s1 = step + 1, b = s1 & 1;
+    if (s1 >= 2) step_wait(c.done + b, kWW * (s1 >> 1));  // steps s1 - 2, s1 - 4, ... read
+    stage(nit, np, b);
+    step_signal(c.ready + b, lane);
     item = nitem;
     p = np;
     it = nit;
@@ -281,8 +313,9 @@ __device__ __forceinline__ void stream_pass(const WCtx& c, int lo, int hi, int& 
     const uint8_t* w[NMAT];   // each stream's first block of the item
     const uint16_t* s[NMAT];  // and its first scales (INT4)
   };
+  int eh_load = -1, eh_comp = -1;  // expert hints of the two cursors
   auto settle = [&](Cur& cu) __attribute__((always_inline)) {  // at the start of item cu.item (< hi)
-    const It it = decode_item(c, cu.item);
+    const It it = decode_item(c, cu.item, eh_load);
 #pragma unroll
     for (int m = 0; m < NMAT; ++m) {
       // (slabs past N: loaded, never stored)
@@ -357,17 +390,20 @@ __device__ __forceinline__ void stream_pass(const WCtx& c, int lo, int hi, int& 
   // between the MFMAs, the g32 kernels gave wrong rows at a ring depth of
   // four blocks, and without the branches they do not.
   // The INT4 path sits behind a run-time test that always holds, and its
-  // column groups and blocks behind scheduling barriers: without them the
-  // compiler interleaves the dequantisation of consecutive blocks and the
-  // INT4 passes spill.
+  // column groups behind scheduling barriers: without them the compiler
+  // interleaves the dequantisation of consecutive blocks and the INT4
+  // passes spill.
   const bool int4_rt = ka->g[GRP].bpp > 0;
   auto compute = [&](const Entry& en, int kk) __attribute__((always_inline)) {
+    // The activation fragments of column group cg + 1 are read from LDS
+    // before the MFMAs of cg, so that the LDS latency hides behind them.
     if (FMT == kInt4 && int4_rt) {
+      f16x8 B[NMAT][4];
+      float sc[NMAT][NQ];
 #pragma unroll
       for (int m = 0; m < NMAT; ++m) {
-        f16x8 B[4];
 #pragma unroll
-        for (int q = 0; q < 4; ++q) B[q] = dequant_word(en.v[m][q], dq_lo, dq_hi, dq_magic);
+        for (int q = 0; q < 4; ++q) B[m][q] = dequant_word(en.v[m][q], dq_lo, dq_hi, dq_magic);
 #pragma unroll
         for (int gq = 0; gq < NQ; ++gq) {
           uint16_t sbits;
@@ -377,29 +413,45 @@ __device__ __forceinline__ void stream_pass(const WCtx& c, int lo, int hi, int& 
             const uint32_t word = en.s[m][NQ == 4 ? (gq >> 1) : 0];
             sbits = static_cast<uint16_t>((gq & 1) ? (word >> 16) : word);
           }
-          const float sc = static_cast<float>(bitcast<_Float16>(sbits));
+          sc[m][gq] = static_cast<float>(bitcast<_Float16>(sbits));
+        }
+      }
+      f16x8 A[2][4];
+      auto read_a = [&](int cg) __attribute__((always_inline)) {
 #pragma unroll
-          for (int cg = 0; cg < NC; ++cg) {
+        for (int q = 0; q < 4; ++q)
+          A[cg & 1][q] = lds16(arow[cg] + 2 * (kk + 8 * int4_word(G, g, q)));
+      };
+      read_a(0);
+#pragma unroll
+      for (int cg = 0; cg < NC; ++cg) {
+        if (cg + 1 < NC) read_a(cg + 1);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int gq = 0; gq < NQ; ++gq) {
+#pragma unroll
+          for (int m = 0; m < NMAT; ++m) {
             f32x4 t = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
             for (int qq = 0; qq < PER; ++qq) {
               const int q = gq * PER + qq;
-              const f16x8 A = lds16(arow[cg] + 2 * (kk + 8 * int4_word(G, g, q)));
-              t = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, B[q], t, 0, 0, 0);
+              t = __builtin_amdgcn_mfma_f32_16x16x32_f16(A[cg & 1][q], B[m][q], t, 0, 0, 0);
             }
-            acc[m][cg] += sc * t;
-            __builtin_amdgcn_sched_barrier(0);
+            acc[m][cg] += sc[m][gq] * t;
           }
         }
+        __builtin_amdgcn_sched_barrier(0);
       }
-      __builtin_amdgcn_sched_barrier(0);
     } else {
+      f16x8 A[2];
+      A[0] = lds16(arow[0] + 2 * (kk + 8 * g));
 #pragma unroll
       for (int cg = 0; cg < NC; ++cg) {
-        const f16x8 A = lds16(arow[cg] + 2 * (kk + 8 * g));
+        if (cg + 1 < NC) A[(cg + 1) & 1] = lds16(arow[cg + 1] + 2 * (kk + 8 * g));
+        if (NC > 4) __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int m = 0; m < NMAT; ++m)
-          acc[m][cg] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, bitcast<f16x8>(en.v[m]),
+          acc[m][cg] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A[cg & 1], bitcast<f16x8>(en.v[m]),
                                                               acc[m][cg], 0, 0, 0);
         if (NC > 4) __builtin_amdgcn_sched_barrier(0);
       }
@@ -444,10 +496,11 @@ __device__ __forceinline__ void stream_pass(const WCtx& c, int lo, int hi, int& 
   auto begin_step = [&](const Cur& cu) __attribute__((always_inline)) {
     if (cu.blk == 0) {
       if (cu.item != lo) item_end();
-      cit = decode_item(c, cu.item);
+      cit = decode_item(c, cu.item, eh_comp);
       cur_m = cit.m;
     }
-    lds_barrier();
+    if (step > 0) step_signal(c.done + ((step - 1) & 1), lane);  // step - 1 read
+    step_wait(c.ready + (step & 1), kWS * ((step >> 1) + 1));
     set_rows(step & 1);
     ++step;
   };
@@ -490,6 +543,7 @@ __global__ __launch_bounds__(kWThreads, 1) void wide_ffn_kernel(WArgs a) {
   int* s_off = reinterpret_cast<int*>(smem);
   int* s_cp = s_off + kMaxE + 4;
   int* s_slots = s_off + 2 * (kMaxE + 4);
+  int* s_steps = s_slots + kWideMaxSlots;  // ready[2], done[2]
   uint8_t* bufs = smem + kWTabBytes;
 
   const int tid = threadIdx.x;
@@ -501,6 +555,7 @@ __global__ __launch_bounds__(kWThreads, 1) void wide_ffn_kernel(WArgs a) {
 
   // ---- tables: offsets (clamped to [0, S]), positions' tokens or slots,
   // routed chunk prefix
+  if (tid < 4) s_steps[tid] = 0;
   for (int i = tid; i <= E; i += kWThreads) s_off[i] = min(max(a.offsets[i], 0), a.S);
   for (int i = tid; i < a.S; i += kWThreads)
     s_slots[i] = STAGE == 1 ? a.sorted_slots[i] / a.k : a.sorted_slots[i];
@@ -597,6 +652,8 @@ __global__ __launch_bounds__(kWThreads, 1) void wide_ffn_kernel(WArgs a) {
   ctx.s_off = s_off;
   ctx.s_cp = s_cp;
   ctx.s_slots = s_slots;
+  ctx.ready = s_steps;
+  ctx.done = s_steps + 2;
   ctx.n1 = static_cast<int>(n1);
   ctx.E = E;
   ctx.T = a.T;
