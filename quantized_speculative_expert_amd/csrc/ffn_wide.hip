@@ -308,10 +308,10 @@ __device__ __forceinline__ void stream_pass(const WCtx& c, int lo, int hi, int& 
   auto slab_of = [&](int tile, int m) __attribute__((always_inline)) {
     return STAGE == 1 ? tile * kWW + wave : (tile * SL + m) * kWW + wave;
   };
-  struct Cur {  // a position in the wave's block sequence (wave-uniform)
+  struct Cur {  // the load cursor: a position in the wave's block sequence (wave-uniform)
     int item, blk;
-    const uint8_t* w[NMAT];   // each stream's first block of the item
-    const uint16_t* s[NMAT];  // and its first scales (INT4)
+    const uint8_t* w[NMAT];   // each stream's current block
+    const uint16_t* s[NMAT];  // and its scales (INT4)
   };
   int eh_load = -1, eh_comp = -1;  // expert hints of the two cursors
   auto settle = [&](Cur& cu) __attribute__((always_inline)) {  // at the start of item cu.item (< hi)
@@ -337,13 +337,14 @@ __device__ __forceinline__ void stream_pass(const WCtx& c, int lo, int hi, int& 
   // Every ring slot takes a load on every pass, also past the end of the
   // range (the last block again), so that the compiler waits only for the
   // oldest block.
+  const uint32_t lane16 = 16 * lane;   // this lane's bytes of a block
+  const uint32_t srow = r16 * NQ;      // and its row's scales
   auto load = [&](Entry& en, const Cur& cu) __attribute__((always_inline)) {
-    const long long tb = min(cu.blk, nblk - 1);
 #pragma unroll
     for (int m = 0; m < NMAT; ++m) {
-      en.v[m] = gload<u32x4>(cu.w[m] + tb * 1024 + 16 * lane);
+      en.v[m] = gload<u32x4>(cu.w[m] + lane16);
       if (FMT == kInt4) {
-        const uint16_t* sp = cu.s[m] + (tb * 16 + r16) * NQ;
+        const uint16_t* sp = cu.s[m] + srow;
         if (NQ == 1) {
           en.s16[m] = gload<uint16_t>(sp);
         } else if (NQ == 2) {
@@ -356,8 +357,17 @@ __device__ __forceinline__ void stream_pass(const WCtx& c, int lo, int hi, int& 
       }
     }
   };
+  // the next block; past the end of the range the cursor stays on the last
+  // block (it is loaded again, never computed)
   auto advance = [&](Cur& cu) __attribute__((always_inline)) {
-    if (++cu.blk >= nblk && cu.item < hi) {
+    if (cu.blk + 1 < nblk) {
+      ++cu.blk;
+#pragma unroll
+      for (int m = 0; m < NMAT; ++m) {
+        cu.w[m] += 1024;
+        if (FMT == kInt4) cu.s[m] += 16 * NQ;
+      }
+    } else if (cu.item < hi) {
       ++cu.item;
       if (cu.item < hi) settle(cu);
     }
@@ -493,10 +503,12 @@ __device__ __forceinline__ void stream_pass(const WCtx& c, int lo, int hi, int& 
       for (int cg = 0; cg < NC; ++cg) acc[m][cg] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
   };
   // before the first block of a step: the step's barrier and A rows
-  auto begin_step = [&](const Cur& cu) __attribute__((always_inline)) {
-    if (cu.blk == 0) {
-      if (cu.item != lo) item_end();
-      cit = decode_item(c, cu.item, eh_comp);
+  // the compute cursor: item, block and block within the phase
+  int c_item = lo, c_blk = 0, c_bip = 0;
+  auto begin_step = [&]() __attribute__((always_inline)) {
+    if (c_blk == 0) {
+      if (c_item != lo) item_end();
+      cit = decode_item(c, c_item, eh_comp);
       cur_m = cit.m;
     }
     if (step > 0) step_signal(c.done + ((step - 1) & 1), lane);  // step - 1 read
@@ -506,10 +518,18 @@ __device__ __forceinline__ void stream_pass(const WCtx& c, int lo, int hi, int& 
   };
 
   int left = (hi - lo) * nblk;  // blocks of the range (the wave streams every block of its slab)
+  auto advance_comp = [&]() __attribute__((always_inline)) {
+    if (++c_blk == nblk) {
+      c_blk = 0;
+      c_bip = 0;
+      ++c_item;
+    } else if (++c_bip == bpp) {
+      c_bip = 0;
+    }
+  };
   Cur L;
   L.item = lo;
   settle(L);
-  Cur Cc = L;
   static_for<0, R>([&](auto rc) {
     load(ring[decltype(rc)::value], L);
     advance(L);
@@ -518,20 +538,20 @@ __device__ __forceinline__ void stream_pass(const WCtx& c, int lo, int hi, int& 
   while (left >= R) {
 #pragma clang loop unroll(full)
     for (int r = 0; r < R; ++r) {
-      if (Cc.blk % bpp == 0) begin_step(Cc);
-      compute(ring[r], (Cc.blk % bpp) * kBlkK);
+      if (c_bip == 0) begin_step();
+      compute(ring[r], c_bip * kBlkK);
       load(ring[r], L);
       advance(L);
-      advance(Cc);
+      advance_comp();
     }
     left -= R;
   }
 #pragma clang loop unroll(full)
   for (int r = 0; r < R; ++r) {
     if (r < left) {
-      if (Cc.blk % bpp == 0) begin_step(Cc);
-      compute(ring[r], (Cc.blk % bpp) * kBlkK);
-      advance(Cc);
+      if (c_bip == 0) begin_step();
+      compute(ring[r], c_bip * kBlkK);
+      advance_comp();
     }
   }
   item_end();
