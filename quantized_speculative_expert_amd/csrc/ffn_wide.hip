@@ -53,7 +53,8 @@ constexpr int kWStageNB = 16;                 // staging loads in flight per lan
 #define SMOE_WIDE_RING 4
 #endif
 constexpr int kWRing = SMOE_WIDE_RING;        // weight blocks in flight per streamer
-constexpr int kWTabInts = 2 * (kMaxE + 4) + kWideMaxSlots + 4;  // + the step counters
+constexpr int kWItems = 64;                   // items of a range in the LDS table
+constexpr int kWTabInts = 2 * (kMaxE + 4) + kWideMaxSlots + 4 + 4 * kWItems;  // + step counters, items
 constexpr int kWTabBytes = (kWTabInts * 4 + 15) / 16 * 16;
 // Positions per chunk: 64 for the routed experts (4 MFMA column groups,
 // k-phases of 512). The FP16 shared gate/up take 128 tokens (8 column
@@ -159,15 +160,17 @@ struct WCtx {
   const int* s_slots;       // stage 1: token of each position; stage 2: its slot
   int* ready;               // [2] staging waves' step counters per buffer
   int* done;                // [2] streamers' step counters per buffer
+  const i32x4* items;       // the first nt items of the workgroup's range
+  int lo, nt;
+  int ph0, ph1;             // staged steps per item of each group
   int n1;                   // shared items (they come first)
   int E, T;
   int wave, lane;
 };
 
-// `eh` is the caller's expert hint: -1 (a binary search), or an expert at
-// or before the item's (the items of a range come in expert order, so the
-// scan from the previous item's expert ends after a step or two).
-__device__ __forceinline__ It decode_item(const WCtx& c, int item, int& eh) {
+// The item's fields, decoded by one lane on its own (a binary search over
+// the routed chunk prefix).
+__device__ __forceinline__ It decode_item(const WCtx& c, int item) {
   ConstWArgs* ka = wkargs();
   It it;
   if (item < c.n1) {
@@ -184,21 +187,31 @@ __device__ __forceinline__ It decode_item(const WCtx& c, int item, int& eh) {
     const int rc = ri / tiles0;
     it.grp = 0;
     it.tile = ri - rc * tiles0;
-    int e = eh;  // the expert with s_cp[e] <= rc < s_cp[e + 1]
-    if (e < 0) {
-      int hi_e = c.E;
-      e = 0;
-      while (hi_e - e > 1) {
-        const int mid = (e + hi_e) >> 1;
-        if (c.s_cp[mid] <= rc) e = mid; else hi_e = mid;
-      }
+    int e = 0, hi_e = c.E;  // s_cp[e] <= rc < s_cp[hi_e]
+    while (hi_e - e > 1) {
+      const int mid = (e + hi_e) >> 1;
+      if (c.s_cp[mid] <= rc) e = mid; else hi_e = mid;
     }
-    while (e + 1 < c.E && uniform(c.s_cp[e + 1]) <= rc) ++e;
-    eh = e;
-    const int lo_e = e;
-    it.e = lo_e;
-    it.seg0 = c.s_off[lo_e] + (rc - c.s_cp[lo_e]) * ch0;
-    it.m = min(ch0, c.s_off[lo_e + 1] - it.seg0);
+    it.e = e;
+    it.seg0 = c.s_off[e] + (rc - c.s_cp[e]) * ch0;
+    it.m = min(ch0, c.s_off[e + 1] - it.seg0);
+  }
+  return it;
+}
+
+// The item's fields for the whole wave: from the workgroup's table of its
+// items (filled once, in parallel), past the table's end decoded here.
+__device__ __forceinline__ It item_at(const WCtx& c, int item) {
+  It it;
+  if (item - c.lo < c.nt) {
+    const i32x4 v = c.items[item - c.lo];
+    it.grp = v[0] >> 16;
+    it.e = v[0] & 0xFFFF;
+    it.seg0 = v[1];
+    it.m = v[2];
+    it.tile = v[3];
+  } else {
+    it = decode_item(c, item);
   }
   it.grp = uniform(it.grp);
   it.e = uniform(it.e);
@@ -208,10 +221,6 @@ __device__ __forceinline__ It decode_item(const WCtx& c, int item, int& eh) {
   return it;
 }
 
-__device__ __forceinline__ int phases_of(int grp) {
-  ConstWArgs* ka = wkargs();
-  return (ka->g[grp].nblk + ka->g[grp].bpp - 1) / ka->g[grp].bpp;
-}
 
 // The staging waves: every (item, phase) of [lo, hi) in order, into the
 // buffer of its step's parity. Lane c of a
@@ -223,17 +232,24 @@ __device__ __forceinline__ void staging_loop(const WCtx& c, int lo, int hi) {
   ConstWArgs* ka = wkargs();
   const int ws = c.wave - kWW;
   const int lane = c.lane;
-  const int buf_bytes = ka->buf_bytes;
+  // the launch's values, read once into scalar registers
+  const int buf_bytes = uniform(ka->buf_bytes);
+  const int K0 = uniform(ka->g[0].K), K1 = uniform(ka->g[1].K);
+  const int kph0 = uniform(ka->g[0].kph), kph1 = uniform(ka->g[1].kph);
+  const int rs0 = uniform(ka->g[0].rstride), rs1 = uniform(ka->g[1].rstride);
+  const uint16_t* const a0 = uniform_ptr(ka->g[0].a);
+  const uint16_t* const a1 = uniform_ptr(ka->g[1].a);
+  const int S = uniform(ka->S);
   auto stage = [&](const It& it, int p, int buf) __attribute__((always_inline)) {
-    const int K = ka->g[it.grp].K;
-    const int kph = ka->g[it.grp].kph;
-    const int rstride = ka->g[it.grp].rstride;
+    const int K = it.grp ? K1 : K0;
+    const int kph = it.grp ? kph1 : kph0;
+    const int rstride = it.grp ? rs1 : rs0;
     const int k0 = p * kph;
     const int npr = min(kph, K - k0) / 8;  // 16-byte pieces per row
-    const uint16_t* src = uniform_ptr(ka->g[it.grp].a) + k0 + 8 * min(lane, npr - 1);
+    const uint16_t* src = (it.grp ? a1 : a0) + k0 + 8 * min(lane, npr - 1);
     uint8_t* dst0 = c.bufs + buf * buf_bytes + 16 * lane;
     const bool on = lane < npr;
-    const int rows = STAGE == 1 ? c.T : (it.grp ? c.T : ka->S);  // rows of the source
+    const int rows = STAGE == 1 ? c.T : (it.grp ? c.T : S);  // rows of the source
     for (int r0 = ws; r0 < it.m; r0 += kWS * kWStageNB) {
       u32x4 v[kWStageNB];
       static_for<0, kWStageNB>([&](auto jc) {
@@ -251,20 +267,19 @@ __device__ __forceinline__ void staging_loop(const WCtx& c, int lo, int hi) {
     }
   };
   int step = 0;
-  int eh = -1;
-  It it = decode_item(c, lo, eh);
+  It it = item_at(c, lo);
   int p = 0;
   stage(it, 0, 0);
   step_signal(c.ready, lane);
   for (int item = lo;;) {
     // the next step: next phase of this item, or the next item's first
     int nitem = item, np = p + 1;
-    if (np >= phases_of(it.grp)) {
+    if (np >= (it.grp ? c.ph1 : c.ph0)) {
       ++nitem;
       np = 0;
     }
     if (nitem >= hi) break;
-    const It nit = nitem == item ? it : decode_item(c, nitem, eh);
+    const It nit = nitem == item ? it : item_at(c, nitem);
     const int s1 = step + 1, b = s1 & 1;
     if (s1 >= 2) step_wait(c.done + b, kWW * (s1 >> 1));  // steps s1 - 2, s1 - 4, ... read
     stage(nit, np, b);
@@ -298,12 +313,19 @@ __device__ __forceinline__ void stream_pass(const WCtx& c, int lo, int hi, int& 
   asm volatile("" : "+v"(lane));
   const int g = lane >> 4;
   const int r16 = lane & 15;
-  const int nblk = ka->g[GRP].nblk, bpp = ka->g[GRP].bpp;
-  const int slabs = ka->g[GRP].slabs;
-  const int rstride = ka->g[GRP].rstride;
-  const int buf_bytes = ka->buf_bytes;
+  // the launch's values, read once into scalar registers (the compiler
+  // would otherwise load them from the argument segment again inside the
+  // loop, each load a wait on the scalar and LDS counters)
+  const int nblk = uniform(ka->g[GRP].nblk), bpp = uniform(ka->g[GRP].bpp);
+  const int slabs = uniform(ka->g[GRP].slabs);
+  const int rstride = uniform(ka->g[GRP].rstride);
+  const int buf_bytes = uniform(ka->buf_bytes);
+  const int H = uniform(ka->H), S = uniform(ka->S);
   const long long west = ka->g[GRP].w_estride;
   const long long sest = ka->g[GRP].s_estride;
+  const uint8_t* const wbase[2] = {uniform_ptr(ka->g[GRP].w[0]), uniform_ptr(ka->g[GRP].w[1])};
+  const uint16_t* const sbase[2] = {uniform_ptr(ka->g[GRP].s[0]), uniform_ptr(ka->g[GRP].s[1])};
+  void* const out = uniform_ptr(ka->g[GRP].out);
 
   auto slab_of = [&](int tile, int m) __attribute__((always_inline)) {
     return STAGE == 1 ? tile * kWW + wave : (tile * SL + m) * kWW + wave;
@@ -313,16 +335,15 @@ __device__ __forceinline__ void stream_pass(const WCtx& c, int lo, int hi, int& 
     const uint8_t* w[NMAT];   // each stream's current block
     const uint16_t* s[NMAT];  // and its scales (INT4)
   };
-  int eh_load = -1, eh_comp = -1;  // expert hints of the two cursors
   auto settle = [&](Cur& cu) __attribute__((always_inline)) {  // at the start of item cu.item (< hi)
-    const It it = decode_item(c, cu.item, eh_load);
+    const It it = item_at(c, cu.item);
 #pragma unroll
     for (int m = 0; m < NMAT; ++m) {
       // (slabs past N: loaded, never stored)
       const long long tb0 = static_cast<long long>(min(slab_of(it.tile, m), slabs - 1)) * nblk;
       const int mat = STAGE == 1 ? m : 0;
-      cu.w[m] = ka->g[GRP].w[mat] + it.e * west + tb0 * 1024;
-      if (FMT == kInt4) cu.s[m] = ka->g[GRP].s[mat] + it.e * sest + tb0 * 16 * NQ;
+      cu.w[m] = wbase[mat] + it.e * west + tb0 * 1024;
+      if (FMT == kInt4) cu.s[m] = sbase[mat] + it.e * sest + tb0 * 16 * NQ;
     }
     cu.blk = 0;
   };
@@ -403,7 +424,7 @@ __device__ __forceinline__ void stream_pass(const WCtx& c, int lo, int hi, int& 
   // column groups behind scheduling barriers: without them the compiler
   // interleaves the dequantisation of consecutive blocks and the INT4
   // passes spill.
-  const bool int4_rt = ka->g[GRP].bpp > 0;
+  const bool int4_rt = bpp > 0;
   auto compute = [&](const Entry& en, int kk) __attribute__((always_inline)) {
     // The activation fragments of column group cg + 1 are read from LDS
     // before the MFMAs of cg, so that the LDS latency hides behind them.
@@ -469,7 +490,6 @@ __device__ __forceinline__ void stream_pass(const WCtx& c, int lo, int hi, int& 
   };
   // outputs of the finished item cit, then the accumulators back to zero
   auto item_end = [&]() __attribute__((always_inline)) {
-    void* out = ka->g[GRP].out;
 #pragma unroll
     for (int j = 0; j < (STAGE == 1 ? 1 : NMAT); ++j) {
       const int slab = slab_of(cit.tile, j);
@@ -490,8 +510,8 @@ __device__ __forceinline__ void stream_pass(const WCtx& c, int lo, int hi, int& 
                              static_cast<_Float16>(h));
           } else {
             const int row = GRP ? cit.seg0 + r : c.s_slots[cit.seg0 + r];
-            if (row < 0 || row >= (GRP ? c.T : ka->S)) continue;
-            gstore<float>(static_cast<float*>(out) + static_cast<long long>(row) * ka->H + n,
+            if (row < 0 || row >= (GRP ? c.T : S)) continue;
+            gstore<float>(static_cast<float*>(out) + static_cast<long long>(row) * H + n,
                           acc[j][cg][i]);
           }
         }
@@ -508,7 +528,7 @@ __device__ __forceinline__ void stream_pass(const WCtx& c, int lo, int hi, int& 
   auto begin_step = [&]() __attribute__((always_inline)) {
     if (c_blk == 0) {
       if (c_item != lo) item_end();
-      cit = decode_item(c, c_item, eh_comp);
+      cit = item_at(c, c_item);
       cur_m = cit.m;
     }
     if (step > 0) step_signal(c.done + ((step - 1) & 1), lane);  // step - 1 read
@@ -564,6 +584,7 @@ __global__ __launch_bounds__(kWThreads, 1) void wide_ffn_kernel(WArgs a) {
   int* s_cp = s_off + kMaxE + 4;
   int* s_slots = s_off + 2 * (kMaxE + 4);
   int* s_steps = s_slots + kWideMaxSlots;  // ready[2], done[2]
+  i32x4* s_items = reinterpret_cast<i32x4*>(s_steps + 4);
   uint8_t* bufs = smem + kWTabBytes;
 
   const int tid = threadIdx.x;
@@ -679,6 +700,16 @@ __global__ __launch_bounds__(kWThreads, 1) void wide_ffn_kernel(WArgs a) {
   ctx.T = a.T;
   ctx.wave = wave;
   ctx.lane = lane;
+  ctx.lo = lo;
+  ctx.nt = min(hi - lo, kWItems);
+  ctx.items = s_items;
+  ctx.ph0 = (a.g[0].nblk + a.g[0].bpp - 1) / a.g[0].bpp;
+  ctx.ph1 = (a.g[1].nblk + a.g[1].bpp - 1) / a.g[1].bpp;
+  for (int i = tid; i < ctx.nt; i += kWThreads) {
+    const It it = decode_item(ctx, lo + i);
+    s_items[i] = i32x4{it.e | (it.grp << 16), it.seg0, it.m, it.tile};
+  }
+  lds_barrier();
 
   if (wave >= kWW) {
     staging_loop<STAGE>(ctx, lo, hi);
