@@ -96,6 +96,8 @@ struct WArgs {
   int shared;               // group 1 (the FP16 shared expert) present
   int buf_bytes;            // LDS bytes per phase buffer
   int zero_dropped;         // stage 2: zero the slot_out rows of dropped slots
+  int* claim;               // routed items claimed so far (zero at the launch), or null
+  int* finished;            // workgroups done claiming (zero at the launch)
   WGroup g[2];              // 0: routed experts, 1: shared expert
 };
 
@@ -160,8 +162,13 @@ struct WCtx {
   const int* s_slots;       // stage 1: token of each position; stage 2: its slot
   int* ready;               // [2] staging waves' step counters per buffer
   int* done;                // [2] streamers' step counters per buffer
-  const i32x4* items;       // the first nt items of the workgroup's range
-  int lo, nt;
+  i32x4* items;             // the workgroup's items by local index (kWItems)
+  int lo, ns;               // its static items: global lo + i for local i < ns
+  int dyn;                  // routed items past the static ones are claimed at run time
+  int* claim;               // the launch's claim and finish counters (dyn)
+  int* finished;
+  int n0;                   // routed items
+  int nwg;
   int ph0, ph1;             // staged steps per item of each group
   int n1;                   // shared items (they come first)
   int E, T;
@@ -199,19 +206,40 @@ __device__ __forceinline__ It decode_item(const WCtx& c, int item) {
   return it;
 }
 
-// The item's fields for the whole wave: from the workgroup's table of its
-// items (filled once, in parallel), past the table's end decoded here.
-__device__ __forceinline__ It item_at(const WCtx& c, int item) {
+// Table entries of items not claimed yet, and the entry after the last item.
+constexpr int kPending = -2, kEnd = -1;
+constexpr int kClaimSpin = 1 << 22;
+
+// Whether the workgroup's local item i exists: a static item, or a claimed
+// one (waits until the claiming wave has written the entry; a wait that
+// gives up, which only a dead wave could cause, reads as the end).
+__device__ __forceinline__ bool item_valid(const WCtx& c, int i) {
+  if (i < c.ns) return true;
+  if (!c.dyn || i >= kWItems) return false;
+  int v = kPending;
+  for (int n = 0; n < kClaimSpin; ++n) {
+    v = __hip_atomic_load(reinterpret_cast<int*>(c.items + i), __ATOMIC_RELAXED,
+                          __HIP_MEMORY_SCOPE_WORKGROUP);
+    if (v != kPending) break;
+    __builtin_amdgcn_s_sleep(1);
+  }
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+  return uniform(v) >= 0;
+}
+
+// The fields of the workgroup's local item i (valid) for the whole wave:
+// from the table, or (static items past its end) decoded here.
+__device__ __forceinline__ It item_at(const WCtx& c, int i) {
   It it;
-  if (item - c.lo < c.nt) {
-    const i32x4 v = c.items[item - c.lo];
+  if (i < kWItems) {
+    const i32x4 v = c.items[i];
     it.grp = v[0] >> 16;
     it.e = v[0] & 0xFFFF;
     it.seg0 = v[1];
     it.m = v[2];
     it.tile = v[3];
   } else {
-    it = decode_item(c, item);
+    it = decode_item(c, c.lo + i);
   }
   it.grp = uniform(it.grp);
   it.e = uniform(it.e);
@@ -222,13 +250,15 @@ __device__ __forceinline__ It item_at(const WCtx& c, int item) {
 }
 
 
-// The staging waves: every (item, phase) of [lo, hi) in order, into the
-// buffer of its step's parity. Lane c of a
+// The staging waves: every (item, phase) of the workgroup's items in order,
+// into the buffer of its step's parity. With run-time claims, the first
+// staging wave also claims the routed items and writes them into the item
+// table. Lane c of a
 // staging wave copies the 16-byte piece c of every fourth row (a row of a
 // phase is at most 64 pieces), so a piece costs an add for its address and
 // a row's token is looked up once.
 template <int STAGE>
-__device__ __forceinline__ void staging_loop(const WCtx& c, int lo, int hi) {
+__device__ __forceinline__ void staging_loop(const WCtx& c) {
   ConstWArgs* ka = wkargs();
   const int ws = c.wave - kWW;
   const int lane = c.lane;
@@ -266,20 +296,71 @@ __device__ __forceinline__ void staging_loop(const WCtx& c, int lo, int hi) {
       });
     }
   };
+  // claims of local items up to i (first staging wave): one device-scope
+  // add per item; the claim that finds no item left ends the workgroup's
+  // claims, and the last workgroup to end them sets the two counters back
+  // to zero for the next launch
+  int claimed = c.ns;
+  bool over = false;
+  auto claim_upto = [&](int i) __attribute__((always_inline)) {
+    if (!c.dyn || ws != 0 || over) return;
+    while (claimed <= i) {
+      int k = c.n0;  // (the table is full: no claim)
+      if (claimed < kWItems - 1) {
+        int kk = 0;
+        if (lane == 0)
+          kk = __hip_atomic_fetch_add(c.claim, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        k = uniform(kk);
+      }
+      int* entry = reinterpret_cast<int*>(c.items + claimed);
+      if (k < c.n0) {
+        if (lane == 0) {
+          const It nt = decode_item(c, c.n1 + k);
+          entry[1] = nt.seg0;
+          entry[2] = nt.m;
+          entry[3] = nt.tile;
+          __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+          __hip_atomic_store(entry, nt.e | (nt.grp << 16), __ATOMIC_RELAXED,
+                             __HIP_MEMORY_SCOPE_WORKGROUP);
+        }
+        ++claimed;
+      } else {
+        int f = 0;
+        if (lane == 0) {
+          __hip_atomic_store(entry, kEnd, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+          f = __hip_atomic_fetch_add(c.finished, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          if (f == c.nwg - 1) {
+            __hip_atomic_store(c.claim, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_store(c.finished, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          }
+        }
+        over = true;
+        break;
+      }
+    }
+  };
+  // An item is claimed when the previous one's last phase is staged: the
+  // streamers' loads, R <= 2 blocks ahead of their MFMAs, reach it only
+  // after that phase's step has begun, and a workgroup holds little claimed
+  // work it has not started when the counter runs out.
+  claim_upto(0);
+  if (!item_valid(c, 0)) return;
   int step = 0;
-  It it = item_at(c, lo);
+  It it = item_at(c, 0);
   int p = 0;
+  if ((it.grp ? c.ph1 : c.ph0) == 1) claim_upto(1);
   stage(it, 0, 0);
   step_signal(c.ready, lane);
-  for (int item = lo;;) {
+  for (int item = 0;;) {
     // the next step: next phase of this item, or the next item's first
     int nitem = item, np = p + 1;
     if (np >= (it.grp ? c.ph1 : c.ph0)) {
       ++nitem;
       np = 0;
+      if (!item_valid(c, nitem)) break;
     }
-    if (nitem >= hi) break;
     const It nit = nitem == item ? it : item_at(c, nitem);
+    if (np == (nit.grp ? c.ph1 : c.ph0) - 1) claim_upto(nitem + 1);
     const int s1 = step + 1, b = s1 & 1;
     if (s1 >= 2) step_wait(c.done + b, kWW * (s1 >> 1));  // steps s1 - 2, s1 - 4, ... read
     stage(nit, np, b);
@@ -291,7 +372,9 @@ __device__ __forceinline__ void staging_loop(const WCtx& c, int lo, int hi) {
   }
 }
 
-// One streamer wave over the items [lo, hi), all of group GRP, whose
+// One streamer wave over the local items [first, last) (last < 0: up to the
+// first local item that does not exist, claimed at run time), all of group
+// GRP, whose
 // weights are in format FMT: NC column groups of 16 positions against 16
 // rows of each weight stream over the whole reduction length. In stage 1
 // the streams are the gate and up rows of slab tile * 8 + wave; in stage 2
@@ -300,7 +383,7 @@ __device__ __forceinline__ void staging_loop(const WCtx& c, int lo, int hi) {
 // of the workgroup (the parity picks the buffer); it runs on from one pass
 // to the next.
 template <int FMT, int G, int STAGE, int NC, int GRP, int SL>
-__device__ __forceinline__ void stream_pass(const WCtx& c, int lo, int hi, int& step) {
+__device__ __forceinline__ void stream_pass(const WCtx& c, int first, int last, int& step) {
   constexpr int NMAT = STAGE == 1 ? 2 : SL;  // weight streams
   constexpr int NQ = FMT == kInt4 ? 128 / G : 1;  // INT4 scales per block and row
   constexpr int NS = NQ == 4 ? 2 : 1;
@@ -332,6 +415,7 @@ __device__ __forceinline__ void stream_pass(const WCtx& c, int lo, int hi, int& 
   };
   struct Cur {  // the load cursor: a position in the wave's block sequence (wave-uniform)
     int item, blk;
+    bool done;                // past the last item
     const uint8_t* w[NMAT];   // each stream's current block
     const uint16_t* s[NMAT];  // and its scales (INT4)
   };
@@ -354,6 +438,9 @@ __device__ __forceinline__ void stream_pass(const WCtx& c, int lo, int hi, int& 
     uint16_t s16[NMAT];
   };
   constexpr int R = kWRing / NMAT;  // ring entries: kWRing weight blocks in flight
+  // The load cursor runs R blocks ahead; a routed item is claimed when the
+  // previous item's last phase is staged, which covers it when R <= 2.
+  static_assert(GRP == 1 || R <= 2, "a claimed item must be in the table before the loads reach it");
   Entry ring[R];
   // Every ring slot takes a load on every pass, also past the end of the
   // range (the last block again), so that the compiler waits only for the
@@ -380,6 +467,7 @@ __device__ __forceinline__ void stream_pass(const WCtx& c, int lo, int hi, int& 
   };
   // the next block; past the end of the range the cursor stays on the last
   // block (it is loaded again, never computed)
+  int c_end = last >= 0 ? last : 0x7FFFFFFF;  // the first local item past the range
   auto advance = [&](Cur& cu) __attribute__((always_inline)) {
     if (cu.blk + 1 < nblk) {
       ++cu.blk;
@@ -388,9 +476,14 @@ __device__ __forceinline__ void stream_pass(const WCtx& c, int lo, int hi, int& 
         cu.w[m] += 1024;
         if (FMT == kInt4) cu.s[m] += 16 * NQ;
       }
-    } else if (cu.item < hi) {
-      ++cu.item;
-      if (cu.item < hi) settle(cu);
+    } else if (!cu.done) {
+      if (last >= 0 ? cu.item + 1 < last : item_valid(c, cu.item + 1)) {
+        ++cu.item;
+        settle(cu);
+      } else {
+        cu.done = true;
+        c_end = cu.item + 1;  // before the compute cursor gets there (it is R blocks behind)
+      }
     }
   };
 
@@ -524,10 +617,10 @@ __device__ __forceinline__ void stream_pass(const WCtx& c, int lo, int hi, int& 
   };
   // before the first block of a step: the step's barrier and A rows
   // the compute cursor: item, block and block within the phase
-  int c_item = lo, c_blk = 0, c_bip = 0;
+  int c_item = first, c_blk = 0, c_bip = 0;
   auto begin_step = [&]() __attribute__((always_inline)) {
     if (c_blk == 0) {
-      if (c_item != lo) item_end();
+      if (c_item != first) item_end();
       cit = item_at(c, c_item);
       cur_m = cit.m;
     }
@@ -537,7 +630,6 @@ __device__ __forceinline__ void stream_pass(const WCtx& c, int lo, int hi, int& 
     ++step;
   };
 
-  int left = (hi - lo) * nblk;  // blocks of the range (the wave streams every block of its slab)
   auto advance_comp = [&]() __attribute__((always_inline)) {
     if (++c_blk == nblk) {
       c_blk = 0;
@@ -548,32 +640,34 @@ __device__ __forceinline__ void stream_pass(const WCtx& c, int lo, int hi, int& 
     }
   };
   Cur L;
-  L.item = lo;
+  L.item = first;
+  L.done = false;
   settle(L);
   static_for<0, R>([&](auto rc) {
     load(ring[decltype(rc)::value], L);
     advance(L);
   });
   constexpr int kBlkK = FMT == kInt4 ? 128 : 32;  // k per block
-  while (left >= R) {
-#pragma clang loop unroll(full)
-    for (int r = 0; r < R; ++r) {
+  // While the load cursor is inside the range, the R blocks in the ring all
+  // lie before it: R blocks a round, no checks. Then at most R are left.
+  while (!L.done) {
+    static_for<0, R>([&](auto rc) {
+      constexpr int r = decltype(rc)::value;
       if (c_bip == 0) begin_step();
       compute(ring[r], c_bip * kBlkK);
       load(ring[r], L);
       advance(L);
       advance_comp();
-    }
-    left -= R;
+    });
   }
-#pragma clang loop unroll(full)
-  for (int r = 0; r < R; ++r) {
-    if (r < left) {
+  static_for<0, R>([&](auto rc) {
+    constexpr int r = decltype(rc)::value;
+    if (c_item < c_end) {
       if (c_bip == 0) begin_step();
       compute(ring[r], c_bip * kBlkK);
       advance_comp();
     }
-  }
+  });
   item_end();
 }
 
@@ -643,20 +737,30 @@ __global__ __launch_bounds__(kWThreads, 1) void wide_ffn_kernel(WArgs a) {
   }
 
   // ---- the work list: the shared items first, then the routed experts
-  // chunk by chunk, tile by tile. The first Ws workgroups share out the
-  // shared items (q or fewer each), the others the routed items, in
-  // contiguous ranges. A shared item is a few times a routed one, so a
-  // split of the whole list by cost would leave some workgroups one whole
-  // shared item over the mean; q is chosen so that the longer of the two
-  // sets is as short as possible (estimated from the items' costs).
+  // chunk by chunk, tile by tile.
+  // Run-time claims (the usual case): the first Ws workgroups share out the
+  // shared items, q each (q shared items about the mean work of a
+  // workgroup); every workgroup then claims routed items one by one from a
+  // device counter, so the workgroups end together whatever their speed
+  // (static ranges of items a few times the mean work would leave some one
+  // whole item over it).
+  // Static ranges (windows with more items than the workgroups' tables
+  // hold): the first Ws workgroups share out the shared items, the others
+  // the routed ones, q chosen so that the longer of the two sets is as short
+  // as possible (estimated from the items' costs).
   const int n1c = a.shared ? (a.T + a.g[1].ch - 1) / a.g[1].ch : 0;  // shared chunks
   const int nrc = uniform(s_cp[E]);                                  // routed chunks
   const long long n1 = static_cast<long long>(n1c) * a.g[1].tiles;
   const long long n0 = static_cast<long long>(nrc) * a.g[0].tiles;
   const long long c1 = a.g[1].cost, c0 = a.g[0].cost;
+  const bool dyn = a.claim != nullptr && n0 > 0 && n1 + n0 <= 16ll * nwg;
   long long Ws = 0;  // workgroups on the shared items
   if (n1 > 0) {
-    if (n0 == 0) {
+    if (dyn) {
+      // (at most 32 static items: the table keeps room for claimed ones)
+      const long long q = min(32ll, max(1ll, (n1 * c1 + n0 * c0) / nwg / c1));
+      Ws = min((n1 + q - 1) / q, static_cast<long long>(nwg));
+    } else if (n0 == 0) {
       Ws = min(n1, static_cast<long long>(nwg));
     } else {
       long long best = -1;
@@ -672,8 +776,11 @@ __global__ __launch_bounds__(kWThreads, 1) void wide_ffn_kernel(WArgs a) {
       }
     }
   }
-  long long lo_l, hi_l;
-  if (Ws == 0) {  // one set over the whole list (no shared items, or too few workgroups)
+  long long lo_l, hi_l;  // the static items
+  if (dyn) {
+    lo_l = b < Ws ? n1 * b / Ws : 0;
+    hi_l = b < Ws ? n1 * (b + 1) / Ws : 0;
+  } else if (Ws == 0) {  // one set over the whole list (no shared items, or too few workgroups)
     lo_l = (n1 + n0) * b / nwg;
     hi_l = (n1 + n0) * (b + 1) / nwg;
   } else if (b < Ws) {
@@ -686,7 +793,7 @@ __global__ __launch_bounds__(kWThreads, 1) void wide_ffn_kernel(WArgs a) {
   }
   const int lo = uniform(static_cast<int>(lo_l));
   const int hi = uniform(static_cast<int>(hi_l));
-  if (lo >= hi) return;  // the whole workgroup: no barrier follows
+  if (!dyn && lo >= hi) return;  // the whole workgroup: no barrier follows
 
   WCtx ctx;
   ctx.bufs = bufs;
@@ -696,30 +803,40 @@ __global__ __launch_bounds__(kWThreads, 1) void wide_ffn_kernel(WArgs a) {
   ctx.ready = s_steps;
   ctx.done = s_steps + 2;
   ctx.n1 = static_cast<int>(n1);
+  ctx.n0 = static_cast<int>(n0);
+  ctx.nwg = nwg;
   ctx.E = E;
   ctx.T = a.T;
   ctx.wave = wave;
   ctx.lane = lane;
   ctx.lo = lo;
-  ctx.nt = min(hi - lo, kWItems);
+  ctx.ns = hi - lo;
+  ctx.dyn = dyn;
+  ctx.claim = a.claim;
+  ctx.finished = a.finished;
   ctx.items = s_items;
   ctx.ph0 = (a.g[0].nblk + a.g[0].bpp - 1) / a.g[0].bpp;
   ctx.ph1 = (a.g[1].nblk + a.g[1].bpp - 1) / a.g[1].bpp;
-  for (int i = tid; i < ctx.nt; i += kWThreads) {
-    const It it = decode_item(ctx, lo + i);
-    s_items[i] = i32x4{it.e | (it.grp << 16), it.seg0, it.m, it.tile};
+  for (int i = tid; i < kWItems; i += kWThreads) {
+    if (i < ctx.ns) {
+      const It it = decode_item(ctx, lo + i);
+      s_items[i] = i32x4{it.e | (it.grp << 16), it.seg0, it.m, it.tile};
+    } else {
+      s_items[i] = i32x4{kPending, 0, 0, 0};
+    }
   }
   lds_barrier();
 
   if (wave >= kWW) {
-    staging_loop<STAGE>(ctx, lo, hi);
+    staging_loop<STAGE>(ctx);
     return;
   }
-  // streamers: the shared items of the range, then its routed items
-  const int mid = min(max(lo, static_cast<int>(n1)), hi);
+  // streamers: the shared items among the static ones, then the routed ones
+  const int ns1 = min(max(static_cast<int>(n1) - lo, 0), ctx.ns);
   int step = 0;
-  if (lo < mid) stream_pass<kFp16, 128, STAGE, STAGE == 1 ? kNC1 : kNC0, 1, 1>(ctx, lo, mid, step);
-  if (mid < hi) stream_pass<WK, G, STAGE, kNC0, 0, STAGE == 2 ? kSL0 : 1>(ctx, mid, hi, step);
+  if (ns1 > 0) stream_pass<kFp16, 128, STAGE, STAGE == 1 ? kNC1 : kNC0, 1, 1>(ctx, 0, ns1, step);
+  if (item_valid(ctx, ns1))
+    stream_pass<WK, G, STAGE, kNC0, 0, STAGE == 2 ? kSL0 : 1>(ctx, ns1, dyn ? -1 : ctx.ns, step);
 }
 
 // ------------------------------------------------------------------ host side
@@ -757,9 +874,13 @@ smoe_status launch_wide(const WArgs& a, long long items, hipStream_t st, const c
 
 }  // namespace
 
+// The fp16 h rows, then 256 bytes of the launches' claim counters.
+static long long h_rows_bytes(long long T, long long k, long long I, long long Is) {
+  return (2 * (T * k * I + T * Is) + 255) / 256 * 256;
+}
+
 size_t wide_h_bytes(long long T, long long k, long long I, long long Is) {
-  const long long bytes = 2 * (T * k * I + T * Is);
-  return static_cast<size_t>((bytes + 255) / 256 * 256);
+  return static_cast<size_t>(h_rows_bytes(T, k, I, Is) + 256);
 }
 
 bool wide_applicable(const WideCall& c) {
@@ -789,6 +910,10 @@ smoe_status wide_ffn(const WideCall& c, hipStream_t st, const char* who) {
   };
   _Float16* h_r = static_cast<_Float16*>(c.h);
   _Float16* h_s = h_r + S * c.I;
+  // claim counters: [0] stage 1 and [1] stage 2 claims, [2], [3] their
+  // finish counts; zero in a fresh workspace, and each launch leaves its
+  // own at zero
+  int* ctr = reinterpret_cast<int*>(static_cast<uint8_t*>(c.h) + h_rows_bytes(c.T, c.k, c.I, c.Is));
   // Work-split cost of a 64-byte block per wave, relative (measured): an
   // INT4 block (dequantised, 64 positions) takes about 2.5x an FP16 block
   // of the 128-token shared chunks, which takes about 1.3x an FP16 block of
@@ -818,6 +943,10 @@ smoe_status wide_ffn(const WideCall& c, hipStream_t st, const char* who) {
   WArgs a1, a2;
   base(a1, 1);
   base(a2, 2);
+  a1.claim = ctr;
+  a1.finished = ctr + 2;
+  a2.claim = ctr + 1;
+  a2.finished = ctr + 3;
   fill(a1.g[0], c.wg, c.wu, c.sg, c.su, c.fmt, c.I, c.H, kNC0, kKph0, 1, c.x, h_r);
   fill(a2.g[0], c.wd, nullptr, c.sd, nullptr, c.fmt, c.H, c.I, kNC0, kKph0, kSL0, h_r,
        c.slot_out);
