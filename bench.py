@@ -745,10 +745,14 @@ def main() -> int:
     fb = ffn_bytes(base, n_active, fused)
     achieved = fb / (ffn_stats["mean"] * 1e3)  # bytes/ns = GB/s
     traffic = recorded_traffic(cfg.name, args.shared, args.layout)
+    # windows of 1024 to 4096 slots over tiled weights take the long-window kernel
+    long_window = args.layout == "tiled" and 1024 <= cfg.T * cfg.k <= 4096
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBPS,
                 "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBPS, 4),
                 "traffic": traffic,
-                "kernel": ("smoe_w4a16_expert_ffn (ffn_kernel stage 1 + 2, routed"
+                "kernel": ("smoe_w4a16_expert_ffn ("
+                           + ("wide_ffn_kernel" if long_window else "ffn_kernel")
+                           + " stage 1 + 2, routed"
                            + (" + shared experts)" if fused else " experts)")),
                 "bytes_per_launch": fb, "us_per_launch": round(ffn_stats["mean"], 2)}
 

@@ -173,8 +173,10 @@ smoe_status smoe_route_align_elb(const void* x, const float* w_router, const flo
  * Device workspace (bytes) that the expert FFN calls need for a window of
  * T tokens, k slots per token, routed intermediate size I and shared
  * intermediate size shared_I (0 = no shared expert): two fp32 buffers of
- * the gate and up projections of every slot, and a small call counter.
- * Returns 0 for invalid sizes.
+ * the gate and up projections of every slot, and a small call counter;
+ * windows that take the long-window kernel (1024 to 4096 slots over tiled
+ * weights) add their fp16 intermediate rows and the counters the kernel's
+ * workgroups claim items from. Returns 0 for invalid sizes.
  *
  * Workspace contract: the caller fills the buffer with zeros
  * (smoe_ffn_workspace_clear, or any fill) before its first use, and again
