@@ -615,6 +615,70 @@ def test_w4a16_ffn_long_window(smoe, E, k, T, H, I, G, Is, drop):
     assert (got[dropped] == 0).all()
 
 
+def test_w4a16_ffn_long_window_claims_across_calls(smoe):
+    # The long-window FFN hands its routed items out at run time from
+    # counters in the workspace, which each launch leaves at zero. Calls in
+    # a row on one workspace with different routings (different numbers of
+    # items), eagerly and replayed from a HIP graph: every call's rows equal
+    # the oracle's, and the same call gives the same bits however its items
+    # fell to the workgroups.
+    E, k, T, H, I, G, Is = 16, 4, 300, 256, 256, 128, 256
+    rng = np.random.default_rng(5)
+    q = _synthetic_int4(E, H, I, G, seed=21)
+    x = rng.standard_normal((T, H)).astype(np.float16)
+    shared = tuple((rng.standard_normal(sh) * 0.02).astype(np.float16)
+                   for sh in ((Is, H), (Is, H), (H, Is)))
+    sh, sh_out, _ = _shared_dev(shared, T, H, smoe, True)
+    ws = torch.zeros(smoe.smoe_ffn_workspace_bytes(T, k, E, H, I, Is), dtype=torch.uint8,
+                     device="cuda")
+    xd = dev(x)
+    w = [dev(q[n]) for n in ("wg_q", "wg_s", "wu_q", "wu_s", "wd_q", "wd_s")]
+    w[0:2] = tile_dev(smoe, w[0], w[1], E, I, H, G)
+    w[2:4] = tile_dev(smoe, w[2], w[3], E, I, H, G)
+    w[4:6] = tile_dev(smoe, w[4], w[5], E, H, I, G)
+    out = torch.empty((T * k, H), dtype=torch.float32, device="cuda")
+
+    def call(ss, off):
+        smoe.smoe_w4a16_expert_ffn_tiled(xd, k, E, I, G, *w, ss, off, ws, out,
+                                         shared=sh, shared_out=sh_out)
+
+    def ref_of(ids):
+        return oracle.routed_ffn_expertwise(x, ids, lambda e: tuple(
+            oracle.dequant_int4(q[n + "_q"][e], q[n + "_s"][e], G) for n in ("wg", "wu", "wd")))
+
+    routings = [_long_window_ids(rng, T, k, E, s, 0.0) for s in (0.0, 1.5, 0.7)]
+    aligned = [oracle.align_by_expert(ids, E) for ids in routings]
+    dev_al = [(dev(al["sorted_slots"]), dev(al["offsets"])) for al in aligned]
+    first = []
+    for ids, (ss, off) in zip(routings, dev_al):
+        out.fill_(float("nan"))
+        call(ss, off)
+        got = host(out)
+        assert np.isfinite(got).all()
+        assert row_rel_err(got, ref_of(ids)) <= ROW_TOL
+        first.append(got)
+    assert row_rel_err(host(sh_out), oracle.shared_ffn(x, *shared)) <= ROW_TOL
+    # graph replays of the second routing, with eager calls of the others between
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(s):
+        call(*dev_al[1])
+        torch.cuda.synchronize()
+        with torch.cuda.graph(g, stream=s):
+            call(*dev_al[1])
+    torch.cuda.current_stream().wait_stream(s)
+    for i in range(3):
+        out.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(host(out), first[1]), i
+        call(*dev_al[(i % 2) * 2])
+        torch.cuda.synchronize()
+        assert np.array_equal(host(out), first[(i % 2) * 2]), i
+
+
 @pytest.mark.parametrize("Is", [0, 256])
 def test_fp16_ffn_long_window(smoe, Is):
     E, k, T, H, I = 12, 4, 300, 256, 384
