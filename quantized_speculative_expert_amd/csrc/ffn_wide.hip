@@ -339,18 +339,19 @@ __device__ __forceinline__ void staging_loop(const WCtx& c) {
       }
     }
   };
-  // An item is claimed when the previous one's last phase is staged: the
-  // streamers' loads, R <= 2 blocks ahead of their MFMAs, reach it only
-  // after that phase's step has begun, and a workgroup holds little claimed
-  // work it has not started when the counter runs out.
+  // An item is claimed right after the previous one's last phase is staged
+  // (so the claim's round trip does not delay that phase): the streamers'
+  // loads, R <= 2 blocks ahead of their MFMAs, reach it only after that
+  // phase's step has begun, and a workgroup holds little claimed work it
+  // has not started when the counter runs out.
   claim_upto(0);
   if (!item_valid(c, 0)) return;
   int step = 0;
   It it = item_at(c, 0);
   int p = 0;
-  if ((it.grp ? c.ph1 : c.ph0) == 1) claim_upto(1);
   stage(it, 0, 0);
   step_signal(c.ready, lane);
+  if ((it.grp ? c.ph1 : c.ph0) == 1) claim_upto(1);
   for (int item = 0;;) {
     // the next step: next phase of this item, or the next item's first
     int nitem = item, np = p + 1;
@@ -360,11 +361,11 @@ __device__ __forceinline__ void staging_loop(const WCtx& c) {
       if (!item_valid(c, nitem)) break;
     }
     const It nit = nitem == item ? it : item_at(c, nitem);
-    if (np == (nit.grp ? c.ph1 : c.ph0) - 1) claim_upto(nitem + 1);
     const int s1 = step + 1, b = s1 & 1;
     if (s1 >= 2) step_wait(c.done + b, kWW * (s1 >> 1));  // steps s1 - 2, s1 - 4, ... read
     stage(nit, np, b);
     step_signal(c.ready + b, lane);
+    if (np == (nit.grp ? c.ph1 : c.ph0) - 1) claim_upto(nitem + 1);
     item = nitem;
     p = np;
     it = nit;
@@ -438,7 +439,7 @@ __device__ __forceinline__ void stream_pass(const WCtx& c, int first, int last, 
     uint16_t s16[NMAT];
   };
   constexpr int R = kWRing / NMAT;  // ring entries: kWRing weight blocks in flight
-  // The load cursor runs R blocks ahead; a routed item is claimed when the
+  // The load cursor runs R blocks ahead; a routed item is claimed once the
   // previous item's last phase is staged, which covers it when R <= 2.
   static_assert(GRP == 1 || R <= 2, "a claimed item must be in the table before the loads reach it");
   Entry ring[R];
