@@ -270,30 +270,52 @@ __device__ __forceinline__ void staging_loop(const WCtx& c) {
   const uint16_t* const a0 = uniform_ptr(ka->g[0].a);
   const uint16_t* const a1 = uniform_ptr(ka->g[1].a);
   const int S = uniform(ka->S);
-  auto stage = [&](const It& it, int p, int buf) __attribute__((always_inline)) {
-    const int K = it.grp ? K1 : K0;
+  // A step is staged in two parts. The first batch of rows (kWStageNB rows
+  // per wave, all of a 64-row chunk) is loaded into registers before the
+  // wave waits for its buffer to be free, so the loads' round trip overlaps
+  // the streamers' use of that buffer; the rest (rows past the batch) is
+  // loaded and written after.
+  struct Src {
+    const uint16_t* src;  // this lane's piece in row 0 of the source
+    int K, rstride, rows;
+    bool on;              // the lane holds a piece of this phase
+  };
+  auto src_of = [&](const It& it, int p) __attribute__((always_inline)) {
+    Src q;
+    q.K = it.grp ? K1 : K0;
     const int kph = it.grp ? kph1 : kph0;
-    const int rstride = it.grp ? rs1 : rs0;
+    q.rstride = it.grp ? rs1 : rs0;
     const int k0 = p * kph;
-    const int npr = min(kph, K - k0) / 8;  // 16-byte pieces per row
-    const uint16_t* src = (it.grp ? a1 : a0) + k0 + 8 * min(lane, npr - 1);
+    const int npr = min(kph, q.K - k0) / 8;  // 16-byte pieces per row
+    q.src = (it.grp ? a1 : a0) + k0 + 8 * min(lane, npr - 1);
+    q.on = lane < npr;
+    q.rows = STAGE == 1 ? c.T : (it.grp ? c.T : S);  // rows of the source
+    return q;
+  };
+  auto load_rows = [&](const It& it, const Src& q, int r0, u32x4 (&v)[kWStageNB])
+      __attribute__((always_inline)) {
+    static_for<0, kWStageNB>([&](auto jc) {
+      constexpr int j = decltype(jc)::value;
+      const int r = min(r0 + j * kWS, it.m - 1);
+      int row = (STAGE == 1 && !it.grp) ? uniform(c.s_slots[it.seg0 + r]) : it.seg0 + r;
+      row = min(max(row, 0), q.rows - 1);
+      v[j] = gload<u32x4>(q.src + static_cast<long long>(row) * q.K);
+    });
+  };
+  auto store_rows = [&](const It& it, const Src& q, int r0, int buf, const u32x4 (&v)[kWStageNB])
+      __attribute__((always_inline)) {
     uint8_t* dst0 = c.bufs + buf * buf_bytes + 16 * lane;
-    const bool on = lane < npr;
-    const int rows = STAGE == 1 ? c.T : (it.grp ? c.T : S);  // rows of the source
-    for (int r0 = ws; r0 < it.m; r0 += kWS * kWStageNB) {
+    static_for<0, kWStageNB>([&](auto jc) {
+      constexpr int j = decltype(jc)::value;
+      const int r = r0 + j * kWS;
+      if (q.on && r < it.m) *reinterpret_cast<u32x4*>(dst0 + r * q.rstride) = v[j];
+    });
+  };
+  auto stage_rest = [&](const It& it, const Src& q, int buf) __attribute__((always_inline)) {
+    for (int r0 = ws + kWS * kWStageNB; r0 < it.m; r0 += kWS * kWStageNB) {
       u32x4 v[kWStageNB];
-      static_for<0, kWStageNB>([&](auto jc) {
-        constexpr int j = decltype(jc)::value;
-        const int r = min(r0 + j * kWS, it.m - 1);
-        int row = (STAGE == 1 && !it.grp) ? uniform(c.s_slots[it.seg0 + r]) : it.seg0 + r;
-        row = min(max(row, 0), rows - 1);
-        v[j] = gload<u32x4>(src + static_cast<long long>(row) * K);
-      });
-      static_for<0, kWStageNB>([&](auto jc) {
-        constexpr int j = decltype(jc)::value;
-        const int r = r0 + j * kWS;
-        if (on && r < it.m) *reinterpret_cast<u32x4*>(dst0 + r * rstride) = v[j];
-      });
+      load_rows(it, q, r0, v);
+      store_rows(it, q, r0, buf, v);
     }
   };
   // claims of local items up to i (first staging wave): one device-scope
@@ -349,7 +371,13 @@ __device__ __forceinline__ void staging_loop(const WCtx& c) {
   int step = 0;
   It it = item_at(c, 0);
   int p = 0;
-  stage(it, 0, 0);
+  u32x4 v[kWStageNB];
+  {
+    const Src q = src_of(it, 0);
+    load_rows(it, q, ws, v);
+    store_rows(it, q, ws, 0, v);
+    stage_rest(it, q, 0);
+  }
   step_signal(c.ready, lane);
   if ((it.grp ? c.ph1 : c.ph0) == 1) claim_upto(1);
   for (int item = 0;;) {
@@ -362,8 +390,11 @@ __device__ __forceinline__ void staging_loop(const WCtx& c) {
     }
     const It nit = nitem == item ? it : item_at(c, nitem);
     const int s1 = step + 1, b = s1 & 1;
+    const Src q = src_of(nit, np);
+    load_rows(nit, q, ws, v);  // in flight while the buffer is still read
     if (s1 >= 2) step_wait(c.done + b, kWW * (s1 >> 1));  // steps s1 - 2, s1 - 4, ... read
-    stage(nit, np, b);
+    store_rows(nit, q, ws, b, v);
+    stage_rest(nit, q, b);
     step_signal(c.ready + b, lane);
     if (np == (nit.grp ? c.ph1 : c.ph0) - 1) claim_upto(nitem + 1);
     item = nitem;
