@@ -152,10 +152,17 @@ def ffn_flops(d, with_shared: bool) -> int:
 # ----------------------------------------------------------------------------- traffic
 
 def source_digest() -> str:
+    """Digest of the FFN sources' code: comments, trailing blanks and empty
+    lines are left out, so that an edit of the comments alone keeps the
+    recorded counters valid."""
     h = hashlib.sha256()
     for f in FFN_SOURCES:
-        with open(f, "rb") as fh:
-            h.update(fh.read())
+        with open(f, encoding="utf-8") as fh:
+            text = re.sub(r"/\*.*?\*/", "", fh.read(), flags=re.S)
+        for line in text.splitlines():
+            line = re.sub(r"//.*", "", line).rstrip()
+            if line:
+                h.update(line.encode() + b"\n")
     return h.hexdigest()[:16]
 
 

@@ -23,16 +23,21 @@
 // no atomics, nothing to clear, the same result on every run.
 //
 // Four more waves stage the item's activation rows into LDS, k-phase by
-// k-phase (double-buffered, one barrier per phase), while the eight stream
-// their weight rows through a register ring of R blocks that runs on across
-// phases and items (the streamers never wait on anything but their oldest
-// weight block and the phase barrier). INT4 and FP16 weights come tiled
+// k-phase (double-buffered; the hand-over is a pair of step counters in LDS,
+// not a barrier), while the eight stream their weight rows through a
+// register ring of R blocks that runs on across phases and items (the
+// streamers never wait on anything but their oldest weight block and the
+// step counter of the buffer they read). INT4 and FP16 weights come tiled
 // (smoe_tile_weights): one wave load reads 16 rows x 64 bytes in one piece.
 //
-// Work split: the items (shared expert first, then the routed experts chunk
-// by chunk, tile by tile) are cut into one contiguous range per workgroup,
-// balanced by the weight blocks a wave streams per item; computed on the
-// device from the expert offsets, nothing read back.
+// Work split, computed on the device from the expert offsets (nothing read
+// back): the shared expert's items are cut into contiguous ranges over the
+// first workgroups, balanced by the weight blocks a wave streams per item;
+// the routed items (chunk by chunk, tile by tile) are claimed one at a time
+// at run time from a counter in the workspace, so that a workgroup that
+// drew cheap items takes more. When a launch has more than 16 items per
+// workgroup (past what the LDS item tables are sized for), every item is
+// cut into static ranges instead.
 #include <algorithm>
 #include <atomic>
 #include <type_traits>
