@@ -615,6 +615,49 @@ def test_w4a16_ffn_long_window(smoe, E, k, T, H, I, G, Is, drop):
     assert (got[dropped] == 0).all()
 
 
+def _wide_items(ids, E, T, n, tiles, shared_tiles):
+    # items of one long-window stage: 64-position chunks of every expert's
+    # slots times the row tiles, plus the shared expert's chunks times its
+    # tiles (shared_tiles = (tokens per chunk, tiles), or None)
+    cnt = np.bincount(ids[ids >= 0].reshape(-1), minlength=E)
+    items = int(np.sum((cnt + n - 1) // n)) * tiles
+    if shared_tiles is not None:
+        ch, st = shared_tiles
+        items += (T + ch - 1) // ch * st
+    return items
+
+
+@pytest.mark.parametrize("stage,H,I,Is", [
+    (1, 128, 8320, 256),     # gate/up: 64 chunks x 65 row tiles
+    (2, 16384, 128, 128),    # down: 64 chunks x 64 tiles of 256 rows, 8 x 128 shared
+])
+def test_w4a16_ffn_long_window_static_split(smoe, stage, H, I, Is):
+    # Launches with more than 16 items per workgroup (past the LDS item
+    # tables' room at 256 workgroups) cut every item into static ranges
+    # instead of claiming the routed ones at run time.
+    E, k, T, G = 8, 8, 512, 128
+    rng = np.random.default_rng(31 + stage)
+    q = _synthetic_int4(E, H, I, G, seed=40 + stage)
+    x = rng.standard_normal((T, H)).astype(np.float16)
+    ids = _long_window_ids(rng, T, k, E, 0.0, 0.02)
+    if stage == 1:
+        n_items = _wide_items(ids, E, T, 64, I // 128, (128, Is // 128))
+    else:
+        n_items = _wide_items(ids, E, T, 64, (H // 16 + 15) // 16, (64, H // 128))
+    assert n_items > 16 * 256, n_items
+    shared = tuple((rng.standard_normal(sh) * 0.02).astype(np.float16)
+                   for sh in ((Is, H), (Is, H), (H, Is)))
+    got, got_s = run_w4a16(smoe, x, ids, E, I, G, q["wg_q"], q["wg_s"], q["wu_q"], q["wu_s"],
+                           q["wd_q"], q["wd_s"], shared=shared, calls=2, tiled=True)
+    assert row_rel_err(got_s, oracle.shared_ffn(x, *shared)) <= ROW_TOL
+    ref = oracle.routed_ffn_expertwise(x, ids, lambda e: tuple(
+        oracle.dequant_int4(q[n + "_q"][e], q[n + "_s"][e], G) for n in ("wg", "wu", "wd")))
+    dropped = ids.reshape(-1) < 0
+    assert np.isfinite(got).all()
+    assert row_rel_err(got[~dropped], ref[~dropped]) <= ROW_TOL
+    assert (got[dropped] == 0).all()
+
+
 def test_w4a16_ffn_long_window_claims_across_calls(smoe):
     # The long-window FFN hands its routed items out at run time from
     # counters in the workspace, which each launch leaves at zero. Calls in
