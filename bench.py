@@ -60,9 +60,11 @@ def parse_args():
     p.add_argument("--shared", choices=("fused", "separate"), default="fused",
                    help="shared experts inside the routed FFN launches (fused) or as a call "
                         "of their own (separate)")
-    p.add_argument("--layer", choices=("one-call", "calls"), default="calls",
-                   help="the layer step as one library call (smoe_moe_layer_w4a16) or as "
-                        "the separate calls")
+    p.add_argument("--layer", choices=("one-call", "calls"), default=None,
+                   help="the layer step as one library call (smoe_moe_layer_w4a16, whose "
+                        "routing launch also reads the shared experts' weights through the "
+                        "caches) or as the separate calls; default: one call with the shared "
+                        "experts fused and no side stream, else the separate calls")
     p.add_argument("--layout", choices=("tiled", "rows"), default="tiled",
                    help="expert weights in the tiled layout of smoe_tile_weights, tiled once "
                         "before timing (default), or row-major")
@@ -675,6 +677,8 @@ def main() -> int:
     side = torch.cuda.Stream(device=dev) if args.side_stream else None
     use_elb = cfg.elb_M > 0
 
+    if args.layer is None:
+        args.layer = "one-call" if fused and side is None else "calls"
     one_call = args.layer == "one-call"
     if one_call and (not fused or side is not None):
         raise SystemExit("--layer one-call runs the shared experts fused and has no side stream")

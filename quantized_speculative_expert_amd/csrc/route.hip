@@ -150,9 +150,37 @@ __global__ __launch_bounds__(kTopkWaves * kWave) void topk_kernel(RouteArgs a) {
 
 // Top-k, alignment and the ELB update of one layer in one workgroup of
 // kAlignThreads (smoe_blocks.hpp), for windows of at most kFusedMaxSlots
-// slots. The results equal those of the three separate kernels.
+// slots. The results equal those of the three separate kernels. Workgroups
+// past the first only read the prefetch list.
+// A prefetch workgroup (blockIdx.x >= 1): 16-byte loads strided over the
+// listed weights, eight in flight per lane; the values are folded into one
+// word that is stored only under a flag that is never set.
+__device__ __forceinline__ void prefetch_block(const FusedArgs& f) {
+  const long long stride = static_cast<long long>(gridDim.x - 1) * kAlignThreads;
+  const long long first = static_cast<long long>(blockIdx.x - 1) * kAlignThreads + threadIdx.x;
+  uint32_t acc = 0;
+  for (int r = 0; r < 3; ++r) {
+    const uint4* p = f.pf[r];
+    const long long n = f.pf_n[r];
+    long long u = first;
+    for (; u + 7 * stride < n; u += 8 * stride) {
+      uint4 v[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) v[j] = p[u + j * stride];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) acc ^= v[j].x ^ v[j].w;
+    }
+    for (; u < n; u += stride) acc ^= p[u].x;
+  }
+  if (f.pf_never) f.counts[0] = static_cast<int32_t>(acc);
+}
+
 __global__ __launch_bounds__(kAlignThreads) void topk_align_elb_kernel(FusedArgs f) {
   __shared__ RouteBlockSmem<kAlignThreads> sm;
+  if (blockIdx.x > 0) {
+    prefetch_block(f);
+    return;
+  }
   route_align_elb_block(f, sm);
 }
 
@@ -241,13 +269,14 @@ extern "C" smoe_status smoe_route_topk(const void* x, const float* w_router,
   return check_launch("route_topk");
 }
 
-extern "C" smoe_status smoe_route_align_elb(
+namespace smoe {
+smoe_status route_align_elb(
     const void* x, const float* w_router, const float* logit_bias, int T, int H, int E, int k,
     int flags, int32_t* topk_ids, float* topk_w, float* logits, const float* shared_gate_w,
     float* shared_gate, int32_t* expert_counts, int32_t* expert_offsets, int32_t* sorted_slots,
     int32_t* active_experts, int32_t* n_active, int32_t* elb_counts, int L, int layer, int M,
-    int32_t* plan_ids, int32_t* plan_counts, int elb_flags, void* stream) {
-  clear_error();
+    int32_t* plan_ids, int32_t* plan_counts, int elb_flags, void* stream,
+    const RoutePrefetch* pf) {
   RouteArgs a;
   smoe_status s = route_check(x, w_router, logit_bias, T, H, E, k, flags, topk_ids, topk_w,
                               logits, shared_gate_w, shared_gate, a);
@@ -287,6 +316,28 @@ extern "C" smoe_status smoe_route_align_elb(
   f.layer = layer;
   f.M = elb_counts != nullptr ? M : 0;
   f.elb_clear = (elb_flags & SMOE_ELB_CLEAR_AFTER) ? 1 : 0;
-  hipLaunchKernelGGL(topk_align_elb_kernel, dim3(1), dim3(kAlignThreads), 0, st, f);
+  f.pf_never = 0;
+  int grid = 1;
+  for (int r = 0; r < 3; ++r) {
+    const bool on = pf != nullptr && pf->wgs > 0 && pf->p[r] != nullptr;
+    f.pf[r] = on ? static_cast<const uint4*>(pf->p[r]) : nullptr;
+    f.pf_n[r] = on ? pf->bytes[r] / 16 : 0;
+    if (f.pf_n[r] > 0) grid = 1 + pf->wgs;
+  }
+  hipLaunchKernelGGL(topk_align_elb_kernel, dim3(grid), dim3(kAlignThreads), 0, st, f);
   return check_launch("route_align_elb");
+}
+}  // namespace smoe
+
+extern "C" smoe_status smoe_route_align_elb(
+    const void* x, const float* w_router, const float* logit_bias, int T, int H, int E, int k,
+    int flags, int32_t* topk_ids, float* topk_w, float* logits, const float* shared_gate_w,
+    float* shared_gate, int32_t* expert_counts, int32_t* expert_offsets, int32_t* sorted_slots,
+    int32_t* active_experts, int32_t* n_active, int32_t* elb_counts, int L, int layer, int M,
+    int32_t* plan_ids, int32_t* plan_counts, int elb_flags, void* stream) {
+  clear_error();
+  return route_align_elb(x, w_router, logit_bias, T, H, E, k, flags, topk_ids, topk_w, logits,
+                         shared_gate_w, shared_gate, expert_counts, expert_offsets,
+                         sorted_slots, active_experts, n_active, elb_counts, L, layer, M,
+                         plan_ids, plan_counts, elb_flags, stream, nullptr);
 }

@@ -358,6 +358,11 @@ struct FusedArgs {
   int32_t* plan_ids;
   int32_t* plan_counts;
   int L, layer, M, elb_clear;
+  // Weights that the launch's other workgroups read through the caches
+  // while the routing workgroup works (16-byte units; none when pf_n are 0).
+  const uint4* pf[3];
+  long long pf_n[3];
+  int pf_never;  // always zero; its test keeps the loads, which store nothing
 };
 
 // Argument checks of smoe_route_topk, filling `a` (route.hip); the one-call
@@ -366,6 +371,25 @@ smoe_status route_check(const void* x, const float* w_router, const float* logit
                         int H, int E, int k, int flags, int32_t* topk_ids, float* topk_w,
                         float* logits, const float* shared_gate_w, float* shared_gate,
                         RouteArgs& a);
+
+// The fused routing call with an optional list of weights that `wgs` more
+// workgroups of the routing launch read through the caches while its one
+// routing workgroup works (smoe_route_align_elb passes none). The layer
+// call lists the shared experts' FP16 weights, which do not depend on the
+// routing: the FFN's first items then find them in the Infinity Cache
+// instead of waiting on HBM, and HBM is otherwise idle during the routing.
+struct RoutePrefetch {
+  const void* p[3];
+  long long bytes[3];  // multiples of 16
+  int wgs;
+};
+smoe_status route_align_elb(
+    const void* x, const float* w_router, const float* logit_bias, int T, int H, int E, int k,
+    int flags, int32_t* topk_ids, float* topk_w, float* logits, const float* shared_gate_w,
+    float* shared_gate, int32_t* expert_counts, int32_t* expert_offsets, int32_t* sorted_slots,
+    int32_t* active_experts, int32_t* n_active, int32_t* elb_counts, int L, int layer, int M,
+    int32_t* plan_ids, int32_t* plan_counts, int elb_flags, void* stream,
+    const RoutePrefetch* pf);
 
 // (NLG: logits the block can stage, at least T * E, plus T for a staged
 // shared gate)
