@@ -389,7 +389,10 @@ smoe_status smoe_combine(const float* slot_out, const float* topk_w, int T, int 
  *
  * The layer takes the launches of the three calls: router logits, the
  * top-k / alignment / ELB workgroup, the two FFN launches and the combine.
- * On error nothing is enqueued.
+ * When that workgroup runs alone (T*k <= 512) and the shared weights total
+ * at most 40 MB, its launch also holds one workgroup per other CU that only
+ * reads the shared weights, so that the FFN finds them in the caches; the
+ * results are unchanged. On error nothing is enqueued.
  */
 smoe_status smoe_moe_layer_w4a16(const void* x, const float* w_router, const float* logit_bias,
                                  int T, int H, int E, int k, int flags,
